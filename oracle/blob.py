@@ -1,0 +1,228 @@
+"""Whole-tensor encode/decode and the blob layout, contiguous and paged.
+
+The pages (the abstract of *Beyond Compression Ratio: High-Throughput KV
+Compression for Disaggregated LLM Serving* and the episode notes of
+*FastKVComp: checking whether high-throughput KV compression pays off*)
+describe compressing the KV cache before it crosses the prefill-to-decode
+link and decoding it on the other side; they define no byte format.  The
+layout used here, for a KV tensor [L, 2, T, H, D] (2 = K then V) with b_K
+and b_V bits per code and group size G:
+
+  codes section  for l in 0..L-1, for kv in (K, V): T*H rows in (t, h)
+                 order, each D*b_kv/8 bytes of packed codes
+  padding        zero bytes up to a multiple of 256
+  meta section   [L, 2, T, H, D/G] entries of 4 bytes: fp16 scale (bytes
+                 0-1) then fp16 zero (bytes 2-3), little endian
+  padding        zero bytes up to a multiple of 256
+
+Paged input: a pool [L, 2, num_blocks, block_size, H, D] and, per request
+r, a row of a block table naming the physical block of each logical block
+of ``block_size`` tokens, and a length seq_len[r].  Request r is encoded as
+the contiguous tensor of its first seq_len[r] tokens; its blob sits at
+offsets[r], the prefix sum of the earlier requests' blob sizes (each a
+multiple of 256).  Table entries past ceil(seq_len / block_size) and the
+slots of the last block past seq_len are ignored, and decode writes only
+the first seq_len[r] tokens of each request.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .rounding import storage_to_f64, f64_to_storage
+from .signs import sign_vector
+from .rht import rotate, unrotate
+from .quant import group_meta, quantize, pack_codes, unpack_codes, dequantize
+
+
+def _align256(n: int) -> int:
+    return (n + 255) // 256 * 256
+
+
+@dataclass(frozen=True)
+class BlobLayout:
+    layers: int
+    tokens: int
+    kv_heads: int
+    head_dim: int
+    bits_k: int
+    bits_v: int
+    group: int
+
+    @property
+    def rows(self) -> int:
+        return self.tokens * self.kv_heads
+
+    def row_bytes(self, kv: int) -> int:
+        return self.head_dim * (self.bits_k if kv == 0 else self.bits_v) // 8
+
+    @property
+    def codes_bytes(self) -> int:
+        return self.layers * self.rows * (self.row_bytes(0) + self.row_bytes(1))
+
+    @property
+    def meta_offset(self) -> int:
+        return _align256(self.codes_bytes)
+
+    @property
+    def groups(self) -> int:
+        return self.head_dim // self.group
+
+    @property
+    def meta_bytes(self) -> int:
+        return self.layers * 2 * self.rows * self.groups * 4
+
+    @property
+    def total(self) -> int:
+        return self.meta_offset + _align256(self.meta_bytes)
+
+    def codes_slab(self, l: int, kv: int) -> int:
+        """Byte offset of the (layer, K/V) code slab."""
+        return l * self.rows * (self.row_bytes(0) + self.row_bytes(1)) + kv * self.rows * self.row_bytes(0)
+
+    def meta_slab(self, l: int, kv: int) -> int:
+        """Byte offset of the (layer, K/V) meta slab."""
+        return self.meta_offset + (l * 2 + kv) * self.rows * self.groups * 4
+
+
+def blob_layout(layers, tokens, kv_heads, head_dim, bits_k, bits_v, group) -> BlobLayout:
+    if head_dim < 2 or head_dim & (head_dim - 1):
+        raise ValueError("head_dim must be a power of two")
+    for b in (bits_k, bits_v):
+        if b not in (2, 4, 8):
+            raise ValueError("bits must be 2, 4 or 8")
+    if group <= 0 or head_dim % group:
+        raise ValueError("group must divide head_dim")
+    return BlobLayout(layers, tokens, kv_heads, head_dim, bits_k, bits_v, group)
+
+
+@dataclass
+class EncodeTrace:
+    """Intermediate values of one oracle encode (indexed [L, 2, T, H, ...])."""
+    y: np.ndarray       # rotated values, float64 [L,2,T,H,D]
+    t: np.ndarray       # pre-rounding code values, float64 [L,2,T,H,D]
+    q: np.ndarray       # codes, uint8 [L,2,T,H,D]
+    scale: np.ndarray   # float16 [L,2,T,H,D/G]
+    zero: np.ndarray    # float16 [L,2,T,H,D/G]
+
+
+def encode(x_bits: np.ndarray, dtype: str, bits_k: int, bits_v: int, group: int, seed: int):
+    """Encode a [L, 2, T, H, D] tensor given as uint16 storage of ``dtype``.
+
+    Returns (blob uint8 array, EncodeTrace).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    L, two, T, H, D = x_bits.shape
+    if two != 2:
+        raise ValueError("second axis must be K/V")
+    lay = blob_layout(L, T, H, D, bits_k, bits_v, group)
+    s = sign_vector(seed, D)
+    x = storage_to_f64(x_bits, dtype)
+    y = rotate(x, s)
+    blob = np.zeros(lay.total, dtype=np.uint8)
+    G = group
+    t_all = np.zeros_like(y)
+    q_all = np.zeros(y.shape, dtype=np.uint8)
+    sc_all = np.zeros((L, 2, T, H, D // G), dtype=np.float16)
+    ze_all = np.zeros_like(sc_all)
+    for l in range(L):
+        for kv in range(2):
+            b = bits_k if kv == 0 else bits_v
+            yl = y[l, kv].reshape(T * H, D)
+            scale, zero = group_meta(yl, G, b)
+            q, t = quantize(yl, scale, zero, G, b)
+            packed = pack_codes(q, b)
+            off = lay.codes_slab(l, kv)
+            blob[off:off + packed.size] = packed.reshape(-1)
+            meta = np.stack([scale.view(np.uint16), zero.view(np.uint16)], axis=-1)
+            mbytes = meta.astype("<u2").view(np.uint8).reshape(-1)
+            moff = lay.meta_slab(l, kv)
+            blob[moff:moff + mbytes.size] = mbytes
+            t_all[l, kv] = t.reshape(T, H, D)
+            q_all[l, kv] = q.reshape(T, H, D)
+            sc_all[l, kv] = scale.reshape(T, H, D // G)
+            ze_all[l, kv] = zero.reshape(T, H, D // G)
+    return blob, EncodeTrace(y=y, t=t_all, q=q_all, scale=sc_all, zero=ze_all)
+
+
+def decode(blob: np.ndarray, shape, dtype: str, bits_k: int, bits_v: int, group: int, seed: int):
+    """Decode a blob back to a [L, 2, T, H, D] tensor.
+
+    Returns (uint16 storage of ``dtype`` rounded to nearest even, float64
+    values before that rounding).
+    """
+    L, two, T, H, D = shape
+    lay = blob_layout(L, T, H, D, bits_k, bits_v, group)
+    blob = np.asarray(blob, dtype=np.uint8)
+    if blob.size < lay.total:
+        raise ValueError("blob smaller than the layout requires")
+    s = sign_vector(seed, D)
+    G = group
+    xhat = np.zeros((L, 2, T, H, D), dtype=np.float64)
+    for l in range(L):
+        for kv in range(2):
+            b = bits_k if kv == 0 else bits_v
+            rb = lay.row_bytes(kv)
+            off = lay.codes_slab(l, kv)
+            packed = blob[off:off + T * H * rb].reshape(T * H, rb)
+            q = unpack_codes(packed, b, D)
+            moff = lay.meta_slab(l, kv)
+            m = blob[moff:moff + T * H * (D // G) * 4].view("<u2").reshape(T * H, D // G, 2)
+            scale = m[..., 0].astype(np.uint16).view(np.float16)
+            zero = m[..., 1].astype(np.uint16).view(np.float16)
+            yhat = dequantize(q, scale, zero, G)
+            xhat[l, kv] = unrotate(yhat, s).reshape(T, H, D)
+    return f64_to_storage(xhat, dtype), xhat
+
+
+def paged_layout(seq_lens, layers, kv_heads, head_dim, bits_k, bits_v, group):
+    """Per-request blob offsets (int64 array) and the total size in bytes."""
+    offsets = []
+    total = 0
+    for n in seq_lens:
+        if n < 0:
+            raise ValueError("negative sequence length")
+        offsets.append(total)
+        total += blob_layout(layers, int(n), kv_heads, head_dim, bits_k, bits_v, group).total
+    return np.array(offsets, dtype=np.int64), total
+
+
+def gather_request(pool: np.ndarray, table_row, seq_len: int) -> np.ndarray:
+    """Tokens 0..seq_len-1 of one request from a [L,2,NB,BS,H,D] pool."""
+    L, two, NB, BS, H, D = pool.shape
+    out = np.zeros((L, 2, seq_len, H, D), dtype=pool.dtype)
+    for t in range(seq_len):
+        blk = int(table_row[t // BS])
+        if not 0 <= blk < NB:
+            raise IndexError("block table entry outside the pool")
+        out[:, :, t] = pool[:, :, blk, t % BS]
+    return out
+
+
+def encode_paged(pool_bits, block_table, seq_lens, dtype, bits_k, bits_v, group, seed):
+    """Encode every request of a paged pool; returns (blob, offsets, traces)."""
+    L, two, NB, BS, H, D = pool_bits.shape
+    offsets, total = paged_layout(seq_lens, L, H, D, bits_k, bits_v, group)
+    blob = np.zeros(total, dtype=np.uint8)
+    traces = []
+    for r, n in enumerate(seq_lens):
+        x = gather_request(pool_bits, block_table[r], int(n))
+        b, tr = encode(x, dtype, bits_k, bits_v, group, seed)
+        blob[offsets[r]:offsets[r] + b.size] = b
+        traces.append(tr)
+    return blob, offsets, traces
+
+
+def decode_paged(blob, pool_bits, block_table, seq_lens, dtype, bits_k, bits_v, group, seed):
+    """Decode every request into a copy of ``pool_bits`` (other slots kept)."""
+    L, two, NB, BS, H, D = pool_bits.shape
+    offsets, total = paged_layout(seq_lens, L, H, D, bits_k, bits_v, group)
+    out = np.array(pool_bits, dtype=np.uint16, copy=True)
+    for r, n in enumerate(seq_lens):
+        n = int(n)
+        lay = blob_layout(L, n, H, D, bits_k, bits_v, group)
+        sub = np.asarray(blob)[offsets[r]:offsets[r] + lay.total]
+        xb, _ = decode(sub, (L, 2, n, H, D), dtype, bits_k, bits_v, group, seed)
+        for t in range(n):
+            out[:, :, int(block_table[r][t // BS]), t % BS] = xb[:, :, t]
+    return out
