@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Throughput of the fused KV encode + decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the whole hot path over one batch: encode the KV
+cache of the workload into its blob, then decode the blob back into a KV
+tensor.  Inputs are resident in HBM before the timed region starts; two
+buffer sets alternate between steps so that consecutive steps do not reuse
+cache-resident data.  Prints ONE JSON line.
+
+Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
+  value          raw bytes / (encode + decode time), GB/s (1e9)
+  encode/decode  per-kernel raw GB/s and algorithmic-HBM GB/s (bytes read
+                 plus bytes written) as a fraction of the 8 TB/s peak
+  roofline       the dominant kernel: algorithmic bytes per launch / mean
+                 launch time (HIP events on the launch stream), vs 8 TB/s
+  break_even     encode + decode time vs the wire time the compression saves
+                 at 100 and 400 Gbit/s
+  cpu_baseline   the CPU oracle on a bounded sample of the same workload
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b_4k")
+    ap.add_argument("--cpu-sample-chunks", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_compression_kvc_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILE_DIR, "counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = rec.get(workload, {}).get(kernel)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+
+def _oracle_chunk(args):
+    name, layer, tokens = args
+    import numpy as np
+    import oracle
+    from kv_cache_compression_kvc_amd import presets, inputs
+    p = presets.preset(name)
+    x = np.stack([inputs.as_u16(inputs.kv_chunk(p, layer, kv, (tokens,), device="cpu"))
+                  for kv in (0, 1)])[None]                       # [1, 2, T, H, D]
+    t0 = time.perf_counter()
+    blob, _ = oracle.encode(x, p.dtype, p.bits_k, p.bits_v, p.group, p.seed)
+    oracle.decode(blob, x.shape, p.dtype, p.bits_k, p.bits_v, p.group, p.seed)
+    return x.size * 2, time.perf_counter() - t0
+
+
+def cpu_baseline(p, chunks):
+    import multiprocessing as mp
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    workers = max(1, min(16, os.cpu_count() or 1, chunks))
+    tokens = max(1, (1 << 19) // (p.kv_heads * p.head_dim))  # 2 x 2^19 elements per chunk
+    jobs = [(p.name, i % max(1, p.layers), tokens) for i in range(chunks)]
+    ctx = mp.get_context("spawn")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        res = pool.map(_oracle_chunk, jobs)
+    wall = time.perf_counter() - t0
+    raw = sum(r[0] for r in res)
+    cpu = sum(r[1] for r in res)
+    return {
+        "value": raw / wall / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+        "sample": "%d chunks of [1,2,%d,%d,%d] %s (%.0f MiB raw), encode+decode, %.1f s of CPU work, "
+                  "%d processes x 1 BLAS thread" % (chunks, tokens, p.kv_heads, p.head_dim, p.dtype,
+                                                    raw / 2 ** 20, cpu, workers),
+    }
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(every tile is independent; see the sharding note in the design document).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_compression_kvc_amd as kvc
+    from kv_cache_compression_kvc_amd import presets, inputs
+
+    p = presets.preset(a.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    D, H, L = p.head_dim, p.kv_heads, p.layers
+    nsets = 2
+
+    if p.paged:
+        lens = inputs.request_lengths(p)
+        table, nb = inputs.block_table(p, lens)
+        offs, total = kvc.paged_layout(lens, L, H, D, p.bits_k, p.bits_v, p.group, p.dtype)
+        pools = [inputs.make_pool(p, nb, device=dev) for _ in range(nsets)]
+        outs = [torch.empty(total, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+        dsts = [torch.empty_like(pools[0]) for _ in range(nsets)]
+        bt = torch.from_numpy(table).to(dev)
+        sl = torch.from_numpy(lens).to(dev)
+        of = torch.from_numpy(offs).to(dev)
+        tokens = int(lens.sum())
+        raw_bytes = L * 2 * tokens * H * D * 2
+        enc_bytes = total
+
+        def enc(i):
+            kvc.encode_paged(pools[i], bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=outs[i])
+
+        def dec(i):
+            kvc.decode_paged(outs[i], dsts[i], bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed)
+        workload = {"workload": p.name, "layers": L, "requests": len(lens), "tokens": tokens,
+                    "kv_heads": H, "head_dim": D, "storage": p.dtype, "bits_k": p.bits_k,
+                    "bits_v": p.bits_v, "group": p.group, "layout": "paged, 16-token blocks"}
+    else:
+        xs = [inputs.make_kv(p, device=dev) for _ in range(nsets)]
+        total, _ = kvc.encoded_size(L, p.tokens, H, D, p.bits_k, p.bits_v, p.group, p.dtype)
+        outs = [torch.empty(total, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+        dsts = [torch.empty_like(xs[0]) for _ in range(nsets)]
+        raw_bytes = xs[0].numel() * 2
+        enc_bytes = total
+
+        def enc(i):
+            kvc.encode(xs[i], p.bits_k, p.bits_v, p.group, seed=p.seed, out=outs[i])
+
+        def dec(i):
+            kvc.decode(outs[i], xs[i].shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed, out=dsts[i])
+        workload = {"workload": p.name, "shape": [L, 2, p.tokens, H, D], "storage": p.dtype,
+                    "bits_k": p.bits_k, "bits_v": p.bits_v, "group": p.group, "layout": "contiguous"}
+
+    algo_bytes = raw_bytes + enc_bytes     # read + write of one encode (or one decode)
+    stream = torch.cuda.current_stream()
+
+    for i in range(a.warmup):
+        enc(i % nsets)
+        dec(i % nsets)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        e = ev[i]
+        e[0].record(stream)
+        enc(i % nsets)
+        e[1].record(stream)
+        dec(i % nsets)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_enc = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps / 1e3   # s per encode
+    t_dec = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps / 1e3
+    ms_per_step = wall / a.steps * 1e3
+
+    # copy probe: achievable streaming bandwidth in the same run
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    kvc.probe_copy(src, dst)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        kvc.probe_copy(src, dst)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 5 / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del src, dst
+
+    enc_alg = algo_bytes / t_enc / 1e9
+    dec_alg = algo_bytes / t_dec / 1e9
+    dominant = "encode" if t_enc >= t_dec else "decode"
+    t_dom = max(t_enc, t_dec)
+    achieved = algo_bytes / t_dom / 1e9
+    saved = raw_bytes - enc_bytes
+    be = {}
+    for gbit in (100, 400):
+        wire_saved_s = saved * 8 / (gbit * 1e9)
+        be["%dGbit" % gbit] = {"wire_time_saved_ms": wire_saved_s * 1e3,
+                               "encode_plus_decode_ms": (t_enc + t_dec) * 1e3,
+                               "pays": (t_enc + t_dec) < wire_saved_s,
+                               "required_raw_GBps_each": 2 * gbit / 8 / (1 - enc_bytes / raw_bytes)}
+    result = {
+        "metric": "encode+decode throughput of raw bf16 KV input (GB/s); per-kernel % of HBM peak; "
+                  "break-even at 400 Gbit",
+        "value": raw_bytes / (t_enc + t_dec) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Gaussian KV with K outlier channels; no model weights)",
+        "config": workload,
+        "encode": {"raw_GBps": raw_bytes / t_enc / 1e9, "hbm_GBps": enc_alg,
+                   "frac_hbm_peak": enc_alg / HBM_PEAK_GBPS, "frac_copy_probe": enc_alg / copy_gbps,
+                   "ms": t_enc * 1e3},
+        "decode": {"raw_GBps": raw_bytes / t_dec / 1e9, "hbm_GBps": dec_alg,
+                   "frac_hbm_peak": dec_alg / HBM_PEAK_GBPS, "frac_copy_probe": dec_alg / copy_gbps,
+                   "ms": t_dec * 1e3},
+        "bytes": {"raw": raw_bytes, "encoded": enc_bytes, "ratio": raw_bytes / enc_bytes},
+        "copy_probe_GBps": copy_gbps,
+        "break_even": be,
+        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": counter_traffic(p.name, dominant),
+                     "algorithmic_bytes_per_launch": algo_bytes, "launch_ms": t_dom * 1e3},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p, a.cpu_sample_chunks)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

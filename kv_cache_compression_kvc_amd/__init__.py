@@ -1,0 +1,173 @@
+"""Fused KV-cache encode / decode for AMD MI355X (gfx950).
+
+Python face of the C ABI in ``include/kvc.h``: every function here only
+marshals torch tensors (device memory) and the current torch stream into a
+call of ``libkvc.so``; all of the encode / decode runs in the HIP kernels.
+There is no CPU fallback: the calls raise if the library is not built.
+
+Encode (per head_dim vector of a [layers, 2, tokens, kv_heads, head_dim]
+bf16 / fp16 tensor): seeded +/-1 sign flip, orthonormal Walsh-Hadamard
+transform, per-group fp16 min/max meta, round-half-even 2/4/8-bit codes,
+LSB-first packing -- the randomized Hadamard transform and low-bit
+quantization stages that the episode notes of "FastKVComp: checking
+whether high-throughput KV compression pays off" describe, fused in one
+pass as the abstract of "Beyond Compression Ratio: High-Throughput KV
+Compression for Disaggregated LLM Serving" states.  Decode is the inverse.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import KvcDesc, KvcPaged, KvcError, DTYPE
+
+__all__ = [
+    "KvcError", "DTYPE", "abi_version", "encoded_size", "sign_mask", "encode", "decode",
+    "paged_layout", "encode_paged", "decode_paged", "debug_rotate", "probe_copy",
+]
+
+_TORCH_TO_NAME = {torch.bfloat16: "bf16", torch.float16: "fp16"}
+_NAME_TO_TORCH = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def _desc(layers, tokens, kv_heads, head_dim, dtype, bits_k, bits_v, group, seed=0):
+    return KvcDesc(int(layers), int(tokens), int(kv_heads), int(head_dim), DTYPE[dtype],
+                   int(bits_k), int(bits_v), int(group), int(seed) & ((1 << 64) - 1))
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def abi_version():
+    return _lib.lib().kvc_abi_version()
+
+
+def encoded_size(layers, tokens, kv_heads, head_dim, bits_k, bits_v, group, dtype="bf16"):
+    """(total bytes, byte offset of the meta section) of a blob."""
+    lib = _lib.lib()
+    total, meta = ctypes.c_uint64(), ctypes.c_uint64()
+    d = _desc(layers, tokens, kv_heads, head_dim, dtype, bits_k, bits_v, group)
+    _lib.check(lib.kvc_encoded_size(ctypes.byref(d), int(tokens), ctypes.byref(total), ctypes.byref(meta)))
+    return total.value, meta.value
+
+
+def sign_mask(seed, head_dim):
+    """Integer whose bit j is set iff sign j of the transform is -1."""
+    lib = _lib.lib()
+    words = (ctypes.c_uint64 * ((head_dim + 63) // 64))()
+    _lib.check(lib.kvc_sign_mask(int(seed) & ((1 << 64) - 1), int(head_dim), words))
+    return sum(int(w) << (64 * i) for i, w in enumerate(words))
+
+
+def encode(kv, bits_k, bits_v, group, seed=0, out=None, stream=None):
+    """Encode a contiguous [L, 2, T, H, D] GPU tensor; returns the uint8 blob."""
+    _check_cuda(kv, out)
+    L, two, T, H, D = kv.shape
+    if two != 2:
+        raise ValueError("axis 1 must hold K and V")
+    dt = _TORCH_TO_NAME[kv.dtype]
+    total, _ = encoded_size(L, T, H, D, bits_k, bits_v, group, dt)
+    if out is None:
+        out = torch.empty(total, dtype=torch.uint8, device=kv.device)
+    d = _desc(L, T, H, D, dt, bits_k, bits_v, group, seed)
+    _lib.check(_lib.lib().kvc_encode(ctypes.byref(d), _ptr(kv), _ptr(out), out.numel(), _stream(stream)))
+    return out
+
+
+def decode(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, stream=None):
+    """Decode a blob into a [L, 2, T, H, D] GPU tensor of ``dtype``."""
+    _check_cuda(blob, out)
+    L, two, T, H, D = shape
+    if out is None:
+        out = torch.empty(tuple(shape), dtype=_NAME_TO_TORCH[dtype], device=blob.device)
+    d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
+    _lib.check(_lib.lib().kvc_decode(ctypes.byref(d), _ptr(blob), blob.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def paged_layout(seq_lens, layers, kv_heads, head_dim, bits_k, bits_v, group, dtype="bf16"):
+    """(offsets int64 numpy array, total bytes) of the per-request blobs."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    offs = np.zeros(len(lens), dtype=np.int64)
+    total = ctypes.c_uint64()
+    d = _desc(layers, 0, kv_heads, head_dim, dtype, bits_k, bits_v, group)
+    _lib.check(_lib.lib().kvc_paged_layout(
+        ctypes.byref(d), lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(lens),
+        offs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ctypes.byref(total)))
+    return offs, total.value
+
+
+def _paged(pool, block_table, seq_lens, out_offsets, err_flag):
+    _check_cuda(block_table, seq_lens, out_offsets, err_flag)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or out_offsets.dtype != torch.int64:
+        raise ValueError("block_table / seq_lens must be int32 and out_offsets int64")
+    R, MB = block_table.shape
+    return KvcPaged(pool.shape[2], pool.shape[3], R, MB, 0, _ptr(block_table).value,
+                    _ptr(seq_lens).value, _ptr(out_offsets).value,
+                    _ptr(err_flag).value if err_flag is not None else None)
+
+
+def encode_paged(pool, block_table, seq_lens, out_offsets, total, bits_k, bits_v, group, seed=0,
+                 out=None, err_flag=None, stream=None):
+    """Encode every request of a [L, 2, NB, BS, H, D] pool into one blob buffer."""
+    _check_cuda(pool, out)
+    L, two, NB, BS, H, D = pool.shape
+    dt = _TORCH_TO_NAME[pool.dtype]
+    if out is None:
+        out = torch.empty(int(total), dtype=torch.uint8, device=pool.device)
+    pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag)
+    d = _desc(L, 0, H, D, dt, bits_k, bits_v, group, seed)
+    _lib.check(_lib.lib().kvc_encode_paged(ctypes.byref(d), _ptr(pool), ctypes.byref(pg), _ptr(out),
+                                           out.numel(), _stream(stream)))
+    return out
+
+
+def decode_paged(blob, pool, block_table, seq_lens, out_offsets, bits_k, bits_v, group, seed=0,
+                 err_flag=None, stream=None):
+    """Decode every request's blob back into the pool slots of its block table."""
+    _check_cuda(blob, pool)
+    L, two, NB, BS, H, D = pool.shape
+    dt = _TORCH_TO_NAME[pool.dtype]
+    pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag)
+    d = _desc(L, 0, H, D, dt, bits_k, bits_v, group, seed)
+    _lib.check(_lib.lib().kvc_decode_paged(ctypes.byref(d), _ptr(blob), blob.numel(), ctypes.byref(pg),
+                                           _ptr(pool), _stream(stream)))
+    return pool
+
+
+def debug_rotate(kv, seed=0, out=None, stream=None):
+    """Rotated values y = H (s * x) / sqrt(D) of the encode path, fp32."""
+    _check_cuda(kv, out)
+    L, two, T, H, D = kv.shape
+    if out is None:
+        out = torch.empty(tuple(kv.shape), dtype=torch.float32, device=kv.device)
+    d = _desc(L, T, H, D, _TORCH_TO_NAME[kv.dtype], 4, 4, 32, seed)
+    _lib.check(_lib.lib().kvc_debug_rotate(ctypes.byref(d), _ptr(kv), _ptr(out), _stream(stream)))
+    return out
+
+
+def probe_copy(src, dst, stream=None):
+    """Streaming device copy of src into dst (same byte size)."""
+    _check_cuda(src, dst)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("destination too small")
+    _lib.check(_lib.lib().kvc_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+    return dst

@@ -1,0 +1,563 @@
+/*
+ * kvc_device.h -- device code of the fused KV-cache encode / decode for
+ * CDNA4 (gfx950): kernels as templates over head_dim, dtype, code width and
+ * group size.  Instantiated by kvc_inst.hip, launched by kvc_launch.hip.
+ *
+ * What is computed follows the episode notes of "FastKVComp: checking
+ * whether high-throughput KV compression pays off" (randomized Hadamard
+ * transform, then low-bit quantization, then a lossless codec that is not
+ * built here) and the abstract of "Beyond Compression Ratio: High-Throughput
+ * KV Compression for Disaggregated LLM Serving" (the transform and the
+ * quantization run fused in one tiled kernel with no full-size intermediate
+ * tensor).  The encode reads each head_dim vector once from HBM, and writes
+ * only its packed codes and its per-group fp16 (scale, zero); the decode
+ * reads those and writes the vector once.
+ *
+ * Work decomposition (one wave64 per workgroup, persistent grid):
+ *   - an item is a tile of up to 64 consecutive head_dim vectors of one
+ *     (layer, K/V) slab, contiguous in the KV tensor or in one pool block;
+ *   - the wave loads the tile with fully coalesced 16-byte loads (1 KiB per
+ *     instruction), transposes it through LDS (rows padded by 16 bytes so
+ *     that both the row-wise writes and the per-lane reads are free of bank
+ *     conflicts), and then every lane owns one whole vector in registers;
+ *   - the Walsh-Hadamard butterfly, the group min/max, the fp16 meta, the
+ *     quantization and the packing all run inside the lane: no cross-lane
+ *     traffic, no intermediate in memory;
+ *   - the next tile's loads are issued before the current tile is
+ *     computed, so HBM reads overlap the arithmetic.
+ */
+#ifndef KVC_DEVICE_H
+#define KVC_DEVICE_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc_plan.h"
+
+namespace kvc {
+namespace dev {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // 16-byte chunk
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+template <int D>
+struct Norm;
+template <>
+struct Norm<64> {
+  static constexpr float inv_sqrt = 0.125f;
+};
+template <>
+struct Norm<128> {
+  static constexpr float inv_sqrt = 0.088388347648318440550f;  // 1/sqrt(128)
+};
+
+/* ---- element conversions ------------------------------------------------ */
+
+/* Two packed storage elements (element 2m in the low half) -> fp32. */
+template <int DT>
+__device__ __forceinline__ void unpack_pair(uint32_t w, float& lo, float& hi) {
+  if constexpr (DT == KVC_BF16) {
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xffff0000u);
+  } else {
+    half2_t h = __builtin_bit_cast(half2_t, w);
+    lo = static_cast<float>(h.x);
+    hi = static_cast<float>(h.y);
+  }
+}
+
+/* fp32 pair -> packed storage, round to nearest even. */
+template <int DT>
+__device__ __forceinline__ uint32_t pack_pair(float lo, float hi) {
+  float2_t f = {lo, hi};
+  if constexpr (DT == KVC_BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf162_t));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, half2_t));
+  }
+}
+
+__device__ __forceinline__ uint32_t f16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+__device__ __forceinline__ float f16_value(uint32_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
+
+/* fp32 -> fp16 rounding toward -inf: round to nearest, then step down one
+ * binary16 value if that overshot. */
+__device__ __forceinline__ uint32_t rd16(float v) {
+  uint32_t h = f16_bits(v);
+  if (f16_value(h) > v) h = (h & 0x8000u) ? h + 1u : (h == 0u ? 0x8001u : h - 1u);
+  return h;
+}
+
+/* fp32 -> fp16 rounding toward +inf. */
+__device__ __forceinline__ uint32_t ru16(float v) {
+  uint32_t h = f16_bits(v);
+  if (f16_value(h) < v) h = (h & 0x8000u) ? (h == 0x8000u ? 1u : h - 1u) : h + 1u;
+  return h;
+}
+
+/* ---- transform ------------------------------------------------------------ */
+
+/* In-place unnormalized Walsh-Hadamard butterfly (Sylvester order). */
+template <int D>
+__device__ __forceinline__ void fwht(float (&y)[D]) {
+#pragma unroll
+  for (int h = 1; h < D; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < D; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        float a = y[j], b = y[j + h];
+        y[j] = a + b;
+        y[j + h] = a - b;
+      }
+    }
+  }
+}
+
+/* ---- quantization and packing ------------------------------------------ */
+
+__device__ __forceinline__ uint32_t put_byte(float t, uint32_t sel, uint32_t acc) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(t), sel, acc);
+}
+
+/* One 32-bit word of packed codes from 32/B consecutive values t. */
+template <int B>
+__device__ __forceinline__ uint32_t pack_word(const float* t) {
+  if constexpr (B == 8) {
+    uint32_t w = put_byte(t[0], 0, 0);
+    w = put_byte(t[1], 1, w);
+    w = put_byte(t[2], 2, w);
+    return put_byte(t[3], 3, w);
+  } else if constexpr (B == 4) {
+    uint32_t e = put_byte(t[0], 0, 0), o = put_byte(t[1], 0, 0);
+    e = put_byte(t[2], 1, e);
+    o = put_byte(t[3], 1, o);
+    e = put_byte(t[4], 2, e);
+    o = put_byte(t[5], 2, o);
+    e = put_byte(t[6], 3, e);
+    o = put_byte(t[7], 3, o);
+    return e | (o << 4);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t v = put_byte(t[i], 0, 0);
+      v = put_byte(t[4 + i], 1, v);
+      v = put_byte(t[8 + i], 2, v);
+      w[i] = put_byte(t[12 + i], 3, v);
+    }
+    return w[0] | (w[1] << 2) | (w[2] << 4) | (w[3] << 6);
+  }
+}
+
+/* Codes of one 32-bit word -> 32/B floats. */
+template <int B>
+__device__ __forceinline__ void unpack_word(uint32_t u, float* q) {
+  auto byte = [](uint32_t x, int k) { return static_cast<float>((x >> (8 * k)) & 0xffu); };
+  if constexpr (B == 8) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = byte(u, k);
+  } else if constexpr (B == 4) {
+    uint32_t e = u & 0x0f0f0f0fu, o = (u >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      q[2 * k] = byte(e, k);
+      q[2 * k + 1] = byte(o, k);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w = (u >> (2 * i)) & 0x03030303u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q[4 * k + i] = byte(w, k);
+    }
+  }
+}
+
+/* ---- tiles ----------------------------------------------------------------- */
+
+struct Tile {
+  const uint8_t* src;  // first byte of the tile's source rows
+  uint8_t* dst;        // first byte of the tile's destination rows
+  uint8_t* codes;      // first code row of the tile (in the blob)
+  uint8_t* meta;       // first meta entry of the tile (in the blob)
+  int count;           // valid vectors, 1..64
+};
+
+__device__ __forceinline__ uint64_t align256(uint64_t n) { return (n + 255u) & ~uint64_t(255); }
+
+/*
+ * Map an item index to a tile.  Contiguous items always exist; paged items
+ * for blocks past a request's length are skipped (returns false), as are
+ * items whose table entry, length or blob extent is invalid (bit 0 of
+ * *err is then set).  `tensor` is the KV-tensor side (source of an encode,
+ * destination of a decode), `blob` the encoded side.
+ */
+template <int D>
+__device__ __forceinline__ bool item_tile(const LaunchArgs& a, int64_t item, const uint8_t* tensor,
+                                          uint8_t* blob, Tile& t) {
+  constexpr int64_t vec_bytes = int64_t(D) * 2;
+  if (!a.paged) {
+    const int64_t i = item / a.tiles_per_slab;
+    const int64_t v0 = (item - i * a.tiles_per_slab) * kTileVectors;
+    const int64_t s = i * a.slab_step + a.slab_first;
+    const int64_t l = s >> 1, kv = s & 1;
+    const int64_t row = kv ? a.row_v : a.row_k;
+    t.count = static_cast<int>(a.rows - v0 < kTileVectors ? a.rows - v0 : kTileVectors);
+    t.src = tensor + (s * a.rows + v0) * vec_bytes;
+    t.codes = blob + l * a.rows * (a.row_k + a.row_v) + kv * a.rows * a.row_k + v0 * row;
+    t.meta = blob + a.meta_offset + (s * a.rows + v0) * a.groups * 4;
+    return true;
+  }
+  const int64_t per_req = int64_t(a.max_blocks) * a.subtiles;
+  const int64_t per_slab = per_req * a.num_reqs;
+  const int64_t i = item / per_slab;
+  int64_t rem = item - i * per_slab;
+  const int32_t r = static_cast<int32_t>(rem / per_req);
+  rem -= int64_t(r) * per_req;
+  const int32_t j = static_cast<int32_t>(rem / a.subtiles);
+  const int32_t sub = static_cast<int32_t>(rem - int64_t(j) * a.subtiles);
+  const int32_t len = a.lens[r];
+  if (len < 0 || int64_t(len) > int64_t(a.max_blocks) * a.block_size) {
+    if (a.err && j == 0 && sub == 0) atomicOr(a.err, 1);
+    return false;
+  }
+  const int32_t first_tok = j * a.block_size;
+  if (first_tok >= len) return false;
+  const int32_t ntok = min(a.block_size, len - first_tok);
+  const int32_t v0 = sub * kTileVectors;
+  const int32_t nvec = ntok * a.heads;
+  if (v0 >= nvec) return false;
+  const int32_t blk = a.table[int64_t(r) * a.max_blocks + j];
+  const int64_t off = a.offsets[r];
+  const int64_t rows = int64_t(len) * a.heads;
+  const uint64_t codes_bytes = uint64_t(a.layers) * rows * (a.row_k + a.row_v);
+  const uint64_t meta_start = align256(codes_bytes);
+  const uint64_t total = meta_start + align256(uint64_t(a.layers) * 2 * rows * a.groups * 4);
+  if (blk < 0 || blk >= a.num_blocks || off < 0 || (off & 15) ||
+      uint64_t(off) > a.blob_bytes || total > a.blob_bytes - uint64_t(off)) {
+    if (a.err) atomicOr(a.err, 1);
+    return false;
+  }
+  const int64_t s = i * a.slab_step + a.slab_first;
+  const int64_t l = s >> 1, kv = s & 1;
+  const int64_t row = kv ? a.row_v : a.row_k;
+  const int64_t row0 = int64_t(first_tok) * a.heads + v0;  // t*H + h of the tile's first vector
+  t.count = min(kTileVectors, nvec - v0);
+  t.src = tensor + ((s * a.num_blocks + blk) * int64_t(a.block_size) * a.heads + v0) * vec_bytes;
+  uint8_t* rb = blob + off;
+  t.codes = rb + l * rows * (a.row_k + a.row_v) + kv * rows * a.row_k + row0 * row;
+  t.meta = rb + meta_start + (s * rows + row0) * a.groups * 4;
+  return true;
+}
+
+/* Advance `item` (stride gridDim.x) to the next item that maps to a tile. */
+template <int D>
+__device__ __forceinline__ bool next_tile(const LaunchArgs& a, int64_t& item, const uint8_t* tensor,
+                                          uint8_t* blob, Tile& t) {
+  while (item < a.total_items) {
+    if (item_tile<D>(a, item, tensor, blob, t)) return true;
+    item += gridDim.x;
+  }
+  return false;
+}
+
+/* Zero the padding of a blob whose codes / meta sections end at the given
+ * offsets (one wave, byte stores; at most 2 * 255 bytes). */
+__device__ void zero_padding(uint8_t* blob, uint64_t codes_bytes, uint64_t meta_start,
+                             uint64_t meta_end, uint64_t total) {
+  for (uint64_t p = codes_bytes + threadIdx.x; p < meta_start; p += 64) blob[p] = 0;
+  for (uint64_t p = meta_end + threadIdx.x; p < total; p += 64) blob[p] = 0;
+}
+
+__device__ void zero_padding_for(const LaunchArgs& a, int64_t item, uint8_t* blob) {
+  if (a.slab_first != 0) return;  // the K launch (or the joint launch) owns the padding
+  if (!a.paged) {
+    if (item != 0) return;
+    const uint64_t codes_bytes = uint64_t(a.layers) * a.rows * (a.row_k + a.row_v);
+    zero_padding(blob, codes_bytes, a.meta_offset,
+                 a.meta_offset + uint64_t(a.layers) * 2 * a.rows * a.groups * 4, a.blob_total);
+    return;
+  }
+  // paged: the item of (slab 0, request r, block 0, subtile 0) pads request r
+  const int64_t per_req = int64_t(a.max_blocks) * a.subtiles;
+  if (item >= per_req * a.num_reqs || item % per_req != 0) return;
+  const int32_t r = static_cast<int32_t>(item / per_req);
+  const int64_t rows = int64_t(a.lens[r]) * a.heads;
+  const uint64_t codes_bytes = uint64_t(a.layers) * rows * (a.row_k + a.row_v);
+  const uint64_t meta_start = align256(codes_bytes);
+  const uint64_t meta_end = meta_start + uint64_t(a.layers) * 2 * rows * a.groups * 4;
+  zero_padding(blob + a.offsets[r], codes_bytes, meta_start, meta_end, align256(meta_end));
+}
+
+/* Coalesced load of a tile: chunk c = k*64 + lane of the tile's 16-byte
+ * chunks goes to st[k]; chunks past the valid vectors read as zero. */
+template <int D>
+__device__ __forceinline__ void load_tile(const Tile& t, v4u (&st)[D / 8]) {
+  constexpr int CH = D / 8;
+  const v4u* p = reinterpret_cast<const v4u*>(t.src);
+  const int lane = threadIdx.x;
+  if (t.count == kTileVectors) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) st[k] = __builtin_nontemporal_load(p + k * 64 + lane);
+  } else {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = k * 64 + lane;
+      st[k] = (c / CH < t.count) ? __builtin_nontemporal_load(p + c) : v4u{0, 0, 0, 0};
+    }
+  }
+}
+
+/* Registers (chunk layout) -> LDS rows of RSW chunks. */
+template <int D>
+__device__ __forceinline__ void stage_rows(v4u* lds, const v4u (&st)[D / 8]) {
+  constexpr int CH = D / 8, RSW = CH + 1;
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int c = k * 64 + lane;
+    lds[(c / CH) * RSW + (c % CH)] = st[k];
+  }
+}
+
+/* Own LDS row -> D fp32 values with the sign flip applied (exact: an xor
+ * of the sign bit on the packed pair before widening). */
+template <int D, int DT>
+__device__ __forceinline__ void read_signed(const v4u* lds, const LaunchArgs& a, float (&y)[D]) {
+  constexpr int CH = D / 8, RSW = CH + 1;
+  const v4u* row = lds + threadIdx.x * RSW;
+#pragma unroll
+  for (int p = 0; p < CH; ++p) {
+    const v4u w = row[p];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * p + i;
+      unpack_pair<DT>(ws[i] ^ a.sign_words[m], y[2 * m], y[2 * m + 1]);
+    }
+  }
+}
+
+/* ---- encode ---------------------------------------------------------------- */
+
+template <int D, int DT, int B, int G>
+__device__ __forceinline__ void encode_vector(const LaunchArgs& a, float (&y)[D], const Tile& t) {
+  constexpr int NG = D / G;
+  constexpr float QMAX = float((1 << B) - 1);
+  constexpr float RS = Norm<D>::inv_sqrt;
+  constexpr int WPG = G * B / 32;  // code words per group
+  constexpr int VPW = 32 / B;      // values per code word
+  fwht<D>(y);
+  uint32_t meta[NG];
+  uint32_t words[D * B / 32];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float mn = y[g * G], mx = y[g * G];
+#pragma unroll
+    for (int j = 1; j < G; ++j) {
+      mn = fminf(mn, y[g * G + j]);
+      mx = fmaxf(mx, y[g * G + j]);
+    }
+    // meta of the normalized values y / sqrt(D)
+    const uint32_t zb = rd16(mn * RS);
+    const float zf = f16_value(zb);
+    const uint32_t sb = ru16((mx * RS - zf) / QMAX);
+    const float sf = f16_value(sb);
+    const float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
+    const float A = inv * RS;
+    const float Bz = -zf * inv;
+    meta[g] = sb | (zb << 16);
+#pragma unroll
+    for (int w = 0; w < WPG; ++w) {
+      float tq[VPW];
+#pragma unroll
+      for (int k = 0; k < VPW; ++k) tq[k] = fmaf(y[g * G + w * VPW + k], A, Bz);
+      words[g * WPG + w] = pack_word<B>(tq);
+    }
+  }
+  if (static_cast<int>(threadIdx.x) < t.count) {
+    constexpr int RB = D * B / 8;
+    v4u* crow = reinterpret_cast<v4u*>(t.codes + threadIdx.x * RB);
+#pragma unroll
+    for (int c = 0; c < RB / 16; ++c)
+      crow[c] = v4u{words[4 * c], words[4 * c + 1], words[4 * c + 2], words[4 * c + 3]};
+    uint32_t* mrow = reinterpret_cast<uint32_t*>(t.meta) + threadIdx.x * NG;
+    if constexpr (NG == 1) {
+      mrow[0] = meta[0];
+    } else if constexpr (NG == 2) {
+      *reinterpret_cast<v2u*>(mrow) = v2u{meta[0], meta[1]};
+    } else {
+      *reinterpret_cast<v4u*>(mrow) = v4u{meta[0], meta[1], meta[2], meta[3]};
+    }
+  }
+}
+
+template <int D, int DT, int B, int G>
+__global__ __launch_bounds__(64) void encode_kernel(const LaunchArgs a) {
+  constexpr int CH = D / 8, RSW = CH + 1;
+  __shared__ v4u lds[kTileVectors * RSW];
+  const uint8_t* tensor = static_cast<const uint8_t*>(a.src);
+  uint8_t* blob = static_cast<uint8_t*>(a.dst);
+  int64_t item = blockIdx.x;
+  Tile cur;
+  if (!next_tile<D>(a, item, tensor, blob, cur)) return;
+  zero_padding_for(a, item, blob);
+  v4u st[CH];
+  load_tile<D>(cur, st);
+  for (;;) {
+    stage_rows<D>(lds, st);
+    int64_t nitem = item + gridDim.x;
+    Tile nxt;
+    const bool more = next_tile<D>(a, nitem, tensor, blob, nxt);
+    if (more) {
+      zero_padding_for(a, nitem, blob);
+      load_tile<D>(nxt, st);
+    }
+    float y[D];
+    read_signed<D, DT>(lds, a, y);
+    encode_vector<D, DT, B, G>(a, y, cur);
+    if (!more) break;
+    cur = nxt;
+    item = nitem;
+  }
+}
+
+/* ---- decode ---------------------------------------------------------------- */
+
+template <int D, int B, int G>
+struct CodeRegs {
+  v4u codes[D * B / 128];
+  uint32_t meta[D / G];
+};
+
+template <int D, int B, int G>
+__device__ __forceinline__ void load_codes(const Tile& t, CodeRegs<D, B, G>& r) {
+  constexpr int RB = D * B / 8, NG = D / G;
+  const int lane = threadIdx.x;
+  if (lane < t.count) {
+    const v4u* crow = reinterpret_cast<const v4u*>(t.codes + lane * RB);
+#pragma unroll
+    for (int c = 0; c < RB / 16; ++c) r.codes[c] = __builtin_nontemporal_load(crow + c);
+    const uint32_t* mrow = reinterpret_cast<const uint32_t*>(t.meta) + lane * NG;
+    if constexpr (NG == 1) {
+      r.meta[0] = __builtin_nontemporal_load(mrow);
+    } else if constexpr (NG == 2) {
+      const v2u m = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(mrow));
+      r.meta[0] = m.x;
+      r.meta[1] = m.y;
+    } else {
+      const v4u m = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(mrow));
+      r.meta[0] = m.x;
+      r.meta[1] = m.y;
+      r.meta[2] = m.z;
+      r.meta[3] = m.w;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < RB / 16; ++c) r.codes[c] = v4u{0, 0, 0, 0};
+#pragma unroll
+    for (int g = 0; g < NG; ++g) r.meta[g] = 0;
+  }
+}
+
+template <int D, int DT, int B, int G>
+__global__ __launch_bounds__(64) void decode_kernel(const LaunchArgs a) {
+  constexpr int CH = D / 8, RSW = CH + 1, NG = D / G;
+  constexpr float RS = Norm<D>::inv_sqrt;
+  constexpr int WPG = G * B / 32, VPW = 32 / B;
+  __shared__ v4u lds[kTileVectors * RSW];
+  uint8_t* tensor = static_cast<uint8_t*>(a.dst);
+  uint8_t* blob = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.src));
+  const int lane = threadIdx.x;
+  int64_t item = blockIdx.x;
+  Tile cur;
+  if (!next_tile<D>(a, item, tensor, blob, cur)) return;
+  CodeRegs<D, B, G> cr;
+  load_codes<D, B, G>(cur, cr);
+  for (;;) {
+    float y[D];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      // dequantize with 1/sqrt(D) folded into scale and zero
+      const float sc = f16_value(cr.meta[g] & 0xffffu) * RS;
+      const float ze = f16_value(cr.meta[g] >> 16) * RS;
+#pragma unroll
+      for (int w = 0; w < WPG; ++w) {
+        const int wi = g * WPG + w;
+        const v4u c4 = cr.codes[wi / 4];
+        const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w};
+        float q[VPW];
+        unpack_word<B>(cw[wi % 4], q);
+#pragma unroll
+        for (int k = 0; k < VPW; ++k) y[g * G + w * VPW + k] = fmaf(q[k], sc, ze);
+      }
+    }
+    int64_t nitem = item + gridDim.x;
+    Tile nxt;
+    const bool more = next_tile<D>(a, nitem, tensor, blob, nxt);
+    if (more) load_codes<D, B, G>(nxt, cr);
+    fwht<D>(y);
+    v4u* row = lds + lane * RSW;
+#pragma unroll
+    for (int p = 0; p < CH; ++p) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * p + i;
+        w[i] = pack_pair<DT>(y[2 * m], y[2 * m + 1]) ^ a.sign_words[m];
+      }
+      row[p] = v4u{w[0], w[1], w[2], w[3]};
+    }
+    v4u* out = reinterpret_cast<v4u*>(const_cast<uint8_t*>(cur.src));
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = k * 64 + lane;
+      if (c / CH < cur.count) out[c] = lds[(c / CH) * RSW + (c % CH)];
+    }
+    if (!more) break;
+    cur = nxt;
+    item = nitem;
+  }
+}
+
+/* ---- rotate (test hook) ---------------------------------------------------- */
+
+template <int D, int DT>
+__global__ __launch_bounds__(64) void rotate_kernel(const LaunchArgs a) {
+  constexpr int CH = D / 8, RSW = CH + 1;
+  constexpr float RS = Norm<D>::inv_sqrt;
+  __shared__ v4u lds[kTileVectors * RSW];
+  const uint8_t* tensor = static_cast<const uint8_t*>(a.src);
+  float* yout = static_cast<float*>(a.dst);
+  for (int64_t item = blockIdx.x; item < a.total_items; item += gridDim.x) {
+    Tile t;
+    item_tile<D>(a, item, tensor, nullptr, t);
+    v4u st[CH];
+    load_tile<D>(t, st);
+    stage_rows<D>(lds, st);
+    float y[D];
+    read_signed<D, DT>(lds, a, y);
+    fwht<D>(y);
+    if (static_cast<int>(threadIdx.x) < t.count) {
+      const int64_t vec = (t.src - tensor) / (2 * D) + threadIdx.x;
+      float4* o = reinterpret_cast<float4*>(yout + vec * D);
+#pragma unroll
+      for (int c = 0; c < D / 4; ++c)
+        o[c] = float4(y[4 * c] * RS, y[4 * c + 1] * RS, y[4 * c + 2] * RS, y[4 * c + 3] * RS);
+    }
+  }
+}
+
+}  // namespace dev
+
+}  // namespace kvc
+
+#endif

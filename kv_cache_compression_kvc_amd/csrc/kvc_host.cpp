@@ -1,0 +1,280 @@
+/*
+ * kvc_host.cpp -- host half of the C ABI: argument validation, blob sizes,
+ * the sign generator and launch plans.  Plain C++ with no HIP dependency,
+ * so it also builds with g++ for unit tests and sanitizers.
+ *
+ * The sign vector of the randomized Hadamard transform (episode notes of
+ * "FastKVComp: checking whether high-throughput KV compression pays off":
+ * randomized Hadamard transform, then low-bit quantization) is drawn from
+ * SplitMix64 (Steele, Lea and Flood, OOPSLA 2014): state += 0x9E3779B97F4A7C15,
+ * then two xor-shift-multiply rounds and a final xor-shift; s_j = -1 iff bit
+ * 63 of the (j+1)-th output is set.
+ */
+#include <stdint.h>
+#include <string.h>
+
+#include "kvc_plan.h"
+
+namespace kvc {
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* r) { return !__builtin_mul_overflow(a, b, r); }
+bool add_ok(uint64_t a, uint64_t b, uint64_t* r) { return !__builtin_add_overflow(a, b, r); }
+
+bool align_up(uint64_t n, uint64_t* r) {
+  uint64_t t;
+  if (!add_ok(n, kAlign - 1, &t)) return false;
+  *r = t / kAlign * kAlign;
+  return true;
+}
+
+uint64_t splitmix64_next(uint64_t* state) {
+  *state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = *state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_desc(const kvc_desc* d) {
+  if (!d) return KVC_EINVAL;
+  if (d->layers < 0 || d->tokens < 0 || d->kv_heads < 0) return KVC_EINVAL;
+  if (d->head_dim != 64 && d->head_dim != 128) return KVC_ESHAPE;
+  if (d->dtype != KVC_BF16 && d->dtype != KVC_FP16) return KVC_EDTYPE;
+  const int32_t widths[2] = {d->bits_k, d->bits_v};
+  for (int32_t b : widths)
+    if (b != 2 && b != 4 && b != 8) return KVC_EBITS;
+  if (d->group != 32 && d->group != 64 && d->group != 128) return KVC_EGROUP;
+  if (d->group > d->head_dim) return KVC_EGROUP;
+  return KVC_OK;
+}
+
+void fill_signs(const kvc_desc* d, LaunchArgs* a) {
+  uint64_t st = d->seed;
+  memset(a->sign_words, 0, sizeof(a->sign_words));
+  for (int j = 0; j < d->head_dim; ++j) {
+    uint64_t z = splitmix64_next(&st);
+    if (z >> 63) a->sign_words[j / 2] |= (j & 1) ? 0x80000000u : 0x00008000u;
+  }
+}
+
+void common_args(const kvc_desc* d, LaunchArgs* a) {
+  memset(a, 0, sizeof(*a));
+  a->layers = d->layers;
+  a->row_k = static_cast<int32_t>(d->head_dim * d->bits_k / 8);
+  a->row_v = static_cast<int32_t>(d->head_dim * d->bits_v / 8);
+  a->groups = static_cast<int32_t>(d->head_dim / d->group);
+  fill_signs(d, a);
+}
+
+/* K and V together when their widths match (or for the rotate hook). */
+void split_slabs(Op op, const kvc_desc* d, Plan* plan, const LaunchArgs& base) {
+  if (op == Op::Rotate || d->bits_k == d->bits_v) {
+    plan->n_launch = 1;
+    plan->bits[0] = d->bits_k;
+    plan->args[0] = base;
+    plan->args[0].n_slabs = 2 * d->layers;
+    plan->args[0].slab_step = 1;
+    plan->args[0].slab_first = 0;
+  } else {
+    plan->n_launch = 2;
+    for (int kv = 0; kv < 2; ++kv) {
+      plan->bits[kv] = kv ? d->bits_v : d->bits_k;
+      plan->args[kv] = base;
+      plan->args[kv].n_slabs = d->layers;
+      plan->args[kv].slab_step = 2;
+      plan->args[kv].slab_first = kv;
+    }
+  }
+}
+
+}  // namespace
+
+int blob_sizes(const kvc_desc* d, int64_t tokens, BlobSizes* out) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (tokens < 0 || !out) return KVC_EINVAL;
+  uint64_t rows, lr, per_row, codes, meta, groups_total, a, b, total;
+  if (!mul_ok(static_cast<uint64_t>(tokens), static_cast<uint64_t>(d->kv_heads), &rows)) return KVC_ESHAPE;
+  if (!mul_ok(rows, static_cast<uint64_t>(d->layers), &lr)) return KVC_ESHAPE;
+  per_row = static_cast<uint64_t>(d->head_dim) * (d->bits_k + d->bits_v) / 8;
+  if (!mul_ok(lr, per_row, &codes)) return KVC_ESHAPE;
+  if (!mul_ok(lr, 2ull * (d->head_dim / d->group), &groups_total)) return KVC_ESHAPE;
+  if (!mul_ok(groups_total, 4, &meta)) return KVC_ESHAPE;
+  if (!align_up(codes, &a) || !align_up(meta, &b) || !add_ok(a, b, &total)) return KVC_ESHAPE;
+  if (total > static_cast<uint64_t>(INT64_MAX)) return KVC_ESHAPE;
+  out->codes = codes;
+  out->meta_offset = a;
+  out->meta = meta;
+  out->total = total;
+  return KVC_OK;
+}
+
+int plan_contiguous(Op op, const kvc_desc* d, const void* src, void* dst,
+                    uint64_t blob_bytes, Plan* plan) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (!plan) return KVC_EINVAL;
+  memset(plan, 0, sizeof(*plan));
+  plan->head_dim = static_cast<int>(d->head_dim);
+  plan->dtype = d->dtype;
+  plan->group = d->group;
+  BlobSizes sz;
+  st = blob_sizes(d, d->tokens, &sz);
+  if (st != KVC_OK) return st;
+  uint64_t rows = static_cast<uint64_t>(d->tokens) * static_cast<uint64_t>(d->kv_heads);
+  uint64_t elems;
+  if (!mul_ok(rows, 2ull * d->layers * d->head_dim, &elems)) return KVC_ESHAPE;
+  if (op != Op::Rotate && blob_bytes < sz.total) return KVC_ENOSPC;
+  if (elems == 0) {  // nothing to read or write
+    plan->n_launch = 0;
+    return KVC_OK;
+  }
+  if (!src || !dst) return KVC_EINVAL;
+  if (!aligned16(src) || !aligned16(dst)) return KVC_EALIGN;
+  LaunchArgs base;
+  common_args(d, &base);
+  base.src = src;
+  base.dst = dst;
+  base.blob_bytes = blob_bytes;
+  base.paged = 0;
+  base.rows = static_cast<int64_t>(rows);
+  base.tiles_per_slab = static_cast<int64_t>((rows + kTileVectors - 1) / kTileVectors);
+  base.meta_offset = sz.meta_offset;
+  base.blob_total = sz.total;
+  split_slabs(op, d, plan, base);
+  for (int i = 0; i < plan->n_launch; ++i) {
+    uint64_t items;
+    if (!mul_ok(static_cast<uint64_t>(plan->args[i].n_slabs),
+                static_cast<uint64_t>(plan->args[i].tiles_per_slab), &items))
+      return KVC_ESHAPE;
+    plan->args[i].total_items = static_cast<int64_t>(items);
+  }
+  return KVC_OK;
+}
+
+int plan_paged(Op op, const kvc_desc* d, const void* src, void* dst,
+               uint64_t blob_bytes, const kvc_paged* pg, Plan* plan) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (!plan || !pg || op == Op::Rotate) return KVC_EINVAL;
+  memset(plan, 0, sizeof(*plan));
+  plan->head_dim = static_cast<int>(d->head_dim);
+  plan->dtype = d->dtype;
+  plan->group = d->group;
+  if (pg->block_size < 1 || pg->block_size > 1024) return KVC_ERANGE;
+  if (pg->num_reqs < 0 || pg->max_blocks < 0 || pg->num_blocks < 0 || pg->reserved != 0)
+    return KVC_ERANGE;
+  uint64_t vecs_per_block;
+  if (!mul_ok(static_cast<uint64_t>(pg->block_size), static_cast<uint64_t>(d->kv_heads), &vecs_per_block) ||
+      vecs_per_block > (1ull << 30))
+    return KVC_ESHAPE;
+  uint64_t subtiles = (vecs_per_block + kTileVectors - 1) / kTileVectors;
+  uint64_t per_slab, items;
+  if (!mul_ok(static_cast<uint64_t>(pg->num_reqs), static_cast<uint64_t>(pg->max_blocks), &per_slab) ||
+      !mul_ok(per_slab, subtiles, &per_slab) ||
+      !mul_ok(per_slab, 2ull * static_cast<uint64_t>(d->layers), &items) || items > (1ull << 62))
+    return KVC_ESHAPE;
+  if (items == 0) {
+    plan->n_launch = 0;
+    return KVC_OK;
+  }
+  if (!src || !dst || !pg->block_table || !pg->seq_lens || !pg->out_offsets) return KVC_EINVAL;
+  if (!aligned16(src) || !aligned16(dst)) return KVC_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(pg->out_offsets) & 7u) ||
+      (reinterpret_cast<uintptr_t>(pg->block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(pg->seq_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(pg->err_flag) & 3u))
+    return KVC_EALIGN;
+  LaunchArgs base;
+  common_args(d, &base);
+  base.src = src;
+  base.dst = dst;
+  base.blob_bytes = blob_bytes;
+  base.paged = 1;
+  base.num_blocks = pg->num_blocks;
+  base.block_size = pg->block_size;
+  base.heads = static_cast<int32_t>(d->kv_heads);
+  base.num_reqs = pg->num_reqs;
+  base.max_blocks = pg->max_blocks;
+  base.subtiles = static_cast<int32_t>(subtiles);
+  base.table = pg->block_table;
+  base.lens = pg->seq_lens;
+  base.offsets = pg->out_offsets;
+  base.err = pg->err_flag;
+  split_slabs(op, d, plan, base);
+  for (int i = 0; i < plan->n_launch; ++i)
+    plan->args[i].total_items = static_cast<int64_t>(per_slab) * plan->args[i].n_slabs;
+  return KVC_OK;
+}
+
+}  // namespace kvc
+
+extern "C" {
+
+int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_strerror(int32_t s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_EINVAL: return "invalid argument (null pointer or negative size)";
+    case KVC_ESHAPE: return "unsupported shape or size overflow";
+    case KVC_EBITS: return "bits must be 2, 4 or 8";
+    case KVC_EGROUP: return "group must be 32, 64 or 128 and at most head_dim";
+    case KVC_EDTYPE: return "dtype must be bf16 or fp16";
+    case KVC_EALIGN: return "device pointer not suitably aligned";
+    case KVC_ENOSPC: return "output buffer too small for the blob";
+    case KVC_EHIP: return "HIP runtime error";
+    case KVC_ERANGE: return "paged argument out of range";
+    default: return "unknown status";
+  }
+}
+
+kvc_status kvc_encoded_size(const kvc_desc* desc, int64_t tokens, uint64_t* total,
+                            uint64_t* meta_offset) {
+  if (!total) return KVC_EINVAL;
+  kvc::BlobSizes sz;
+  int st = kvc::blob_sizes(desc, tokens, &sz);
+  if (st != KVC_OK) return static_cast<kvc_status>(st);
+  *total = sz.total;
+  if (meta_offset) *meta_offset = sz.meta_offset;
+  return KVC_OK;
+}
+
+kvc_status kvc_sign_mask(uint64_t seed, int64_t head_dim, uint64_t* mask_words) {
+  if (!mask_words || head_dim <= 0 || head_dim > 4096) return KVC_EINVAL;
+  uint64_t st = seed;
+  for (int64_t w = 0; w < (head_dim + 63) / 64; ++w) mask_words[w] = 0;
+  for (int64_t j = 0; j < head_dim; ++j)
+    if (kvc::splitmix64_next(&st) >> 63) mask_words[j / 64] |= 1ull << (j % 64);
+  return KVC_OK;
+}
+
+kvc_status kvc_paged_layout(const kvc_desc* desc, const int32_t* seq_lens_host,
+                            int32_t num_reqs, int64_t* offsets_host, uint64_t* total) {
+  if (!total || num_reqs < 0) return KVC_EINVAL;
+  if (num_reqs > 0 && (!seq_lens_host || !offsets_host)) return KVC_EINVAL;
+  uint64_t acc = 0;
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    if (seq_lens_host[r] < 0) return KVC_EINVAL;
+    kvc::BlobSizes sz;
+    int st = kvc::blob_sizes(desc, seq_lens_host[r], &sz);
+    if (st != KVC_OK) return static_cast<kvc_status>(st);
+    offsets_host[r] = static_cast<int64_t>(acc);
+    if (__builtin_add_overflow(acc, sz.total, &acc) || acc > static_cast<uint64_t>(INT64_MAX))
+      return KVC_ESHAPE;
+  }
+  if (num_reqs == 0) {  // still validate the descriptor
+    kvc::BlobSizes sz;
+    int st = kvc::blob_sizes(desc, 0, &sz);
+    if (st != KVC_OK) return static_cast<kvc_status>(st);
+  }
+  *total = acc;
+  return KVC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+/*
+ * kvc_launch.hip -- GPU entry points of the C ABI (include/kvc.h): pick the
+ * kernel instance for a validated plan and launch it on the caller's stream
+ * with a persistent grid (compute units x resident workgroups per unit).
+ */
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "kvc_device.h"
+#include "kvc_pick.h"
+#include "kvc_plan.h"
+
+namespace kvc {
+namespace dev {
+
+/* Streaming 16-byte copy: the achievable-bandwidth yardstick. */
+__global__ __launch_bounds__(256) void copy_kernel(const v4u* __restrict__ src, v4u* __restrict__ dst,
+                                                   uint64_t n) {
+  const uint64_t stride = uint64_t(gridDim.x) * blockDim.x;
+  uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const v4u a0 = __builtin_nontemporal_load(src + i);
+    const v4u a1 = __builtin_nontemporal_load(src + i + stride);
+    const v4u a2 = __builtin_nontemporal_load(src + i + 2 * stride);
+    const v4u a3 = __builtin_nontemporal_load(src + i + 3 * stride);
+    __builtin_nontemporal_store(a0, dst + i);
+    __builtin_nontemporal_store(a1, dst + i + stride);
+    __builtin_nontemporal_store(a2, dst + i + 2 * stride);
+    __builtin_nontemporal_store(a3, dst + i + 3 * stride);
+  }
+  for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+}  // namespace dev
+
+namespace {
+
+Kernel pick(Op op, int d, int dt, int b, int g) {
+  if (d == 64) return dt == KVC_BF16 ? pick_d64_t0(op, b, g) : pick_d64_t1(op, b, g);
+  if (d == 128) return dt == KVC_BF16 ? pick_d128_t0(op, b, g) : pick_d128_t1(op, b, g);
+  return nullptr;
+}
+
+/* Resident workgroups per device for a kernel: CUs x occupancy, cached. */
+struct GridCache {
+  std::mutex mu;
+  static constexpr int kMax = 512;
+  int n = 0;
+  int dev[kMax];
+  const void* fn[kMax];
+  int64_t grid[kMax];
+};
+GridCache g_grid;
+
+int resident_groups(Kernel k, int threads, int64_t* out) {
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return KVC_EHIP;
+  {
+    std::lock_guard<std::mutex> lk(g_grid.mu);
+    for (int i = 0; i < g_grid.n; ++i)
+      if (g_grid.dev[i] == device && g_grid.fn[i] == reinterpret_cast<const void*>(k)) {
+        *out = g_grid.grid[i];
+        return KVC_OK;
+      }
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return KVC_EHIP;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), threads, 0) !=
+      hipSuccess)
+    return KVC_EHIP;
+  const int64_t g = int64_t(cus) * (per_cu > 0 ? per_cu : 1);
+  std::lock_guard<std::mutex> lk(g_grid.mu);
+  if (g_grid.n < GridCache::kMax) {
+    g_grid.dev[g_grid.n] = device;
+    g_grid.fn[g_grid.n] = reinterpret_cast<const void*>(k);
+    g_grid.grid[g_grid.n] = g;
+    ++g_grid.n;
+  }
+  *out = g;
+  return KVC_OK;
+}
+
+int run_plan(Op op, const Plan& plan, void* stream) {
+  for (int i = 0; i < plan.n_launch; ++i) {
+    Kernel k = pick(op, plan.head_dim, plan.dtype, plan.bits[i], plan.group);
+    if (!k) return KVC_ESHAPE;
+    int64_t resident = 0;
+    int st = resident_groups(k, 64, &resident);
+    if (st != KVC_OK) return st;
+    const int64_t grid = std::min<int64_t>(plan.args[i].total_items, resident);
+    if (grid <= 0) continue;
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64), 0,
+                       static_cast<hipStream_t>(stream), plan.args[i]);
+    if (hipGetLastError() != hipSuccess) return KVC_EHIP;
+  }
+  return KVC_OK;
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" {
+
+kvc_status kvc_encode(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes, void* stream) {
+  kvc::Plan plan;
+  int st = kvc::plan_contiguous(kvc::Op::Encode, desc, kv, out, out_bytes, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Encode, plan, stream);
+  return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_decode(const kvc_desc* desc, const void* in, uint64_t in_bytes, void* kv_out, void* stream) {
+  kvc::Plan plan;
+  int st = kvc::plan_contiguous(kvc::Op::Decode, desc, in, kv_out, in_bytes, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Decode, plan, stream);
+  return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_encode_paged(const kvc_desc* desc, const void* pool, const kvc_paged* paged, void* out,
+                            uint64_t out_bytes, void* stream) {
+  kvc::Plan plan;
+  int st = kvc::plan_paged(kvc::Op::Encode, desc, pool, out, out_bytes, paged, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Encode, plan, stream);
+  return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_decode_paged(const kvc_desc* desc, const void* in, uint64_t in_bytes, const kvc_paged* paged,
+                            void* pool, void* stream) {
+  kvc::Plan plan;
+  int st = kvc::plan_paged(kvc::Op::Decode, desc, in, pool, in_bytes, paged, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Decode, plan, stream);
+  return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_debug_rotate(const kvc_desc* desc, const void* kv, float* y_out, void* stream) {
+  kvc::Plan plan;
+  int st = kvc::plan_contiguous(kvc::Op::Rotate, desc, kv, y_out, 0, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Rotate, plan, stream);
+  return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_probe_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
+  if (bytes == 0) return KVC_OK;
+  if (!src || !dst) return KVC_EINVAL;
+  if ((bytes & 15u) || (reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(dst) & 15u))
+    return KVC_EALIGN;
+  int64_t resident = 0;
+  int st = kvc::resident_groups(reinterpret_cast<kvc::Kernel>(kvc::dev::copy_kernel), 256, &resident);
+  if (st != KVC_OK) return static_cast<kvc_status>(st);
+  const uint64_t n = bytes / 16;
+  const uint64_t grid = std::min<uint64_t>(uint64_t(resident), (n + 255) / 256);
+  hipLaunchKernelGGL(kvc::dev::copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const kvc::dev::v4u*>(src), static_cast<kvc::dev::v4u*>(dst), n);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_EHIP;
+}
+
+}  // extern "C"

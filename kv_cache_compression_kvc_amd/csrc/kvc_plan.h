@@ -1,0 +1,90 @@
+/*
+ * kvc_plan.h -- launch plans shared by the host half (kvc_host.cpp, plain
+ * C++) and the device half (kvc_kernels.hip).  No HIP types: the host half
+ * builds with g++ and is unit-tested without a GPU.
+ *
+ * A plan describes one kernel launch over "items".  Each item is a tile of
+ * at most 64 consecutive head_dim vectors of one (layer, K/V) slab; every
+ * vector of a tile is contiguous in the KV tensor (or in one pool block)
+ * and its code rows and meta entries are contiguous in the blob.
+ */
+#ifndef KVC_PLAN_H
+#define KVC_PLAN_H
+
+#include <stdint.h>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+constexpr int kTileVectors = 64;   // one vector per lane of a wave64
+
+/* Arguments of one encode / decode / rotate launch (passed by value). */
+struct LaunchArgs {
+  const void* src;        // encode: KV tensor or pool; decode: blob
+  void* dst;              // encode: blob; decode: KV tensor or pool; rotate: fp32 y
+  uint64_t blob_bytes;    // size of the blob buffer (bounds checks)
+
+  // slab s = i * slab_step + slab_first, i in [0, n_slabs); s = l * 2 + kv
+  int64_t n_slabs;
+  int64_t slab_step;
+  int64_t slab_first;
+  int64_t layers;         // L of the whole tensor
+  int32_t row_k;          // code bytes per K vector (D * bits_k / 8)
+  int32_t row_v;          // code bytes per V vector
+  int32_t groups;         // D / group
+  int32_t paged;          // 0: contiguous, 1: paged
+
+  // contiguous layout
+  int64_t rows;           // T * H vectors per slab
+  int64_t tiles_per_slab; // ceil(rows / 64)
+  uint64_t meta_offset;   // byte offset of the meta section in the blob
+  uint64_t blob_total;    // bytes of the blob proper (codes, meta, padding)
+
+  // paged layout
+  int64_t num_blocks;
+  int32_t block_size;
+  int32_t heads;
+  int32_t num_reqs;
+  int32_t max_blocks;
+  int32_t subtiles;       // ceil(block_size * H / 64)
+  int32_t pad0;
+  const int32_t* table;
+  const int32_t* lens;
+  const int64_t* offsets;
+  int32_t* err;
+
+  int64_t total_items;    // items of this launch
+  uint32_t sign_words[64];// bit 15 / bit 31 of word m: sign of element 2m / 2m+1
+};
+
+enum class Op { Encode, Decode, Rotate };
+
+/* Up to two launches: K and V run together when their code widths match. */
+struct Plan {
+  int n_launch;
+  int bits[2];
+  int head_dim;
+  int dtype;
+  int group;
+  LaunchArgs args[2];
+};
+
+/* Host half: validate and fill a plan.  Returns a kvc_status. */
+int plan_contiguous(Op op, const kvc_desc* d, const void* src, void* dst,
+                    uint64_t blob_bytes, Plan* plan);
+int plan_paged(Op op, const kvc_desc* d, const void* src, void* dst,
+               uint64_t blob_bytes, const kvc_paged* pg, Plan* plan);
+
+/* Sizes of a blob for T tokens (no validation beyond overflow). */
+struct BlobSizes {
+  uint64_t codes;       // bytes of the codes section before padding
+  uint64_t meta_offset; // start of the meta section
+  uint64_t meta;        // bytes of the meta section before padding
+  uint64_t total;
+};
+int blob_sizes(const kvc_desc* d, int64_t tokens, BlobSizes* out);
+
+}  // namespace kvc
+
+#endif

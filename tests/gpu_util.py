@@ -1,0 +1,86 @@
+"""Shared helpers of the GPU tests (test infrastructure)."""
+
+import numpy as np
+import torch
+
+import oracle
+import parity
+from kv_cache_compression_kvc_amd import inputs
+
+CANARY = 0xA5
+PAD = 4096
+
+
+def guarded(nbytes, device):
+    """A uint8 buffer of nbytes with PAD canary bytes on both sides; returns (whole, view)."""
+    whole = torch.full((nbytes + 2 * PAD,), CANARY, dtype=torch.uint8, device=device)
+    return whole, whole[PAD:PAD + nbytes]
+
+
+def canaries_intact(whole):
+    host = whole.cpu().numpy()
+    return bool((host[:PAD] == CANARY).all() and (host[-PAD:] == CANARY).all())
+
+
+def sample_vectors(p, rng, n_random=1500):
+    """Vector indices of a contiguous [L,2,T,H,D] tensor: random ones plus every
+    slab's first and last vector and a few tile boundaries."""
+    rows = p.tokens * p.kv_heads
+    slabs = 2 * p.layers
+    idx = set(rng.integers(0, rows * slabs, n_random).tolist())
+    for s in range(0, slabs, max(1, slabs // 8)):
+        for r in (0, 63, 64, rows - 1):
+            if 0 <= r < rows:
+                idx.add(s * rows + r)
+    idx.add(slabs * rows - 1)
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def check_sampled_encode(p, x_gpu, blob_gpu, idx):
+    """Criteria (2) and (3) on sampled vectors of a full-size contiguous encode."""
+    D = p.head_dim
+    rows = p.tokens * p.kv_heads
+    lay = oracle.blob_layout(p.layers, p.tokens, p.kv_heads, D, p.bits_k, p.bits_v, p.group)
+    xs = inputs.as_u16(x_gpu.view(-1, D)[torch.from_numpy(idx).to(x_gpu.device)])
+    rep = parity.CodeReport()
+    for kv in (0, 1):
+        sel = np.nonzero((idx // rows) % 2 == kv)[0]
+        if not len(sel):
+            continue
+        v = idx[sel]
+        s = v // rows
+        r = v % rows
+        l = s // 2
+        b = p.bits_k if kv == 0 else p.bits_v
+        rb = lay.row_bytes(kv)
+        ng = lay.groups
+        code_off = torch.from_numpy(np.array([lay.codes_slab(int(li), kv) for li in l]) + r * rb)
+        meta_off = torch.from_numpy(np.array([lay.meta_slab(int(li), kv) for li in l]) + r * ng * 4)
+        dev = blob_gpu.device
+        ci = (code_off[:, None] + torch.arange(rb)[None, :]).to(dev)
+        mi = (meta_off[:, None] + torch.arange(ng * 4)[None, :]).to(dev)
+        codes = blob_gpu[ci].cpu().numpy()
+        meta = blob_gpu[mi].cpu().numpy().view("<u2").reshape(len(v), ng, 2)
+        rep.merge(parity.check_rows(xs[sel], p.dtype, b, p.group, p.seed, codes, meta))
+    return rep
+
+
+def decode_error_bound_ok(p, x_gpu, xhat_gpu, blob_gpu):
+    """Every vector: ||x - xhat|| <= sqrt(D) * max group scale / 2 + the output rounding."""
+    D = p.head_dim
+    lay = oracle.blob_layout(p.layers, p.tokens, p.kv_heads, D, p.bits_k, p.bits_v, p.group)
+    ng = lay.groups
+    meta = blob_gpu[lay.meta_offset:lay.meta_offset + lay.meta_bytes].view(torch.int16)
+    scale = meta.view(-1, ng, 2)[..., 0].contiguous().view(torch.float16).float()
+    smax = scale.max(dim=1).values
+    worst = 0.0
+    nvec = x_gpu.numel() // D
+    chunk = 1 << 22
+    for v0 in range(0, nvec, chunk):
+        xv = x_gpu.view(-1, D)[v0:v0 + chunk].float()
+        xh = xhat_gpu.view(-1, D)[v0:v0 + chunk].float()
+        err = (xv - xh).norm(dim=1)
+        ulp = 2.0 ** -8 if p.dtype == "bf16" else 2.0 ** -11
+        bound = (D ** 0.5) * smax[v0:v0 + chunk] / 2 * (1 + 1e-5) + ulp * xh.norm(dim=1)
+        worst = max(worst, float((err / bound.clamp_min(1e-30)).max()))
+    return worst

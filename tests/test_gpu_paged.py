@@ -1,0 +1,171 @@
+"""GPU parity of the paged encode / decode against the oracle."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import gpu_util
+import kv_cache_compression_kvc_amd as kvc
+from kv_cache_compression_kvc_amd import inputs, presets
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _setup(p, lens, max_blocks=None, junk=True):
+    lens = np.asarray(lens, dtype=np.int32)
+    table, nb = inputs.block_table(p, lens, max_blocks=max_blocks)
+    if junk:  # entries past each request's last block must never be read
+        for r, n in enumerate(lens):
+            table[r, -(-int(n) // p.block_size):] = 0x7FFFFFF0
+    pool = inputs.make_pool(p, nb)
+    offs, total = kvc.paged_layout(lens, p.layers, p.kv_heads, p.head_dim, p.bits_k, p.bits_v,
+                                   p.group, p.dtype)
+    o2, t2 = oracle.paged_layout(lens, p.layers, p.kv_heads, p.head_dim, p.bits_k, p.bits_v, p.group)
+    assert np.array_equal(offs, o2) and total == t2
+    return lens, table, pool, offs, total
+
+
+def _gpu(lens, table, offs):
+    return (torch.from_numpy(table).to(DEV), torch.from_numpy(lens).to(DEV),
+            torch.from_numpy(offs).to(DEV))
+
+
+CASES = [
+    # (head_dim, dtype, bits_k, bits_v, group, heads, lengths)
+    (128, "bf16", 2, 4, 64, 4, [37, 0, 16, 5, 1, 33, 200]),
+    (128, "bf16", 4, 4, 128, 8, [17, 64, 3]),
+    (64, "fp16", 8, 2, 32, 2, [15, 16, 31, 2]),
+    (128, "fp16", 4, 8, 32, 1, [100, 7]),
+]
+
+
+@pytest.mark.parametrize("D,dtype,bk,bv,G,H,lens", CASES)
+def test_paged_matches_oracle(D, dtype, bk, bv, G, H, lens):
+    p = presets.preset("qwen7b_paged").with_(name="paged-%d-%s-%d%d-%d-%d" % (D, dtype, bk, bv, G, H),
+                                              layers=2, kv_heads=H, head_dim=D, dtype=dtype,
+                                              bits_k=bk, bits_v=bv, group=G, seed=5)
+    lens, table, pool, offs, total = _setup(p, lens)
+    bt, sl, of = _gpu(lens, table, offs)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    whole, out = gpu_util.guarded(total, DEV)
+    _say("paged encode", p.name)
+    kvc.encode_paged(pool.to(DEV), bt, sl, of, total, bk, bv, G, seed=p.seed, out=out, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert gpu_util.canaries_intact(whole)
+    blob = out.cpu().numpy()
+    pool_b = inputs.as_u16(pool)
+    oblob, _, _ = oracle.encode_paged(pool_b, table, lens, dtype, bk, bv, G, p.seed)
+    for r, n in enumerate(lens):
+        x = oracle.gather_request(pool_b, table[r], int(n))
+        sub = blob[offs[r]:offs[r] + oracle.blob_layout(p.layers, int(n), H, D, bk, bv, G).total]
+        parity.check_blob(x, sub, dtype, bk, bv, G, p.seed)
+    # decode into a pool filled with a sentinel: used slots decoded, the rest untouched
+    _say("paged decode", p.name)
+    sentinel = torch.full(pool.shape, 7.0, dtype=pool.dtype, device=DEV)
+    kvc.decode_paged(out, sentinel, bt, sl, of, bk, bv, G, seed=p.seed, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = inputs.as_u16(sentinel)
+    ref = oracle.decode_paged(oblob, np.full(pool_b.shape, inputs.as_u16(torch.tensor([7.0], dtype=pool.dtype))[0],
+                                             dtype=np.uint16), table, lens, dtype, bk, bv, G, p.seed)
+    used = np.zeros(pool.shape[2:4], dtype=bool)
+    for r, n in enumerate(lens):
+        for t in range(int(n)):
+            used[table[r][t // p.block_size], t % p.block_size] = True
+    assert np.array_equal(got[:, :, ~used], ref[:, :, ~used])
+    parity.check_decode(got[:, :, used], ref[:, :, used], dtype)
+
+
+def test_paged_bad_table_entry_is_flagged_not_faulted():
+    p = presets.preset("qwen7b_paged").with_(name="paged-bad", layers=1, kv_heads=4, seed=1)
+    lens, table, pool, offs, total = _setup(p, [40, 20])
+    table[1, 0] = pool.shape[2] + 5          # outside the pool
+    bt, sl, of = _gpu(lens, table, offs)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.zeros(total, dtype=torch.uint8, device=DEV)
+    kvc.encode_paged(pool.to(DEV), bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=1,
+                     out=out, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 1
+    # request 0 is still encoded correctly
+    pool_b = inputs.as_u16(pool)
+    x = oracle.gather_request(pool_b, table[0], 40)
+    sub = out.cpu().numpy()[offs[0]:offs[0] + oracle.blob_layout(1, 40, 4, 128, p.bits_k, p.bits_v, p.group).total]
+    parity.check_blob(x, sub, p.dtype, p.bits_k, p.bits_v, p.group, 1)
+
+
+def test_paged_length_above_table_is_flagged():
+    p = presets.preset("qwen7b_paged").with_(name="paged-long", layers=1, kv_heads=4, seed=1)
+    lens, table, pool, offs, total = _setup(p, [40, 20], max_blocks=3)
+    bt, _, of = _gpu(lens, table, offs)
+    sl = torch.tensor([40, 3 * 16 + 1], dtype=torch.int32, device=DEV)   # more tokens than the row holds
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.zeros(total + 8192, dtype=torch.uint8, device=DEV)
+    kvc.encode_paged(pool.to(DEV), bt, sl, of, total + 8192, p.bits_k, p.bits_v, p.group, seed=1,
+                     out=out, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 1
+
+
+@pytest.mark.slow
+def test_paged_full_size_sampled():
+    p = presets.preset("qwen7b_paged")
+    lens = inputs.request_lengths(p)
+    table, nb = inputs.block_table(p, lens)
+    offs, total = kvc.paged_layout(lens, p.layers, p.kv_heads, p.head_dim, p.bits_k, p.bits_v,
+                                   p.group, p.dtype)
+    _say("paged full size: generate pool of", nb, "blocks")
+    pool = inputs.make_pool(p, nb, device=DEV)
+    bt, sl, of = _gpu(lens, table, offs)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    whole, out = gpu_util.guarded(total, DEV)
+    _say("paged full size: encode")
+    kvc.encode_paged(pool, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=out, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and gpu_util.canaries_intact(whole)
+    rng = np.random.default_rng(3)
+    rep = parity.CodeReport()
+    D, H, BS = p.head_dim, p.kv_heads, p.block_size
+    for r in rng.choice(len(lens), 6, replace=False).tolist() + [int(np.argmin(lens)), int(np.argmax(lens))]:
+        n = int(lens[r])
+        lay = oracle.blob_layout(p.layers, n, H, D, p.bits_k, p.bits_v, p.group)
+        sub = out[int(offs[r]):int(offs[r]) + lay.total].cpu().numpy()
+        for l in rng.choice(p.layers, 2, replace=False):
+            for kv in (0, 1):
+                toks = np.unique(np.concatenate([rng.integers(0, n, 40), [0, n - 1]]))
+                blk = torch.from_numpy(table[r][toks // BS].astype(np.int64)).to(DEV)
+                x = pool[int(l), kv][blk, torch.from_numpy(toks % BS).to(DEV)]       # [k, H, D]
+                xb = inputs.as_u16(x).reshape(-1, D)
+                rows = (toks[:, None] * H + np.arange(H)[None, :]).reshape(-1)
+                codes, meta = parity.blob_rows(sub, lay, int(l), kv, rows)
+                b = p.bits_k if kv == 0 else p.bits_v
+                rep.merge(parity.check_rows(xb, p.dtype, b, p.group, p.seed, codes, meta))
+    _say("  sampled paged codes vs oracle:", rep)
+    _say("paged full size: decode")
+    dst = torch.zeros_like(pool)
+    kvc.decode_paged(out, dst, bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    # relative RMS error of the round trip over every used slot of a few requests
+    for r in range(0, len(lens), 16):
+        n = int(lens[r])
+        toks = np.arange(n)
+        blk = torch.from_numpy(table[r][toks // BS].astype(np.int64)).to(DEV)
+        slot = torch.from_numpy(toks % BS).to(DEV)
+        a = pool[:, :, blk, slot].float()
+        b = dst[:, :, blk, slot].float()
+        rel = float((a - b).norm() / a.norm())
+        assert rel < 0.2, rel
+    del pool, dst, whole, out
+    torch.cuda.empty_cache()
