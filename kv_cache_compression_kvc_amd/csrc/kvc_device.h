@@ -123,8 +123,11 @@ __device__ __forceinline__ void fwht(float (&y)[D]) {
 
 /* ---- quantization and packing ------------------------------------------ */
 
+/* v_cvt_pk_u8_f32 rounds to nearest even and clamps to [0, 255] (checked on
+ * gfx950 for ties k + 1/2, negative values and values above 255), so it both
+ * rounds the code and inserts it into byte `sel` of `acc`. */
 __device__ __forceinline__ uint32_t put_byte(float t, uint32_t sel, uint32_t acc) {
-  return __builtin_amdgcn_cvt_pk_u8_f32(__builtin_rintf(t), sel, acc);
+  return __builtin_amdgcn_cvt_pk_u8_f32(t, sel, acc);
 }
 
 /* One 32-bit word of packed codes from 32/B consecutive values t. */
@@ -366,20 +369,32 @@ __device__ __forceinline__ void encode_vector(const LaunchArgs& a, float (&y)[D]
       mn = fminf(mn, y[g * G + j]);
       mx = fmaxf(mx, y[g * G + j]);
     }
-    // meta of the normalized values y / sqrt(D)
-    const uint32_t zb = rd16(mn * RS);
-    const float zf = f16_value(zb);
-    const uint32_t sb = ru16((mx * RS - zf) / QMAX);
-    const float sf = f16_value(sb);
-    const float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
-    const float A = inv * RS;
-    const float Bz = -zf * inv;
+    // Meta of the normalized values y / sqrt(D).  Every binary32 operation
+    // here rounds on its own (no contraction into fused multiply-adds):
+    //   zero  = RD16(mn * rs)
+    //   scale = RU16(((mx * rs) - zero) / (2^b - 1))
+    //   inv = 1 / scale, A = inv * rs, Bz = -zero * inv
+    uint32_t zb, sb;
+    float A, Bz;
+    {
+#pragma clang fp contract(off)
+      zb = rd16(mn * RS);
+      const float zf = f16_value(zb);
+      const float mxn = mx * RS;
+      sb = ru16((mxn - zf) / QMAX);
+      const float sf = f16_value(sb);
+      const float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
+      A = inv * RS;
+      Bz = -zf * inv;
+    }
     meta[g] = sb | (zb << 16);
 #pragma unroll
     for (int w = 0; w < WPG; ++w) {
       float tq[VPW];
+      // t = fma(u, A, Bz), clamped above at 2^b - 1 (the byte conversion
+      // clamps below at 0 and rounds half to even)
 #pragma unroll
-      for (int k = 0; k < VPW; ++k) tq[k] = fmaf(y[g * G + w * VPW + k], A, Bz);
+      for (int k = 0; k < VPW; ++k) tq[k] = fminf(fmaf(y[g * G + w * VPW + k], A, Bz), QMAX);
       words[g * WPG + w] = pack_word<B>(tq);
     }
   }
@@ -413,7 +428,9 @@ __global__ __launch_bounds__(64) void encode_kernel(const LaunchArgs a) {
   v4u st[CH];
   load_tile<D>(cur, st);
   for (;;) {
+    __syncthreads();  // previous tile's rows fully read
     stage_rows<D>(lds, st);
+    __syncthreads();  // this tile's rows visible to every lane
     int64_t nitem = item + gridDim.x;
     Tile nxt;
     const bool more = next_tile<D>(a, nitem, tensor, blob, nxt);
@@ -506,6 +523,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const LaunchArgs a) {
     if (more) load_codes<D, B, G>(nxt, cr);
     fwht<D>(y);
     v4u* row = lds + lane * RSW;
+    __syncthreads();  // previous tile's rows fully read
 #pragma unroll
     for (int p = 0; p < CH; ++p) {
       uint32_t w[4];
@@ -516,6 +534,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const LaunchArgs a) {
       }
       row[p] = v4u{w[0], w[1], w[2], w[3]};
     }
+    __syncthreads();  // every lane's row written
     v4u* out = reinterpret_cast<v4u*>(const_cast<uint8_t*>(cur.src));
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
@@ -542,7 +561,9 @@ __global__ __launch_bounds__(64) void rotate_kernel(const LaunchArgs a) {
     item_tile<D>(a, item, tensor, nullptr, t);
     v4u st[CH];
     load_tile<D>(t, st);
+    __syncthreads();
     stage_rows<D>(lds, st);
+    __syncthreads();
     float y[D];
     read_signed<D, DT>(lds, a, y);
     fwht<D>(y);

@@ -34,8 +34,9 @@ Hadamard, numpy's float16 conversion) or published test vectors under
 from .signs import splitmix64_outputs, sign_vector, sign_bits_mask
 from .rounding import round_binary, to_fp16, rd16, ru16, rne_bf16, rne_fp16, \
     storage_to_f64, f64_to_storage
-from .rht import hadamard, rotate, unrotate
-from .quant import group_meta, quantize, pack_codes, unpack_codes, dequantize
+from .rht import hadamard, rotate_raw, rotate, unrotate
+from .quant import fl, div_f32, group_meta, code_values, quantize, pack_codes, unpack_codes, \
+    dequantize
 from .blob import BlobLayout, blob_layout, encode, decode, EncodeTrace, \
     paged_layout, gather_request, encode_paged, decode_paged
 
@@ -43,8 +44,9 @@ __all__ = [
     "splitmix64_outputs", "sign_vector", "sign_bits_mask",
     "round_binary", "to_fp16", "rd16", "ru16", "rne_bf16", "rne_fp16",
     "storage_to_f64", "f64_to_storage",
-    "hadamard", "rotate", "unrotate",
-    "group_meta", "quantize", "pack_codes", "unpack_codes", "dequantize",
+    "hadamard", "rotate_raw", "rotate", "unrotate",
+    "fl", "div_f32", "group_meta", "code_values", "quantize", "pack_codes", "unpack_codes",
+    "dequantize",
     "BlobLayout", "blob_layout", "encode", "decode", "EncodeTrace",
     "paged_layout", "gather_request", "encode_paged", "decode_paged",
 ]

@@ -36,6 +36,12 @@ def hadamard(D: int) -> np.ndarray:
     return np.where(_popcount(i[:, None] & i[None, :]) % 2 == 0, 1.0, -1.0)
 
 
+def rotate_raw(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """Rows of x (..., D) -> u = H (s * x), the transform before the 1/sqrt(D)."""
+    x = np.asarray(x, dtype=np.float64)
+    return (x * signs) @ hadamard(x.shape[-1])
+
+
 def rotate(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
     """Rows of x (..., D) -> y = H (s * x) / sqrt(D), float64."""
     x = np.asarray(x, dtype=np.float64)

@@ -5,8 +5,10 @@ Every step is computed a second way, from definitions rather than formulas:
   * Hadamard entries from (-1)**popcount(i & j), transform by explicit sums;
   * fp16 directed rounding by searching the sorted list of every finite
     binary16 value (largest value <= x, smallest value >= x);
-  * codes by trying every code k in [0, 2**b) and keeping the one whose
-    reconstruction zero + k*scale is nearest to y (ties to the even code);
+  * every binary32 step of the decision arithmetic (see ``oracle/quant.py``)
+    evaluated exactly in rational arithmetic (``fractions.Fraction``) and
+    rounded to the nearest binary32 value by an exact integer rounding;
+  * codes as the integer nearest to t, ties to even, in rational arithmetic;
   * packing bit by bit;
   * output rounding to bf16 / fp16 by nearest-value search over the format's
     finite values, ties to the even bit pattern.
@@ -19,6 +21,7 @@ per-group fp16 zero rounded down and scale rounded up, LSB-first packing.
 import bisect
 import math
 import struct
+from fractions import Fraction
 
 from .signs import sign_vector
 
@@ -97,6 +100,53 @@ def nearest_even_search(x: float, fmt: str) -> int:
     return pat
 
 
+def f32_round(v) -> float:
+    """Nearest binary32 value to the rational v, ties to even (exact)."""
+    v = Fraction(v)
+    if v == 0:
+        return 0.0
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    quantum = Fraction(2) ** (e - 23)
+    m = a / quantum
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * float(n * quantum)
+
+
+def nearest_int_even(v) -> int:
+    v = Fraction(v)
+    n = math.floor(v)
+    rem = v - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n
+
+
+def rotate_rows_raw(x_rows, seed, D):
+    """u = H (s * x) by exact rational sums."""
+    s = sign_vector(seed, D)
+    out = []
+    for row in x_rows:
+        u = []
+        for i in range(D):
+            acc = Fraction(0)
+            for j in range(D):
+                h = -1 if bin(i & j).count("1") % 2 else 1
+                acc += h * int(s[j]) * Fraction(row[j])
+            u.append(acc)
+        out.append(u)
+    return out
+
+
 def rotate_rows(x_rows, seed, D):
     s = sign_vector(seed, D)
     inv = math.sqrt(D)
@@ -115,28 +165,33 @@ def rotate_rows(x_rows, seed, D):
 
 def encode_rows(x_rows, D, G, bits, seed):
     """Returns (packed rows as lists of bytes, meta [(scale_bits, zero_bits)], codes)."""
-    ys = rotate_rows(x_rows, seed, D)
+    us = rotate_rows_raw(x_rows, seed, D)
     qmax = 2 ** bits - 1
+    rs = Fraction(f32_round(Fraction(1.0 / math.sqrt(D))))
     packed_rows, metas, codes_rows = [], [], []
-    for y in ys:
+    for u in us:
         codes = []
         row_meta = []
         for g in range(D // G):
-            part = y[g * G:(g + 1) * G]
-            z = rd16_search(min(part))
-            s = ru16_search((max(part) - z) / qmax)
+            part = u[g * G:(g + 1) * G]
+            mn = Fraction(f32_round(min(part)))
+            mx = Fraction(f32_round(max(part)))
+            z = rd16_search(f32_round(mn * rs))
+            zq = Fraction(z)
+            d = Fraction(f32_round(Fraction(f32_round(mx * rs)) - zq))
+            s = ru16_search(f32_round(d / qmax))
+            sq = Fraction(s)
             row_meta.append((fp16_bits_of(s), fp16_bits_of(z)))
+            if s == 0.0:
+                codes.extend([0] * G)
+                continue
+            inv = Fraction(f32_round(1 / sq))
+            a = Fraction(f32_round(inv * rs))
+            c = Fraction(f32_round(-zq * inv))
             for v in part:
-                if s == 0.0:
-                    codes.append(0)
-                    continue
-                best = None
-                for k in range(qmax + 1):
-                    err = abs(v - (z + k * s))
-                    key = (err, k & 1)
-                    if best is None or key < best[0]:
-                        best = (key, k)
-                codes.append(best[1])
+                t = Fraction(f32_round(Fraction(f32_round(v)) * a + c))
+                t = min(max(t, Fraction(0)), Fraction(qmax))
+                codes.append(nearest_int_even(t))
         nbytes = D * bits // 8
         packed = [0] * nbytes
         for j, c in enumerate(codes):

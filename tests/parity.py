@@ -3,9 +3,10 @@
 The four parity criteria, on identical seeded inputs:
   (1) rotated values: |y_gpu - y_ref| <= 1e-5 * max(|y_ref|, rms of y_ref's vector);
   (2) meta: fp16 scale / zero within 1 ulp (distance of ordered bit patterns);
-  (3) codes: bit-exact except where the pre-rounding value, recomputed in
-      float64 from y_ref and the GPU's own stored meta, lies within 1e-5 of
-      a rounding boundary k + 1/2 (mismatches are counted and reported);
+  (3) codes: bit-exact except where the pre-rounding value t, recomputed by
+      the oracle (binary32 decision arithmetic) from its rotated values and
+      the GPU's own stored meta, lies within 1e-5 of a rounding boundary
+      k + 1/2 (mismatches are counted and reported);
   (4) decode: relative RMS of GPU decode vs the oracle's decode (rounded to
       the storage dtype) <= 1e-3 per (layer, K/V) slice.
 """
@@ -66,9 +67,9 @@ def check_rows(x_bits, dtype, bits, group, seed, codes_gpu, meta_gpu, boundary=B
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     N, D = x_bits.shape
     s = oracle.sign_vector(seed, D)
-    y = oracle.rotate(oracle.storage_to_f64(x_bits, dtype), s)
-    scale, zero = oracle.group_meta(y, group, bits)
-    q_ref, _ = oracle.quantize(y, scale, zero, group, bits)
+    u = oracle.rotate_raw(oracle.storage_to_f64(x_bits, dtype), s)
+    scale, zero = oracle.group_meta(u, group, bits)
+    q_ref, _ = oracle.quantize(u, scale, zero, group, bits)
     sg = np.asarray(meta_gpu[..., 0], dtype=np.uint16)
     zg = np.asarray(meta_gpu[..., 1], dtype=np.uint16)
     ds = np.abs(ordered16(sg) - ordered16(scale.view(np.uint16)))
@@ -77,14 +78,10 @@ def check_rows(x_bits, dtype, bits, group, seed, codes_gpu, meta_gpu, boundary=B
         "meta differs by more than one fp16 ulp (scale %d, zero %d)" % (ds.max(), dz.max())
     rep = CodeReport(vectors=N, groups=ds.size, meta_diff_groups=int(((ds > 0) | (dz > 0)).sum()))
     q_gpu = oracle.unpack_codes(np.asarray(codes_gpu, dtype=np.uint8), bits, D)
-    # pre-rounding value from the oracle's y and the GPU's own stored meta
-    sf = sg.view(np.float16).astype(np.float64)
-    zf = zg.view(np.float16).astype(np.float64)
-    yg = y.reshape(N, D // group, group)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        t = np.where(sf[..., None] > 0, (yg - zf[..., None]) / np.where(sf > 0, sf, 1)[..., None], 0.0)
-    t = t.reshape(N, D)
-    q_exp = np.clip(np.rint(t), 0, 2 ** bits - 1)
+    # pre-rounding value from the oracle's rotated values and the GPU's own
+    # stored meta, in the oracle's binary32 decision arithmetic
+    t = oracle.code_values(u, sg.view(np.float16), zg.view(np.float16), group)
+    q_exp = np.rint(np.clip(t, 0, 2 ** bits - 1))
     dist = np.abs(t - (np.floor(t) + 0.5))
     near = dist < boundary
     neighbor = (q_gpu == np.floor(t)) | (q_gpu == np.floor(t) + 1)
