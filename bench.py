@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b_4k")
-    ap.add_argument("--cpu-sample-chunks", type=int, default=48)
+    ap.add_argument("--cpu-sample-chunks", type=int, default=192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
