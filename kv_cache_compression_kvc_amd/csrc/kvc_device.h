@@ -16,15 +16,15 @@
  * Work decomposition (one wave64 per workgroup, persistent grid):
  *   - an item is a tile of up to 64 consecutive head_dim vectors of one
  *     (layer, K/V) slab, contiguous in the KV tensor or in one pool block;
- *   - the wave loads the tile with fully coalesced 16-byte loads (1 KiB per
- *     instruction), transposes it through LDS (rows padded by 16 bytes so
- *     that both the row-wise writes and the per-lane reads are free of bank
- *     conflicts), and then every lane owns one whole vector in registers;
+ *   - the tile reaches LDS by DMA (global_load_lds_dwordx4: 1 KiB per
+ *     instruction, fully coalesced, no register staging), laid out with an
+ *     XOR swizzle so that the per-lane row reads are free of bank conflicts;
+ *     every lane then owns one whole vector in registers;
  *   - the Walsh-Hadamard butterfly, the group min/max, the fp16 meta, the
  *     quantization and the packing all run inside the lane: no cross-lane
  *     traffic, no intermediate in memory;
- *   - the next tile's loads are issued before the current tile is
- *     computed, so HBM reads overlap the arithmetic.
+ *   - as soon as the rows are in registers the DMA of the wave's next tile
+ *     starts into the same buffer, so HBM reads overlap the arithmetic.
  */
 #ifndef KVC_DEVICE_H
 #define KVC_DEVICE_H
@@ -36,6 +36,18 @@
 
 namespace kvc {
 namespace dev {
+
+/* Register budget: at least this many waves per SIMD (512 / N registers per
+ * lane), so that other waves can issue while one waits on LDS or memory. */
+#ifndef KVC_WAVES_PER_EU
+#define KVC_WAVES_PER_EU 2
+#endif
+#define KVC_KERNEL __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(KVC_WAVES_PER_EU)))
+
+/* Phase boundary for the instruction scheduler: nothing moves across it, so
+ * loads of a later phase are not hoisted into an earlier one (which would
+ * keep their results live over the 128-register transform). */
+#define KVC_PHASE() __builtin_amdgcn_sched_barrier(0)
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -184,72 +196,141 @@ __device__ __forceinline__ void unpack_word(uint32_t u, float* q) {
   }
 }
 
-/* ---- tiles ----------------------------------------------------------------- */
+/* ---- work items ------------------------------------------------------------ */
 
 struct Tile {
-  const uint8_t* src;  // first byte of the tile's source rows
-  uint8_t* dst;        // first byte of the tile's destination rows
-  uint8_t* codes;      // first code row of the tile (in the blob)
-  uint8_t* meta;       // first meta entry of the tile (in the blob)
+  const uint8_t* src;  // first byte of the tile's vectors in the KV tensor / pool
+  uint8_t* codes;      // first code row of the tile in the blob
+  uint8_t* meta;       // first meta entry of the tile in the blob
   int count;           // valid vectors, 1..64
 };
 
+/* Zero the two padding runs of one blob (one wave, byte stores, < 512 bytes):
+ * [codes_end, meta_start) and [meta_end, blob_end). */
+__device__ __noinline__ void write_padding(uint8_t* blob, uint64_t codes_end, uint64_t meta_start,
+                                           uint64_t meta_end, uint64_t blob_end) {
+  for (uint64_t p = codes_end + threadIdx.x; p < meta_start; p += 64) blob[p] = 0;
+  for (uint64_t p = meta_end + threadIdx.x; p < blob_end; p += 64) blob[p] = 0;
+}
+
 __device__ __forceinline__ uint64_t align256(uint64_t n) { return (n + 255u) & ~uint64_t(255); }
 
+/* Wave-uniform read of a value that no kernel of the launch writes (block
+ * table, lengths, offsets): through the constant address space, so it
+ * becomes a scalar load and never joins the vector-memory wait counter. */
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 /*
- * Map an item index to a tile.  Contiguous items always exist; paged items
- * for blocks past a request's length are skipped (returns false), as are
- * items whose table entry, length or blob extent is invalid (bit 0 of
- * *err is then set).  `tensor` is the KV-tensor side (source of an encode,
- * destination of a decode), `blob` the encoded side.
+ * Wave-uniform position in a launch's item space, advanced by the grid size
+ * without divisions.  Contiguous items are (slab i, tile) in radix
+ * tiles_per_slab; paged items are (slab i, request r, block j, subtile sub)
+ * in radices (num_reqs, max_blocks, subtiles).
  */
-template <int D>
-__device__ __forceinline__ bool item_tile(const LaunchArgs& a, int64_t item, const uint8_t* tensor,
-                                          uint8_t* blob, Tile& t) {
+struct Cursor {
+  int64_t item, i, tile, di, dtile;
+  int32_t r, j, sub, dr, dj, dsub;
+};
+
+__device__ __forceinline__ void split_paged(const LaunchArgs& a, int64_t x, int64_t& i, int32_t& r,
+                                            int32_t& j, int32_t& sub) {
+  sub = static_cast<int32_t>(x % a.subtiles);
+  x /= a.subtiles;
+  j = static_cast<int32_t>(x % a.max_blocks);
+  x /= a.max_blocks;
+  r = static_cast<int32_t>(x % a.num_reqs);
+  i = x / a.num_reqs;
+}
+
+__device__ __forceinline__ void cursor_init(const LaunchArgs& a, Cursor& c) {
+  const int64_t start = blockIdx.x, step = gridDim.x;
+  c.item = start;
+  if (!a.paged) {
+    c.i = start / a.tiles_per_slab;
+    c.tile = start - c.i * a.tiles_per_slab;
+    c.di = step / a.tiles_per_slab;
+    c.dtile = step - c.di * a.tiles_per_slab;
+  } else {
+    split_paged(a, start, c.i, c.r, c.j, c.sub);
+    split_paged(a, step, c.di, c.dr, c.dj, c.dsub);
+  }
+}
+
+__device__ __forceinline__ void cursor_next(const LaunchArgs& a, Cursor& c) {
+  c.item += gridDim.x;
+  if (!a.paged) {
+    c.tile += c.dtile;
+    c.i += c.di;
+    if (c.tile >= a.tiles_per_slab) {
+      c.tile -= a.tiles_per_slab;
+      ++c.i;
+    }
+    return;
+  }
+  c.sub += c.dsub;
+  int32_t carry = c.sub >= a.subtiles;
+  if (carry) c.sub -= a.subtiles;
+  c.j += c.dj + carry;
+  carry = c.j >= a.max_blocks;
+  if (carry) c.j -= a.max_blocks;
+  c.r += c.dr + carry;
+  carry = c.r >= a.num_reqs;
+  if (carry) c.r -= a.num_reqs;
+  c.i += c.di + carry;
+}
+
+/*
+ * The tile of the cursor's item.  Paged items past a request's length are
+ * skipped (false), as are items whose table entry, length or blob extent is
+ * invalid (bit 0 of *err is then set).  `tensor` is the KV side (source of
+ * an encode, destination of a decode), `blob` the encoded side.  With PAD,
+ * the first tile of each blob (of the launch that owns slab 0) also zeroes
+ * that blob's padding, right when it is found.
+ */
+template <int D, bool PAD>
+__device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c, const uint8_t* tensor,
+                                            uint8_t* blob, Tile& t) {
   constexpr int64_t vec_bytes = int64_t(D) * 2;
   if (!a.paged) {
-    const int64_t i = item / a.tiles_per_slab;
-    const int64_t v0 = (item - i * a.tiles_per_slab) * kTileVectors;
-    const int64_t s = i * a.slab_step + a.slab_first;
+    const int64_t v0 = c.tile * kTileVectors;
+    const int64_t s = c.i * a.slab_step + a.slab_first;
     const int64_t l = s >> 1, kv = s & 1;
     const int64_t row = kv ? a.row_v : a.row_k;
     t.count = static_cast<int>(a.rows - v0 < kTileVectors ? a.rows - v0 : kTileVectors);
     t.src = tensor + (s * a.rows + v0) * vec_bytes;
     t.codes = blob + l * a.rows * (a.row_k + a.row_v) + kv * a.rows * a.row_k + v0 * row;
     t.meta = blob + a.meta_offset + (s * a.rows + v0) * a.groups * 4;
+    if (PAD && c.item == 0 && a.slab_first == 0)
+      write_padding(blob, uint64_t(a.layers) * a.rows * (a.row_k + a.row_v), a.meta_offset,
+                    a.meta_offset + uint64_t(a.layers) * 2 * a.rows * a.groups * 4, a.blob_total);
     return true;
   }
-  const int64_t per_req = int64_t(a.max_blocks) * a.subtiles;
-  const int64_t per_slab = per_req * a.num_reqs;
-  const int64_t i = item / per_slab;
-  int64_t rem = item - i * per_slab;
-  const int32_t r = static_cast<int32_t>(rem / per_req);
-  rem -= int64_t(r) * per_req;
-  const int32_t j = static_cast<int32_t>(rem / a.subtiles);
-  const int32_t sub = static_cast<int32_t>(rem - int64_t(j) * a.subtiles);
-  const int32_t len = a.lens[r];
+  const int32_t len = ld_const(a.lens + c.r);
   if (len < 0 || int64_t(len) > int64_t(a.max_blocks) * a.block_size) {
-    if (a.err && j == 0 && sub == 0) atomicOr(a.err, 1);
+    if (a.err && c.j == 0 && c.sub == 0) atomicOr(a.err, 1);
     return false;
   }
-  const int32_t first_tok = j * a.block_size;
+  const int32_t first_tok = c.j * a.block_size;
   if (first_tok >= len) return false;
   const int32_t ntok = min(a.block_size, len - first_tok);
-  const int32_t v0 = sub * kTileVectors;
+  const int32_t v0 = c.sub * kTileVectors;
   const int32_t nvec = ntok * a.heads;
   if (v0 >= nvec) return false;
-  const int32_t blk = a.table[int64_t(r) * a.max_blocks + j];
-  const int64_t off = a.offsets[r];
+  const int32_t blk = ld_const(a.table + int64_t(c.r) * a.max_blocks + c.j);
+  const int64_t off = ld_const(a.offsets + c.r);
   const int64_t rows = int64_t(len) * a.heads;
   const uint64_t codes_bytes = uint64_t(a.layers) * rows * (a.row_k + a.row_v);
   const uint64_t meta_start = align256(codes_bytes);
-  const uint64_t total = meta_start + align256(uint64_t(a.layers) * 2 * rows * a.groups * 4);
-  if (blk < 0 || blk >= a.num_blocks || off < 0 || (off & 15) ||
-      uint64_t(off) > a.blob_bytes || total > a.blob_bytes - uint64_t(off)) {
+  const uint64_t meta_end = meta_start + uint64_t(a.layers) * 2 * rows * a.groups * 4;
+  const uint64_t total = align256(meta_end);
+  if (blk < 0 || blk >= a.num_blocks || off < 0 || (off & 15) || uint64_t(off) > a.blob_bytes ||
+      total > a.blob_bytes - uint64_t(off)) {
     if (a.err) atomicOr(a.err, 1);
     return false;
   }
-  const int64_t s = i * a.slab_step + a.slab_first;
+  const int64_t s = c.i * a.slab_step + a.slab_first;
   const int64_t l = s >> 1, kv = s & 1;
   const int64_t row = kv ? a.row_v : a.row_k;
   const int64_t row0 = int64_t(first_tok) * a.heads + v0;  // t*H + h of the tile's first vector
@@ -258,107 +339,143 @@ __device__ __forceinline__ bool item_tile(const LaunchArgs& a, int64_t item, con
   uint8_t* rb = blob + off;
   t.codes = rb + l * rows * (a.row_k + a.row_v) + kv * rows * a.row_k + row0 * row;
   t.meta = rb + meta_start + (s * rows + row0) * a.groups * 4;
+  if (PAD && c.i == 0 && c.j == 0 && c.sub == 0 && a.slab_first == 0)
+    write_padding(rb, codes_bytes, meta_start, meta_end, total);
   return true;
 }
 
-/* Advance `item` (stride gridDim.x) to the next item that maps to a tile. */
-template <int D>
-__device__ __forceinline__ bool next_tile(const LaunchArgs& a, int64_t& item, const uint8_t* tensor,
-                                          uint8_t* blob, Tile& t) {
-  while (item < a.total_items) {
-    if (item_tile<D>(a, item, tensor, blob, t)) return true;
-    item += gridDim.x;
+/* Advance to the next item of this wave that maps to a tile. */
+template <int D, bool PAD>
+__device__ __forceinline__ bool next_tile(const LaunchArgs& a, Cursor& c, const uint8_t* tensor, uint8_t* blob,
+                                          Tile& t, bool first) {
+  if (!first) cursor_next(a, c);
+  while (c.item < a.total_items) {
+    if (cursor_tile<D, PAD>(a, c, tensor, blob, t)) return true;
+    cursor_next(a, c);
   }
   return false;
 }
 
-/* Zero the padding of a blob whose codes / meta sections end at the given
- * offsets (one wave, byte stores; at most 2 * 255 bytes). */
-__device__ void zero_padding(uint8_t* blob, uint64_t codes_bytes, uint64_t meta_start,
-                             uint64_t meta_end, uint64_t total) {
-  for (uint64_t p = codes_bytes + threadIdx.x; p < meta_start; p += 64) blob[p] = 0;
-  for (uint64_t p = meta_end + threadIdx.x; p < total; p += 64) blob[p] = 0;
+/* ---- LDS staging ------------------------------------------------------------- */
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+/*
+ * Synchronization inside a one-wave workgroup.  LDS instructions of a wave
+ * execute in order, so cross-lane exchange through LDS needs only that the
+ * compiler keeps program order (a memory clobber) -- no workgroup barrier,
+ * whose release fence would also wait for every outstanding global store.
+ *
+ * wait_vmem<N>: at most N of this wave's vector-memory operations still
+ *   outstanding (they complete in issue order), then LDS may be read: the
+ *   DMA data issued before the last N operations has landed.
+ * lds_done: every LDS access issued so far has completed (before a DMA
+ *   overwrites a buffer that was just read).
+ */
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__device__ void zero_padding_for(const LaunchArgs& a, int64_t item, uint8_t* blob) {
-  if (a.slab_first != 0) return;  // the K launch (or the joint launch) owns the padding
-  if (!a.paged) {
-    if (item != 0) return;
-    const uint64_t codes_bytes = uint64_t(a.layers) * a.rows * (a.row_k + a.row_v);
-    zero_padding(blob, codes_bytes, a.meta_offset,
-                 a.meta_offset + uint64_t(a.layers) * 2 * a.rows * a.groups * 4, a.blob_total);
-    return;
-  }
-  // paged: the item of (slab 0, request r, block 0, subtile 0) pads request r
-  const int64_t per_req = int64_t(a.max_blocks) * a.subtiles;
-  if (item >= per_req * a.num_reqs || item % per_req != 0) return;
-  const int32_t r = static_cast<int32_t>(item / per_req);
-  const int64_t rows = int64_t(a.lens[r]) * a.heads;
-  const uint64_t codes_bytes = uint64_t(a.layers) * rows * (a.row_k + a.row_v);
-  const uint64_t meta_start = align256(codes_bytes);
-  const uint64_t meta_end = meta_start + uint64_t(a.layers) * 2 * rows * a.groups * 4;
-  zero_padding(blob + a.offsets[r], codes_bytes, meta_start, meta_end, align256(meta_end));
+__device__ __forceinline__ void lds_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+/* This lane's index as a value the compiler cannot see through: address
+ * arithmetic derived from it stays inside the loop that uses it instead of
+ * being hoisted out and held in registers (or spilled) across the loop. */
+__device__ __forceinline__ int opaque_lane() {
+  int v = threadIdx.x;
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
-/* Coalesced load of a tile: chunk c = k*64 + lane of the tile's 16-byte
- * chunks goes to st[k]; chunks past the valid vectors read as zero. */
+/*
+ * Tile of `count` vectors of D 16-bit elements -> LDS by DMA
+ * (global_load_lds_dwordx4, no register staging).  Instruction k copies the
+ * k-th KiB of the tile; its lanes write consecutive 16-byte LDS slots, so the
+ * row of vector v occupies slots [v*CH, v*CH + CH).  Lane l of instruction k
+ * fetches chunk p = (l % CH) ^ (v % CH) of vector v = k*VPI + l / CH, so
+ * chunk p of row v lands in column p ^ (v % CH): the later per-lane row
+ * reads then hit 16 different bank groups in every 16-lane phase.
+ *
+ * The lane's byte offset inside instruction k's KiB is
+ * (l / CH) * 16 * CH + 16 * ((l % CH) ^ (v % CH)); with v % CH =
+ * ((k * VPI) % CH) | (l / CH) (no carries: VPI is a power of two and
+ * l / CH < VPI) this is L0 ^ (16 * ((k * VPI) % CH)), L0 the k = 0 offset.
+ */
 template <int D>
-__device__ __forceinline__ void load_tile(const Tile& t, v4u (&st)[D / 8]) {
-  constexpr int CH = D / 8;
-  const v4u* p = reinterpret_cast<const v4u*>(t.src);
-  const int lane = threadIdx.x;
-  if (t.count == kTileVectors) {
+__device__ __forceinline__ void dma_rows(const uint8_t* src, int count, v4u* lds) {
+  constexpr int CH = D / 8, VPI = 64 / CH;
+  const int lane = opaque_lane();
+  const int vin = lane / CH, col = lane % CH;
+  const uint32_t l0 = uint32_t(vin * CH * 16 + 16 * (col ^ vin));
+  if (count == kTileVectors) {
 #pragma unroll
-    for (int k = 0; k < CH; ++k) st[k] = __builtin_nontemporal_load(p + k * 64 + lane);
+    for (int k = 0; k < CH; ++k) {
+      const uint32_t off = l0 ^ uint32_t(16 * ((k * VPI) % CH));
+      const uint8_t* bk = src + k * 1024;  // wave-uniform
+      __builtin_amdgcn_global_load_lds(bk + off, (lds_void*)(lds + k * 64), 16, 0, 0);
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const int c = k * 64 + lane;
-      st[k] = (c / CH < t.count) ? __builtin_nontemporal_load(p + c) : v4u{0, 0, 0, 0};
+      const uint32_t off = l0 ^ uint32_t(16 * ((k * VPI) % CH));
+      if (k * VPI + vin < count)
+        __builtin_amdgcn_global_load_lds(src + k * 1024 + off, (lds_void*)(lds + k * 64), 16, 0, 0);
     }
   }
 }
 
-/* Registers (chunk layout) -> LDS rows of RSW chunks. */
-template <int D>
-__device__ __forceinline__ void stage_rows(v4u* lds, const v4u (&st)[D / 8]) {
-  constexpr int CH = D / 8, RSW = CH + 1;
-  const int lane = threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < CH; ++k) {
-    const int c = k * 64 + lane;
-    lds[(c / CH) * RSW + (c % CH)] = st[k];
-  }
-}
-
-/* Own LDS row -> D fp32 values with the sign flip applied (exact: an xor
- * of the sign bit on the packed pair before widening). */
+/* Own LDS row -> D fp32 values with the sign flip applied (an exact xor of
+ * the sign bit on each packed pair, before widening).  Chunk p of this
+ * lane's row v is at slot v * CH + (p ^ (v % CH)) = base ^ p. */
 template <int D, int DT>
-__device__ __forceinline__ void read_signed(const v4u* lds, const LaunchArgs& a, float (&y)[D]) {
-  constexpr int CH = D / 8, RSW = CH + 1;
-  const v4u* row = lds + threadIdx.x * RSW;
+__device__ __forceinline__ void read_row_signed(const v4u* lds, const uint32_t* signs, float (&y)[D]) {
+  constexpr int CH = D / 8;
+  const int v = opaque_lane();
+  const int base = v * CH + (v % CH);
+  const v4u* sg = reinterpret_cast<const v4u*>(signs);
 #pragma unroll
   for (int p = 0; p < CH; ++p) {
-    const v4u w = row[p];
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const v4u w = lds[base ^ p];
+    const v4u s = sg[p];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * p + i;
-      unpack_pair<DT>(ws[i] ^ a.sign_words[m], y[2 * m], y[2 * m + 1]);
-    }
+    for (int i = 0; i < 4; ++i) unpack_pair<DT>(w[i] ^ s[i], y[8 * p + 2 * i], y[8 * p + 2 * i + 1]);
   }
+}
+
+/* Sign words into LDS (word m: bit 15 / 31 set when element 2m / 2m + 1 flips). */
+__device__ __forceinline__ void load_signs(const LaunchArgs& a, uint32_t* signs) {
+  signs[threadIdx.x] = a.sign_words[threadIdx.x];
 }
 
 /* ---- encode ---------------------------------------------------------------- */
 
-template <int D, int DT, int B, int G>
-__device__ __forceinline__ void encode_vector(const LaunchArgs& a, float (&y)[D], const Tile& t) {
+template <int B>
+__device__ __forceinline__ void quantize_group(const float* y, float A, float Bz, bool clamp, uint32_t* words) {
+  constexpr int VPW = 32 / B;
+  constexpr float QMAX = float((1 << B) - 1);
+  (void)VPW;
+  float tq[VPW];
+#pragma unroll
+  for (int k = 0; k < VPW; ++k) {
+    const float t = fmaf(y[k], A, Bz);
+    tq[k] = clamp ? fminf(t, QMAX) : t;
+  }
+  *words = pack_word<B>(tq);
+}
+
+template <int D, int B, int G>
+__device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t) {
   constexpr int NG = D / G;
   constexpr float QMAX = float((1 << B) - 1);
   constexpr float RS = Norm<D>::inv_sqrt;
   constexpr int WPG = G * B / 32;  // code words per group
   constexpr int VPW = 32 / B;      // values per code word
   fwht<D>(y);
+  KVC_PHASE();
   uint32_t meta[NG];
   uint32_t words[D * B / 32];
 #pragma unroll
@@ -388,22 +505,25 @@ __device__ __forceinline__ void encode_vector(const LaunchArgs& a, float (&y)[D]
       Bz = -zf * inv;
     }
     meta[g] = sb | (zb << 16);
+    // t = fma(u, A, Bz) is monotone in u (A >= 0), so the group's largest
+    // t is the one of its maximum: below 2^b - 1/2 no code can exceed
+    // 2^b - 1 and the clamp min(t, 2^b - 1) cannot change any code.  Only a
+    // degenerate group (huge offset, tiny range) takes the clamping path.
+    const bool clamp = !(fmaf(mx, A, Bz) < QMAX + 0.5f);
+    if (!clamp) {
 #pragma unroll
-    for (int w = 0; w < WPG; ++w) {
-      float tq[VPW];
-      // t = fma(u, A, Bz), clamped above at 2^b - 1 (the byte conversion
-      // clamps below at 0 and rounds half to even)
+      for (int w = 0; w < WPG; ++w) quantize_group<B>(&y[g * G + w * VPW], A, Bz, false, &words[g * WPG + w]);
+    } else {
 #pragma unroll
-      for (int k = 0; k < VPW; ++k) tq[k] = fminf(fmaf(y[g * G + w * VPW + k], A, Bz), QMAX);
-      words[g * WPG + w] = pack_word<B>(tq);
+      for (int w = 0; w < WPG; ++w) quantize_group<B>(&y[g * G + w * VPW], A, Bz, true, &words[g * WPG + w]);
     }
+    KVC_PHASE();
   }
   if (static_cast<int>(threadIdx.x) < t.count) {
     constexpr int RB = D * B / 8;
     v4u* crow = reinterpret_cast<v4u*>(t.codes + threadIdx.x * RB);
 #pragma unroll
-    for (int c = 0; c < RB / 16; ++c)
-      crow[c] = v4u{words[4 * c], words[4 * c + 1], words[4 * c + 2], words[4 * c + 3]};
+    for (int c = 0; c < RB / 16; ++c) crow[c] = v4u{words[4 * c], words[4 * c + 1], words[4 * c + 2], words[4 * c + 3]};
     uint32_t* mrow = reinterpret_cast<uint32_t*>(t.meta) + threadIdx.x * NG;
     if constexpr (NG == 1) {
       mrow[0] = meta[0];
@@ -415,46 +535,58 @@ __device__ __forceinline__ void encode_vector(const LaunchArgs& a, float (&y)[D]
   }
 }
 
+/*
+ * Encode: per tile, the rows arrive in LDS by DMA; each lane reads its own
+ * row into registers, the wave then starts the DMA of its next tile into the
+ * same buffer and computes the current one while that load is in flight.
+ */
 template <int D, int DT, int B, int G>
-__global__ __launch_bounds__(64) void encode_kernel(const LaunchArgs a) {
-  constexpr int CH = D / 8, RSW = CH + 1;
-  __shared__ v4u lds[kTileVectors * RSW];
+KVC_KERNEL void encode_kernel(const LaunchArgs a) {
+  constexpr int CH = D / 8;
+  __shared__ v4u lds[kTileVectors * CH];
+  __shared__ uint32_t signs[64];
   const uint8_t* tensor = static_cast<const uint8_t*>(a.src);
   uint8_t* blob = static_cast<uint8_t*>(a.dst);
-  int64_t item = blockIdx.x;
+  load_signs(a, signs);
+  Cursor c;
+  cursor_init(a, c);
   Tile cur;
-  if (!next_tile<D>(a, item, tensor, blob, cur)) return;
-  zero_padding_for(a, item, blob);
-  v4u st[CH];
-  load_tile<D>(cur, st);
+  if (!next_tile<D, true>(a, c, tensor, blob, cur, true)) return;
+  dma_rows<D>(cur.src, cur.count, lds);
+  wait_vmem<0>();
+  lds_order();
   for (;;) {
-    __syncthreads();  // previous tile's rows fully read
-    stage_rows<D>(lds, st);
-    __syncthreads();  // this tile's rows visible to every lane
-    int64_t nitem = item + gridDim.x;
-    Tile nxt;
-    const bool more = next_tile<D>(a, nitem, tensor, blob, nxt);
-    if (more) {
-      zero_padding_for(a, nitem, blob);
-      load_tile<D>(nxt, st);
-    }
     float y[D];
-    read_signed<D, DT>(lds, a, y);
-    encode_vector<D, DT, B, G>(a, y, cur);
+    read_row_signed<D, DT>(lds, signs, y);
+    KVC_PHASE();
+    lds_done();  // every lane's row is in registers: the buffer is free
+    Tile nxt;
+    const bool more = next_tile<D, true>(a, c, tensor, blob, nxt, false);
+    if (more) dma_rows<D>(nxt.src, nxt.count, lds);
+    KVC_PHASE();
+    encode_vector<D, B, G>(y, cur);
     if (!more) break;
+    // outstanding: the next tile's DMA, then this tile's code and meta
+    // stores (RB / 16 + 1 instructions, issued by the lanes < count)
+    wait_vmem<D * B / 128 + 1>();
+    lds_order();
     cur = nxt;
-    item = nitem;
   }
 }
 
 /* ---- decode ---------------------------------------------------------------- */
 
+/* A tile's codes and meta for one lane (its own row), held in registers:
+ * RB / 16 16-byte chunks and D / G meta words. */
 template <int D, int B, int G>
 struct CodeRegs {
   v4u codes[D * B / 128];
   uint32_t meta[D / G];
 };
 
+/* Prefetch of this lane's code row and meta entries (lanes past the tile's
+ * count load nothing).  Plain vector loads: their wait counts are tracked per
+ * register, so the compiler waits for them only where they are used. */
 template <int D, int B, int G>
 __device__ __forceinline__ void load_codes(const Tile& t, CodeRegs<D, B, G>& r) {
   constexpr int RB = D * B / 8, NG = D / G;
@@ -462,7 +594,7 @@ __device__ __forceinline__ void load_codes(const Tile& t, CodeRegs<D, B, G>& r) 
   if (lane < t.count) {
     const v4u* crow = reinterpret_cast<const v4u*>(t.codes + lane * RB);
 #pragma unroll
-    for (int c = 0; c < RB / 16; ++c) r.codes[c] = __builtin_nontemporal_load(crow + c);
+    for (int p = 0; p < RB / 16; ++p) r.codes[p] = __builtin_nontemporal_load(crow + p);
     const uint32_t* mrow = reinterpret_cast<const uint32_t*>(t.meta) + lane * NG;
     if constexpr (NG == 1) {
       r.meta[0] = __builtin_nontemporal_load(mrow);
@@ -472,31 +604,40 @@ __device__ __forceinline__ void load_codes(const Tile& t, CodeRegs<D, B, G>& r) 
       r.meta[1] = m.y;
     } else {
       const v4u m = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(mrow));
-      r.meta[0] = m.x;
-      r.meta[1] = m.y;
-      r.meta[2] = m.z;
-      r.meta[3] = m.w;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) r.meta[g] = m[g];
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < RB / 16; ++c) r.codes[c] = v4u{0, 0, 0, 0};
+    for (int p = 0; p < RB / 16; ++p) r.codes[p] = v4u{0, 0, 0, 0};
 #pragma unroll
     for (int g = 0; g < NG; ++g) r.meta[g] = 0;
   }
 }
 
+/*
+ * Decode: per tile, each lane dequantizes its own vector from the prefetched
+ * codes, runs the butterfly, packs to the storage type with the sign flip and
+ * writes its row to LDS, half a row at a time; the wave then stores the half
+ * rows with coalesced 16-byte stores.  The next tile's codes are loaded into
+ * registers while the current one is computed.
+ */
 template <int D, int DT, int B, int G>
-__global__ __launch_bounds__(64) void decode_kernel(const LaunchArgs a) {
-  constexpr int CH = D / 8, RSW = CH + 1, NG = D / G;
+KVC_KERNEL void decode_kernel(const LaunchArgs a) {
+  constexpr int CH = D / 8, NG = D / G;
   constexpr float RS = Norm<D>::inv_sqrt;
   constexpr int WPG = G * B / 32, VPW = 32 / B;
-  __shared__ v4u lds[kTileVectors * RSW];
+  constexpr int HALF = CH / 2;                    // chunks per row staged at a time
+  __shared__ v4u lds_out[kTileVectors * HALF];    // half of every row of the tile
+  __shared__ uint32_t signs[64];
   uint8_t* tensor = static_cast<uint8_t*>(a.dst);
   uint8_t* blob = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.src));
   const int lane = threadIdx.x;
-  int64_t item = blockIdx.x;
+  load_signs(a, signs);
+  Cursor c;
+  cursor_init(a, c);
   Tile cur;
-  if (!next_tile<D>(a, item, tensor, blob, cur)) return;
+  if (!next_tile<D, false>(a, c, tensor, blob, cur, true)) return;
   CodeRegs<D, B, G> cr;
   load_codes<D, B, G>(cur, cr);
   for (;;) {
@@ -509,70 +650,78 @@ __global__ __launch_bounds__(64) void decode_kernel(const LaunchArgs a) {
 #pragma unroll
       for (int w = 0; w < WPG; ++w) {
         const int wi = g * WPG + w;
-        const v4u c4 = cr.codes[wi / 4];
-        const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w};
         float q[VPW];
-        unpack_word<B>(cw[wi % 4], q);
+        unpack_word<B>(cr.codes[wi / 4][wi % 4], q);
 #pragma unroll
         for (int k = 0; k < VPW; ++k) y[g * G + w * VPW + k] = fmaf(q[k], sc, ze);
       }
     }
-    int64_t nitem = item + gridDim.x;
+    KVC_PHASE();
     Tile nxt;
-    const bool more = next_tile<D>(a, nitem, tensor, blob, nxt);
+    const bool more = next_tile<D, false>(a, c, tensor, blob, nxt, false);
     if (more) load_codes<D, B, G>(nxt, cr);
+    KVC_PHASE();
     fwht<D>(y);
-    v4u* row = lds + lane * RSW;
-    __syncthreads();  // previous tile's rows fully read
-#pragma unroll
-    for (int p = 0; p < CH; ++p) {
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * p + i;
-        w[i] = pack_pair<DT>(y[2 * m], y[2 * m + 1]) ^ a.sign_words[m];
-      }
-      row[p] = v4u{w[0], w[1], w[2], w[3]};
-    }
-    __syncthreads();  // every lane's row written
+    KVC_PHASE();
+    const v4u* sg = reinterpret_cast<const v4u*>(signs);
     v4u* out = reinterpret_cast<v4u*>(const_cast<uint8_t*>(cur.src));
 #pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int c = k * 64 + lane;
-      if (c / CH < cur.count) out[c] = lds[(c / CH) * RSW + (c % CH)];
+    for (int h = 0; h < 2; ++h) {
+      // chunks [h*HALF, h*HALF + HALF) of every row through LDS; half-row
+      // chunk q of row v sits in column q ^ (v % HALF)
+      lds_order();
+#pragma unroll
+      for (int q = 0; q < HALF; ++q) {
+        const int p = h * HALF + q;
+        const v4u s = sg[p];
+        v4u w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_pair<DT>(y[8 * p + 2 * i], y[8 * p + 2 * i + 1]) ^ s[i];
+        lds_out[(lane * HALF) + (q ^ (lane % HALF))] = w;
+        KVC_PHASE();
+      }
+      lds_order();
+#pragma unroll
+      for (int k = 0; k < HALF; ++k) {
+        const int slot = k * 64 + lane;
+        const int v = slot / HALF;
+        const int q = (slot % HALF) ^ (v % HALF);
+        if (v < cur.count) out[v * CH + h * HALF + q] = lds_out[slot];
+      }
     }
     if (!more) break;
     cur = nxt;
-    item = nitem;
   }
 }
 
 /* ---- rotate (test hook) ---------------------------------------------------- */
 
 template <int D, int DT>
-__global__ __launch_bounds__(64) void rotate_kernel(const LaunchArgs a) {
-  constexpr int CH = D / 8, RSW = CH + 1;
+KVC_KERNEL void rotate_kernel(const LaunchArgs a) {
+  constexpr int CH = D / 8;
   constexpr float RS = Norm<D>::inv_sqrt;
-  __shared__ v4u lds[kTileVectors * RSW];
+  __shared__ v4u lds[kTileVectors * CH];
+  __shared__ uint32_t signs[64];
   const uint8_t* tensor = static_cast<const uint8_t*>(a.src);
   float* yout = static_cast<float*>(a.dst);
-  for (int64_t item = blockIdx.x; item < a.total_items; item += gridDim.x) {
-    Tile t;
-    item_tile<D>(a, item, tensor, nullptr, t);
-    v4u st[CH];
-    load_tile<D>(t, st);
-    __syncthreads();
-    stage_rows<D>(lds, st);
-    __syncthreads();
+  load_signs(a, signs);
+  Cursor c;
+  cursor_init(a, c);
+  Tile t;
+  for (bool ok = next_tile<D, false>(a, c, tensor, nullptr, t, true); ok; ok = next_tile<D, false>(a, c, tensor, nullptr, t, false)) {
+    lds_done();
+    dma_rows<D>(t.src, t.count, lds);
+    wait_vmem<0>();
+    lds_order();
     float y[D];
-    read_signed<D, DT>(lds, a, y);
+    read_row_signed<D, DT>(lds, signs, y);
     fwht<D>(y);
     if (static_cast<int>(threadIdx.x) < t.count) {
       const int64_t vec = (t.src - tensor) / (2 * D) + threadIdx.x;
       float4* o = reinterpret_cast<float4*>(yout + vec * D);
 #pragma unroll
-      for (int c = 0; c < D / 4; ++c)
-        o[c] = float4(y[4 * c] * RS, y[4 * c + 1] * RS, y[4 * c + 2] * RS, y[4 * c + 3] * RS);
+      for (int q = 0; q < D / 4; ++q)
+        o[q] = float4(y[4 * q] * RS, y[4 * q + 1] * RS, y[4 * q + 2] * RS, y[4 * q + 3] * RS);
     }
   }
 }
