@@ -244,10 +244,11 @@ __device__ __forceinline__ void split_paged(const LaunchArgs& a, int64_t x, int6
   i = x / a.num_reqs;
 }
 
+template <bool PAGED>
 __device__ __forceinline__ void cursor_init(const LaunchArgs& a, Cursor& c) {
   const int64_t start = blockIdx.x, step = gridDim.x;
   c.item = start;
-  if (!a.paged) {
+  if constexpr (!PAGED) {
     c.i = start / a.tiles_per_slab;
     c.tile = start - c.i * a.tiles_per_slab;
     c.di = step / a.tiles_per_slab;
@@ -258,9 +259,10 @@ __device__ __forceinline__ void cursor_init(const LaunchArgs& a, Cursor& c) {
   }
 }
 
+template <bool PAGED>
 __device__ __forceinline__ void cursor_next(const LaunchArgs& a, Cursor& c) {
   c.item += gridDim.x;
-  if (!a.paged) {
+  if constexpr (!PAGED) {
     c.tile += c.dtile;
     c.i += c.di;
     if (c.tile >= a.tiles_per_slab) {
@@ -289,11 +291,11 @@ __device__ __forceinline__ void cursor_next(const LaunchArgs& a, Cursor& c) {
  * the first tile of each blob (of the launch that owns slab 0) also zeroes
  * that blob's padding, right when it is found.
  */
-template <int D, bool PAD>
+template <int D, bool PAD, bool PAGED>
 __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c, const uint8_t* tensor,
                                             uint8_t* blob, Tile& t) {
   constexpr int64_t vec_bytes = int64_t(D) * 2;
-  if (!a.paged) {
+  if constexpr (!PAGED) {
     const int64_t v0 = c.tile * kTileVectors;
     const int64_t s = c.i * a.slab_step + a.slab_first;
     const int64_t l = s >> 1, kv = s & 1;
@@ -345,13 +347,13 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
 }
 
 /* Advance to the next item of this wave that maps to a tile. */
-template <int D, bool PAD>
+template <int D, bool PAD, bool PAGED>
 __device__ __forceinline__ bool next_tile(const LaunchArgs& a, Cursor& c, const uint8_t* tensor, uint8_t* blob,
                                           Tile& t, bool first) {
-  if (!first) cursor_next(a, c);
+  if (!first) cursor_next<PAGED>(a, c);
   while (c.item < a.total_items) {
-    if (cursor_tile<D, PAD>(a, c, tensor, blob, t)) return true;
-    cursor_next(a, c);
+    if (cursor_tile<D, PAD, PAGED>(a, c, tensor, blob, t)) return true;
+    cursor_next<PAGED>(a, c);
   }
   return false;
 }
@@ -359,6 +361,17 @@ __device__ __forceinline__ bool next_tile(const LaunchArgs& a, Cursor& c, const 
 /* ---- LDS staging ------------------------------------------------------------- */
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+/* Cache policy of the streaming accesses (the NT bit of the DMA loads and
+ * the decode's output stores).  A contiguous tensor is read or written once,
+ * front to back, and the NT hint keeps it from displacing other lines in L2
+ * and the memory-side cache: measured on a 0.54 GB encode + decode pair, the
+ * two kernels run 15% faster back to back and the decode no longer leaves
+ * dirty lines for the next kernel to write back.  On the paged pool (16 KiB
+ * blocks scattered over the pool) the same hint made both kernels about 5%
+ * slower, so paged launches keep the default policy. */
+constexpr int kCacheDefault = 0;
+constexpr int kCacheStream = 2;
 
 /*
  * Synchronization inside a one-wave workgroup.  LDS instructions of a wave
@@ -405,8 +418,8 @@ __device__ __forceinline__ int opaque_lane() {
  * ((k * VPI) % CH) | (l / CH) (no carries: VPI is a power of two and
  * l / CH < VPI) this is L0 ^ (16 * ((k * VPI) % CH)), L0 the k = 0 offset.
  */
-template <int D>
-__device__ __forceinline__ void dma_rows(const uint8_t* src, int count, v4u* lds) {
+template <int D, int AUX>
+__device__ __forceinline__ void dma_rows_policy(const uint8_t* src, int count, v4u* lds) {
   constexpr int CH = D / 8, VPI = 64 / CH;
   const int lane = opaque_lane();
   const int vin = lane / CH, col = lane % CH;
@@ -416,16 +429,21 @@ __device__ __forceinline__ void dma_rows(const uint8_t* src, int count, v4u* lds
     for (int k = 0; k < CH; ++k) {
       const uint32_t off = l0 ^ uint32_t(16 * ((k * VPI) % CH));
       const uint8_t* bk = src + k * 1024;  // wave-uniform
-      __builtin_amdgcn_global_load_lds(bk + off, (lds_void*)(lds + k * 64), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bk + off, (lds_void*)(lds + k * 64), 16, 0, AUX);
     }
   } else {
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const uint32_t off = l0 ^ uint32_t(16 * ((k * VPI) % CH));
       if (k * VPI + vin < count)
-        __builtin_amdgcn_global_load_lds(src + k * 1024 + off, (lds_void*)(lds + k * 64), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + k * 1024 + off, (lds_void*)(lds + k * 64), 16, 0, AUX);
     }
   }
+}
+
+template <int D, bool STREAM>
+__device__ __forceinline__ void dma_rows(const uint8_t* src, int count, v4u* lds) {
+  dma_rows_policy<D, STREAM ? kCacheStream : kCacheDefault>(src, count, lds);
 }
 
 /* Own LDS row -> D fp32 values with the sign flip applied (an exact xor of
@@ -540,7 +558,7 @@ __device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t) {
  * row into registers, the wave then starts the DMA of its next tile into the
  * same buffer and computes the current one while that load is in flight.
  */
-template <int D, int DT, int B, int G>
+template <int D, int DT, int B, int G, bool PAGED>
 KVC_KERNEL void encode_kernel(const LaunchArgs a) {
   constexpr int CH = D / 8;
   __shared__ v4u lds[kTileVectors * CH];
@@ -549,10 +567,10 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
   uint8_t* blob = static_cast<uint8_t*>(a.dst);
   load_signs(a, signs);
   Cursor c;
-  cursor_init(a, c);
+  cursor_init<PAGED>(a, c);
   Tile cur;
-  if (!next_tile<D, true>(a, c, tensor, blob, cur, true)) return;
-  dma_rows<D>(cur.src, cur.count, lds);
+  if (!next_tile<D, true, PAGED>(a, c, tensor, blob, cur, true)) return;
+  dma_rows<D, !PAGED>(cur.src, cur.count, lds);
   wait_vmem<0>();
   lds_order();
   for (;;) {
@@ -561,8 +579,8 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
     KVC_PHASE();
     lds_done();  // every lane's row is in registers: the buffer is free
     Tile nxt;
-    const bool more = next_tile<D, true>(a, c, tensor, blob, nxt, false);
-    if (more) dma_rows<D>(nxt.src, nxt.count, lds);
+    const bool more = next_tile<D, true, PAGED>(a, c, tensor, blob, nxt, false);
+    if (more) dma_rows<D, !PAGED>(nxt.src, nxt.count, lds);
     KVC_PHASE();
     encode_vector<D, B, G>(y, cur);
     if (!more) break;
@@ -622,7 +640,7 @@ __device__ __forceinline__ void load_codes(const Tile& t, CodeRegs<D, B, G>& r) 
  * rows with coalesced 16-byte stores.  The next tile's codes are loaded into
  * registers while the current one is computed.
  */
-template <int D, int DT, int B, int G>
+template <int D, int DT, int B, int G, bool PAGED>
 KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   constexpr int CH = D / 8, NG = D / G;
   constexpr float RS = Norm<D>::inv_sqrt;
@@ -635,9 +653,9 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   const int lane = threadIdx.x;
   load_signs(a, signs);
   Cursor c;
-  cursor_init(a, c);
+  cursor_init<PAGED>(a, c);
   Tile cur;
-  if (!next_tile<D, false>(a, c, tensor, blob, cur, true)) return;
+  if (!next_tile<D, false, PAGED>(a, c, tensor, blob, cur, true)) return;
   CodeRegs<D, B, G> cr;
   load_codes<D, B, G>(cur, cr);
   for (;;) {
@@ -658,7 +676,7 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
     }
     KVC_PHASE();
     Tile nxt;
-    const bool more = next_tile<D, false>(a, c, tensor, blob, nxt, false);
+    const bool more = next_tile<D, false, PAGED>(a, c, tensor, blob, nxt, false);
     if (more) load_codes<D, B, G>(nxt, cr);
     KVC_PHASE();
     fwht<D>(y);
@@ -686,7 +704,12 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
         const int slot = k * 64 + lane;
         const int v = slot / HALF;
         const int q = (slot % HALF) ^ (v % HALF);
-        if (v < cur.count) out[v * CH + h * HALF + q] = lds_out[slot];
+        if (v < cur.count) {
+          if constexpr (!PAGED)
+            __builtin_nontemporal_store(lds_out[slot], out + v * CH + h * HALF + q);
+          else
+            out[v * CH + h * HALF + q] = lds_out[slot];
+        }
       }
     }
     if (!more) break;
@@ -706,11 +729,12 @@ KVC_KERNEL void rotate_kernel(const LaunchArgs a) {
   float* yout = static_cast<float*>(a.dst);
   load_signs(a, signs);
   Cursor c;
-  cursor_init(a, c);
+  cursor_init<false>(a, c);
   Tile t;
-  for (bool ok = next_tile<D, false>(a, c, tensor, nullptr, t, true); ok; ok = next_tile<D, false>(a, c, tensor, nullptr, t, false)) {
+  for (bool ok = next_tile<D, false, false>(a, c, tensor, nullptr, t, true); ok;
+       ok = next_tile<D, false, false>(a, c, tensor, nullptr, t, false)) {
     lds_done();
-    dma_rows<D>(t.src, t.count, lds);
+    dma_rows<D, false>(t.src, t.count, lds);
     wait_vmem<0>();
     lds_order();
     float y[D];

@@ -38,9 +38,9 @@ __global__ __launch_bounds__(256) void copy_kernel(const v4u* __restrict__ src, 
 
 namespace {
 
-Kernel pick(Op op, int d, int dt, int b, int g) {
-  if (d == 64) return dt == KVC_BF16 ? pick_d64_t0(op, b, g) : pick_d64_t1(op, b, g);
-  if (d == 128) return dt == KVC_BF16 ? pick_d128_t0(op, b, g) : pick_d128_t1(op, b, g);
+Kernel pick(Op op, int d, int dt, int b, int g, bool paged) {
+  if (d == 64) return dt == KVC_BF16 ? pick_d64_t0(op, b, g, paged) : pick_d64_t1(op, b, g, paged);
+  if (d == 128) return dt == KVC_BF16 ? pick_d128_t0(op, b, g, paged) : pick_d128_t1(op, b, g, paged);
   return nullptr;
 }
 
@@ -85,7 +85,7 @@ int resident_groups(Kernel k, int threads, int64_t* out) {
 
 int run_plan(Op op, const Plan& plan, void* stream) {
   for (int i = 0; i < plan.n_launch; ++i) {
-    Kernel k = pick(op, plan.head_dim, plan.dtype, plan.bits[i], plan.group);
+    Kernel k = pick(op, plan.head_dim, plan.dtype, plan.bits[i], plan.group, plan.args[i].paged != 0);
     if (!k) return KVC_ESHAPE;
     int64_t resident = 0;
     int st = resident_groups(k, 64, &resident);

@@ -11,10 +11,10 @@ using Kernel = void (*)(LaunchArgs);
 #define KVC_PICK_CAT(D, DT) pick_d##D##_t##DT
 #define KVC_PICK_NAME(D, DT) KVC_PICK_CAT(D, DT)
 
-Kernel pick_d64_t0(Op op, int bits, int group);
-Kernel pick_d64_t1(Op op, int bits, int group);
-Kernel pick_d128_t0(Op op, int bits, int group);
-Kernel pick_d128_t1(Op op, int bits, int group);
+Kernel pick_d64_t0(Op op, int bits, int group, bool paged);
+Kernel pick_d64_t1(Op op, int bits, int group, bool paged);
+Kernel pick_d128_t0(Op op, int bits, int group, bool paged);
+Kernel pick_d128_t1(Op op, int bits, int group, bool paged);
 
 }  // namespace kvc
 
