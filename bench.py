@@ -17,6 +17,9 @@ Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
                  launch time (HIP events on the launch stream), vs 8 TB/s
   break_even     encode + decode time vs the wire time the compression saves
                  at 100 and 400 Gbit/s
+  unfused        the same encode / decode run as separate kernels that pass
+                 fp32 / byte intermediates through HBM (contiguous workloads):
+                 times, stage bytes, and the fused kernels' speedup over them
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
 """
 
@@ -45,10 +48,14 @@ def parse():
     return ap.parse_args()
 
 
+# the sources the fused encode / decode kernels are built from
+FUSED_SOURCES = ["kvc_device.h", "kvc_host.cpp", "kvc_inst.hip", "kvc_launch.hip", "kvc_pick.h", "kvc_plan.h"]
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_compression_kvc_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in FUSED_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -109,6 +116,49 @@ def cpu_baseline(p, chunks):
 
 
 # ---------------------------------------------------------------------------
+# Separate-kernel comparator (same results, intermediates through HBM)
+
+def unfused_leg(kvc, p, xs, outs, dsts, a, stream, t_enc, t_dec, raw_bytes):
+    import torch
+    L, T, H, D = p.layers, p.tokens, p.kv_heads, p.head_dim
+    ws_bytes = kvc.unfused_workspace_size(L, T, H, D, p.bits_k, p.bits_v, p.group, p.dtype)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=xs[0].device)
+    nsets = len(xs)
+
+    def enc(i):
+        kvc.encode_unfused(xs[i], p.bits_k, p.bits_v, p.group, seed=p.seed, out=outs[i], workspace=ws)
+
+    def dec(i):
+        kvc.decode_unfused(outs[i], xs[i].shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed,
+                           out=dsts[i], workspace=ws)
+    for i in range(max(1, a.warmup)):
+        enc(i % nsets)
+        dec(i % nsets)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        enc(i % nsets)
+        ev[i][1].record(stream)
+        dec(i % nsets)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    te = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps / 1e3
+    td = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps / 1e3
+    del ws
+    elems = raw_bytes // 2
+    bk, bv, G = p.bits_k, p.bits_v, p.group
+    # bytes each stage reads + writes, per element (K and V halves averaged)
+    b8 = (bk + bv) / 2 / 8
+    enc_b = elems * ((2 + 4) + (4 + 4 / G) + (4 + 4 / G + 1) + (1 + b8))
+    dec_b = elems * ((b8 + 1) + (1 + 4 / G + 4) + (4 + 2))
+    return {"encode_ms": te * 1e3, "decode_ms": td * 1e3,
+            "encode_hbm_GBps": enc_b / te / 1e9, "decode_hbm_GBps": dec_b / td / 1e9,
+            "encode_bytes": int(enc_b), "decode_bytes": int(dec_b),
+            "fused_speedup_encode": te / t_enc, "fused_speedup_decode": td / t_dec,
+            "fused_speedup_step": (te + td) / (t_enc + t_dec),
+            "stages": "encode: rotate, minmax, quantize, pack, padding; decode: unpack, dequant, unrotate"}
+
 
 def main():
     a = parse()
@@ -190,6 +240,10 @@ def main():
     t_dec = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps / 1e3
     ms_per_step = wall / a.steps * 1e3
 
+    unfused = None
+    if not p.paged:
+        unfused = unfused_leg(kvc, p, xs, outs, dsts, a, stream, t_enc, t_dec, raw_bytes)
+
     # copy probe: achievable streaming bandwidth in the same run
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -245,6 +299,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counter_traffic(p.name, dominant),
                      "algorithmic_bytes_per_launch": algo_bytes, "launch_ms": t_dom * 1e3},
+        "unfused": unfused,
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline:

@@ -184,6 +184,31 @@ kvc_status kvc_debug_rotate(const kvc_desc* desc, const void* kv, float* y_out,
                             void* stream);
 
 /*
+ * Comparator for the fused kernels: the same encode / decode as kvc_encode
+ * and kvc_decode (bit-identical blob and output), computed by separate
+ * kernels -- rotate, group min/max, quantize, pack (decode: unpack,
+ * dequantize, inverse rotate) -- that pass fp32 and byte intermediates
+ * through `workspace`.  The arxivlens summary of "Beyond Compression Ratio:
+ * High-Throughput KV Compression for Disaggregated LLM Serving" (key
+ * results) compares its fused kernel with such separate kernels; its
+ * abstract names the intermediate tensor and the repeated memory accesses
+ * as what fusion removes.  Contiguous tensors only.
+ *
+ * kvc_unfused_workspace_size: bytes of device workspace both calls need
+ * for desc's shape (5 bytes per element plus alignment; 0 for an empty
+ * tensor).  Host only.
+ * kvc_encode_unfused / kvc_decode_unfused: arguments as kvc_encode /
+ * kvc_decode, plus a caller-owned device workspace (16-byte aligned,
+ * workspace_bytes >= the size above, else KVC_ENOSPC) whose contents are
+ * overwritten.  Calls that share a workspace must be ordered on one stream.
+ */
+kvc_status kvc_unfused_workspace_size(const kvc_desc* desc, uint64_t* bytes);
+kvc_status kvc_encode_unfused(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes,
+                              void* workspace, uint64_t workspace_bytes, void* stream);
+kvc_status kvc_decode_unfused(const kvc_desc* desc, const void* in, uint64_t in_bytes, void* kv_out,
+                              void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
  * Measurement helper: copy `bytes` (a multiple of 16) from src to dst with
  * 16-byte streaming loads and stores, to measure the achievable HBM
  * bandwidth next to the encode / decode kernels.

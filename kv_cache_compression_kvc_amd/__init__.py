@@ -26,6 +26,7 @@ from ._lib import KvcDesc, KvcPaged, KvcError, DTYPE
 __all__ = [
     "KvcError", "DTYPE", "abi_version", "encoded_size", "sign_mask", "encode", "decode",
     "paged_layout", "encode_paged", "decode_paged", "debug_rotate", "probe_copy",
+    "unfused_workspace_size", "encode_unfused", "decode_unfused",
 ]
 
 _TORCH_TO_NAME = {torch.bfloat16: "bf16", torch.float16: "fp16"}
@@ -99,6 +100,51 @@ def decode(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, stream=N
         out = torch.empty(tuple(shape), dtype=_NAME_TO_TORCH[dtype], device=blob.device)
     d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
     _lib.check(_lib.lib().kvc_decode(ctypes.byref(d), _ptr(blob), blob.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def unfused_workspace_size(layers, tokens, kv_heads, head_dim, bits_k, bits_v, group, dtype="bf16"):
+    """Device workspace bytes of the separate-kernel comparator for this shape."""
+    n = ctypes.c_uint64()
+    d = _desc(layers, tokens, kv_heads, head_dim, dtype, bits_k, bits_v, group)
+    _lib.check(_lib.lib().kvc_unfused_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(ws, nbytes, device):
+    if ws is None:
+        ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    _check_cuda(ws)
+    return ws
+
+
+def encode_unfused(kv, bits_k, bits_v, group, seed=0, out=None, workspace=None, stream=None):
+    """Comparator: :func:`encode` computed by separate kernels through ``workspace``."""
+    _check_cuda(kv, out)
+    L, two, T, H, D = kv.shape
+    if two != 2:
+        raise ValueError("axis 1 must hold K and V")
+    dt = _TORCH_TO_NAME[kv.dtype]
+    total, _ = encoded_size(L, T, H, D, bits_k, bits_v, group, dt)
+    if out is None:
+        out = torch.empty(total, dtype=torch.uint8, device=kv.device)
+    ws = _workspace(workspace, unfused_workspace_size(L, T, H, D, bits_k, bits_v, group, dt), kv.device)
+    d = _desc(L, T, H, D, dt, bits_k, bits_v, group, seed)
+    _lib.check(_lib.lib().kvc_encode_unfused(ctypes.byref(d), _ptr(kv), _ptr(out), out.numel(), _ptr(ws),
+                                             ws.numel(), _stream(stream)))
+    return out
+
+
+def decode_unfused(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, workspace=None, stream=None):
+    """Comparator: :func:`decode` computed by separate kernels through ``workspace``."""
+    _check_cuda(blob, out)
+    L, two, T, H, D = shape
+    if out is None:
+        out = torch.empty(tuple(shape), dtype=_NAME_TO_TORCH[dtype], device=blob.device)
+    ws = _workspace(workspace, unfused_workspace_size(L, T, H, D, bits_k, bits_v, group, dtype), blob.device)
+    d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
+    _lib.check(_lib.lib().kvc_decode_unfused(ctypes.byref(d), _ptr(blob), blob.numel(), _ptr(out), _ptr(ws),
+                                             ws.numel(), _stream(stream)))
     return out
 
 

@@ -26,10 +26,11 @@ DTYPE = {"bf16": 0, "fp16": 1}
 EXPORTS = [
     "kvc_abi_version", "kvc_strerror", "kvc_encoded_size", "kvc_sign_mask", "kvc_encode",
     "kvc_decode", "kvc_paged_layout", "kvc_encode_paged", "kvc_decode_paged",
-    "kvc_debug_rotate", "kvc_probe_copy",
+    "kvc_debug_rotate", "kvc_unfused_workspace_size", "kvc_encode_unfused", "kvc_decode_unfused",
+    "kvc_probe_copy",
 ]
 HOST_EXPORTS = ["kvc_abi_version", "kvc_strerror", "kvc_encoded_size", "kvc_sign_mask",
-                "kvc_paged_layout"]
+                "kvc_paged_layout", "kvc_unfused_workspace_size"]
 
 
 class KvcDesc(ctypes.Structure):
@@ -87,6 +88,11 @@ def _declare(lib, names):
                                               P(KvcPaged), ctypes.c_void_p, ctypes.c_void_p]),
         "kvc_debug_rotate": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p]),
+        "kvc_unfused_workspace_size": (ctypes.c_int32, [P(KvcDesc), P(ctypes.c_uint64)]),
+        "kvc_encode_unfused": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                                ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
+        "kvc_decode_unfused": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
         "kvc_probe_copy": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                             ctypes.c_void_p]),
     }

@@ -471,6 +471,39 @@ __device__ __forceinline__ void load_signs(const LaunchArgs& a, uint32_t* signs)
 
 /* ---- encode ---------------------------------------------------------------- */
 
+/*
+ * Meta of one group of the normalized values y = u / sqrt(D), from the
+ * min / max of its unnormalized values u.  Every binary32 operation rounds
+ * on its own (no contraction into fused multiply-adds):
+ *   zero  = RD16(mn * rs)
+ *   scale = RU16(((mx * rs) - zero) / (2^b - 1))
+ * Returns scale | zero << 16 (the blob's little-endian meta entry).
+ */
+template <int D, int B>
+__device__ __forceinline__ uint32_t group_meta_word(float mn, float mx) {
+#pragma clang fp contract(off)
+  constexpr float RS = Norm<D>::inv_sqrt;
+  constexpr float QMAX = float((1 << B) - 1);
+  const uint32_t zb = rd16(mn * RS);
+  const float zf = f16_value(zb);
+  const float mxn = mx * RS;
+  const uint32_t sb = ru16((mxn - zf) / QMAX);
+  return sb | (zb << 16);
+}
+
+/* Code of u is round(fma(u, A, Bz)): inv = 1 / scale (0 for scale 0),
+ * A = inv * rs, Bz = -zero * inv, each rounded on its own. */
+template <int D>
+__device__ __forceinline__ void code_affine(uint32_t meta, float& A, float& Bz) {
+#pragma clang fp contract(off)
+  constexpr float RS = Norm<D>::inv_sqrt;
+  const float sf = f16_value(meta & 0xffffu);
+  const float zf = f16_value(meta >> 16);
+  const float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
+  A = inv * RS;
+  Bz = -zf * inv;
+}
+
 template <int B>
 __device__ __forceinline__ void quantize_group(const float* y, float A, float Bz, bool clamp, uint32_t* words) {
   constexpr int VPW = 32 / B;
@@ -489,7 +522,6 @@ template <int D, int B, int G>
 __device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t) {
   constexpr int NG = D / G;
   constexpr float QMAX = float((1 << B) - 1);
-  constexpr float RS = Norm<D>::inv_sqrt;
   constexpr int WPG = G * B / 32;  // code words per group
   constexpr int VPW = 32 / B;      // values per code word
   fwht<D>(y);
@@ -504,25 +536,9 @@ __device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t) {
       mn = fminf(mn, y[g * G + j]);
       mx = fmaxf(mx, y[g * G + j]);
     }
-    // Meta of the normalized values y / sqrt(D).  Every binary32 operation
-    // here rounds on its own (no contraction into fused multiply-adds):
-    //   zero  = RD16(mn * rs)
-    //   scale = RU16(((mx * rs) - zero) / (2^b - 1))
-    //   inv = 1 / scale, A = inv * rs, Bz = -zero * inv
-    uint32_t zb, sb;
+    meta[g] = group_meta_word<D, B>(mn, mx);
     float A, Bz;
-    {
-#pragma clang fp contract(off)
-      zb = rd16(mn * RS);
-      const float zf = f16_value(zb);
-      const float mxn = mx * RS;
-      sb = ru16((mxn - zf) / QMAX);
-      const float sf = f16_value(sb);
-      const float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
-      A = inv * RS;
-      Bz = -zf * inv;
-    }
-    meta[g] = sb | (zb << 16);
+    code_affine<D>(meta[g], A, Bz);
     // t = fma(u, A, Bz) is monotone in u (A >= 0), so the group's largest
     // t is the one of its maximum: below 2^b - 1/2 no code can exceed
     // 2^b - 1 and the clamp min(t, 2^b - 1) cannot change any code.  Only a

@@ -114,6 +114,21 @@ int blob_sizes(const kvc_desc* d, int64_t tokens, BlobSizes* out) {
   return KVC_OK;
 }
 
+int unfused_workspace(const kvc_desc* d, uint64_t* bytes, uint64_t* fp32_offset) {
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  if (!bytes) return KVC_EINVAL;
+  uint64_t rows, elems, off, fp, total;
+  if (!mul_ok(static_cast<uint64_t>(d->tokens), static_cast<uint64_t>(d->kv_heads), &rows) ||
+      !mul_ok(rows, 2ull * static_cast<uint64_t>(d->layers), &rows) ||
+      !mul_ok(rows, static_cast<uint64_t>(d->head_dim), &elems) || !align_up(elems, &off) ||
+      !mul_ok(elems, 4, &fp) || !add_ok(off, fp, &total) || total > static_cast<uint64_t>(INT64_MAX))
+    return KVC_ESHAPE;
+  *bytes = total;
+  if (fp32_offset) *fp32_offset = off;
+  return KVC_OK;
+}
+
 int plan_contiguous(Op op, const kvc_desc* d, const void* src, void* dst,
                     uint64_t blob_bytes, Plan* plan) {
   int st = check_desc(d);
@@ -252,6 +267,10 @@ kvc_status kvc_sign_mask(uint64_t seed, int64_t head_dim, uint64_t* mask_words) 
   for (int64_t j = 0; j < head_dim; ++j)
     if (kvc::splitmix64_next(&st) >> 63) mask_words[j / 64] |= 1ull << (j % 64);
   return KVC_OK;
+}
+
+kvc_status kvc_unfused_workspace_size(const kvc_desc* desc, uint64_t* bytes) {
+  return static_cast<kvc_status>(kvc::unfused_workspace(desc, bytes, nullptr));
 }
 
 kvc_status kvc_paged_layout(const kvc_desc* desc, const int32_t* seq_lens_host,

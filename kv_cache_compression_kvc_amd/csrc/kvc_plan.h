@@ -85,6 +85,11 @@ struct BlobSizes {
 };
 int blob_sizes(const kvc_desc* d, int64_t tokens, BlobSizes* out);
 
+/* Workspace of the separate-kernel comparator for the contiguous shape in
+ * d: one byte per element (codes), then four per element (fp32) at byte
+ * *fp32_offset.  *bytes is 0 for an empty tensor. */
+int unfused_workspace(const kvc_desc* d, uint64_t* bytes, uint64_t* fp32_offset);
+
 }  // namespace kvc
 
 #endif

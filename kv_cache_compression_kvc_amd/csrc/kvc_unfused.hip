@@ -1,0 +1,477 @@
+/*
+ * kvc_unfused.hip -- the encode and decode of kvc_encode / kvc_decode as a
+ * chain of separate kernels that hand full-size intermediates to each other
+ * through HBM.  This is the comparator for the fused kernels: the arxivlens
+ * summary of "Beyond Compression Ratio: High-Throughput KV Compression for
+ * Disaggregated LLM Serving" (key results) credits the fused kernel with up
+ * to 5.9x over separate kernels, and its abstract attributes the gain to
+ * removing the intermediate tensor and the repeated memory accesses.
+ *
+ * Encode (contiguous [L, 2, T, H, D] tensors), per (layer, K/V) slab:
+ *   E1 rotate    x (bf16 / fp16)  -> u  fp32 [rows, D]  sign flip + butterfly
+ *   E2 minmax    u                -> meta (the blob's meta section)
+ *   E3 quantize  u, meta          -> q  u8 [rows, D]
+ *   E4 pack      q                -> codes (the blob's codes section)
+ *   E5 padding   zeroes the blob's two padding runs
+ * Decode:
+ *   D1 unpack    codes            -> q  u8 [rows, D]
+ *   D2 dequant   q, meta          -> z  fp32 [rows, D]  (1/sqrt(D) folded in)
+ *   D3 unrotate  z                -> x  butterfly, sign flip, round to dtype
+ *
+ * Each stage makes the same binary32 decisions as the fused kernels (same
+ * butterfly order and operand order, the same meta and code arithmetic), so
+ * the blob and the decoded tensor are bit-identical to theirs; only the
+ * memory traffic differs.  The stages are written to run near the HBM
+ * bound on their own: 256-thread blocks, vector loads and stores that are
+ * contiguous across the wave, butterfly stages across lanes by shuffles.
+ */
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "../../include/kvc.h"
+#include "kvc_device.h"
+#include "kvc_plan.h"
+
+namespace kvc {
+namespace uf {
+
+using dev::v2u;
+using dev::v4u;
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / 64;
+constexpr int kUnroll = 4;           // independent rows / units per thread per iteration
+constexpr int64_t kMaxBlocks = 8192;  // blocks per launch (all slabs together)
+
+__device__ __forceinline__ int64_t slab_of(const LaunchArgs& a) {
+  return int64_t(blockIdx.y) * a.slab_step + a.slab_first;
+}
+
+/* Butterfly stages of D values spread over D/4 consecutive lanes, 4 per
+ * lane (lane m holds elements 4m .. 4m+3): two stages inside the lane, then
+ * one exchange per stage with the lane whose index differs in bit h.  The
+ * lower element of every pair becomes a + b and the upper a - b, in the
+ * same order as the fused kernels' in-register butterfly. */
+template <int D>
+__device__ __forceinline__ void fwht_lanes(float (&v)[4], int m) {
+  float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
+  v[0] = a0 + a2;
+  v[2] = a0 - a2;
+  v[1] = a1 + a3;
+  v[3] = a1 - a3;
+#pragma unroll
+  for (int h = 1; h < D / 4; h <<= 1) {
+    const bool upper = (m & h) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float t = __shfl_xor(v[i], h);
+      v[i] = upper ? t - v[i] : v[i] + t;
+    }
+  }
+}
+
+/* ---- encode stages ---------------------------------------------------------- */
+
+/* E1: one row per D/4 lanes, 4 elements per lane. */
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads) void rotate_kernel(const LaunchArgs a, float* u) {
+  constexpr int LPR = D / 4, RPW = 64 / LPR, STEP = RPW * kUnroll;
+  const int lane = threadIdx.x & 63, m = lane % LPR, sub = lane / LPR;
+  const int64_t s = slab_of(a);
+  const v2u* x = static_cast<const v2u*>(a.src) + s * a.rows * LPR;
+  float4* y = reinterpret_cast<float4*>(u) + s * a.rows * LPR;
+  const uint32_t s0 = a.sign_words[2 * m], s1 = a.sign_words[2 * m + 1];
+  const int64_t wave = int64_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / 64;
+  const int64_t stride = int64_t(gridDim.x) * kWavesPerBlock * STEP;
+  for (int64_t r0 = wave * STEP; r0 < a.rows; r0 += stride) {  // wave-uniform
+    v2u w[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t r = r0 + k * RPW + sub;
+      w[k] = r < a.rows ? x[r * LPR + m] : v2u{0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      float v[4];
+      dev::unpack_pair<DT>(w[k].x ^ s0, v[0], v[1]);
+      dev::unpack_pair<DT>(w[k].y ^ s1, v[2], v[3]);
+      fwht_lanes<D>(v, m);
+      const int64_t r = r0 + k * RPW + sub;
+      if (r < a.rows) y[r * LPR + m] = float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+/* E2: min / max per group across G/4 lanes, then the meta word. */
+template <int D, int B, int G>
+__global__ __launch_bounds__(kThreads) void minmax_kernel(const LaunchArgs a, const float* u) {
+  constexpr int LPR = D / 4, RPW = 64 / LPR, STEP = RPW * kUnroll, GL = G / 4, NG = D / G;
+  const int lane = threadIdx.x & 63, m = lane % LPR, sub = lane / LPR;
+  const int64_t s = slab_of(a);
+  const float4* y = reinterpret_cast<const float4*>(u) + s * a.rows * LPR;
+  uint32_t* meta = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.dst) + a.meta_offset) + s * a.rows * NG;
+  const int64_t wave = int64_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / 64;
+  const int64_t stride = int64_t(gridDim.x) * kWavesPerBlock * STEP;
+  for (int64_t r0 = wave * STEP; r0 < a.rows; r0 += stride) {
+    float4 w[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t r = r0 + k * RPW + sub;
+      w[k] = r < a.rows ? y[r * LPR + m] : float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      float mn = fminf(fminf(w[k].x, w[k].y), fminf(w[k].z, w[k].w));
+      float mx = fmaxf(fmaxf(w[k].x, w[k].y), fmaxf(w[k].z, w[k].w));
+#pragma unroll
+      for (int h = 1; h < GL; h <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, h));
+        mx = fmaxf(mx, __shfl_xor(mx, h));
+      }
+      const int64_t r = r0 + k * RPW + sub;
+      if (r < a.rows && m % GL == 0) meta[r * NG + m / GL] = dev::group_meta_word<D, B>(mn, mx);
+    }
+  }
+}
+
+/* E3: 4 codes per unit (one fp32 float4 in, one u32 of bytes out). */
+template <int D, int B, int G>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const LaunchArgs a, const float* u, uint8_t* q8) {
+  constexpr float QMAX = float((1 << B) - 1);
+  constexpr int NG = D / G;
+  const int64_t s = slab_of(a);
+  const int64_t units = a.rows * (D / 4);
+  const float4* y = reinterpret_cast<const float4*>(u) + s * units;
+  uint32_t* q = reinterpret_cast<uint32_t*>(q8) + s * units;
+  const uint32_t* meta =
+      reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.dst) + a.meta_offset) + s * a.rows * NG;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; i0 < units; i0 += stride * kUnroll) {
+    float4 w[kUnroll];
+    uint32_t mw[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t i = i0 + k * stride;
+      w[k] = i < units ? y[i] : float4(0.0f, 0.0f, 0.0f, 0.0f);
+      mw[k] = i < units ? meta[i * 4 / G] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t i = i0 + k * stride;
+      float A, Bz;
+      dev::code_affine<D>(mw[k], A, Bz);
+      // min(t, 2^b - 1) changes no code of an ordinary group (every t there
+      // is below 2^b - 1/2) and bounds the codes of a degenerate one; the
+      // conversion rounds half to even and clamps below at 0
+      uint32_t c = dev::put_byte(fminf(fmaf(w[k].x, A, Bz), QMAX), 0, 0);
+      c = dev::put_byte(fminf(fmaf(w[k].y, A, Bz), QMAX), 1, c);
+      c = dev::put_byte(fminf(fmaf(w[k].z, A, Bz), QMAX), 2, c);
+      c = dev::put_byte(fminf(fmaf(w[k].w, A, Bz), QMAX), 3, c);
+      if (i < units) q[i] = c;
+    }
+  }
+}
+
+/* Bytes of the codes of one slab: start of its packed rows in the blob. */
+__device__ __forceinline__ uint8_t* codes_of(const LaunchArgs& a, uint8_t* blob, int64_t s) {
+  const int64_t l = s >> 1, kv = s & 1;
+  return blob + l * a.rows * (a.row_k + a.row_v) + kv * a.rows * a.row_k;
+}
+
+/* 32/B codes (bytes) of a unit -> one packed 32-bit word, code k at bits
+ * [B*k, B*k + B). */
+template <int B>
+__device__ __forceinline__ uint32_t pack_bytes(const uint32_t* w) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int k = 0; k < 32 / B; ++k) out |= ((w[k / 4] >> (8 * (k % 4))) & ((1u << B) - 1)) << (B * k);
+  return out;
+}
+
+template <int B>
+__device__ __forceinline__ void unpack_bytes(uint32_t p, uint32_t* w) {
+#pragma unroll
+  for (int j = 0; j < 8 / B; ++j) w[j] = 0;
+#pragma unroll
+  for (int k = 0; k < 32 / B; ++k) w[k / 4] |= ((p >> (B * k)) & ((1u << B) - 1)) << (8 * (k % 4));
+}
+
+/* E4: one packed word per unit (32/B code bytes in). */
+template <int D, int B>
+__global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, const uint8_t* q8) {
+  constexpr int IN = 32 / B / 4;  // 32-bit words of code bytes per unit
+  const int64_t s = slab_of(a);
+  const int64_t units = a.rows * D * B / 32;
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(q8 + s * a.rows * D);
+  uint32_t* out = reinterpret_cast<uint32_t*>(codes_of(a, static_cast<uint8_t*>(a.dst), s));
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; i0 < units; i0 += stride * kUnroll) {
+    uint32_t w[kUnroll][IN];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t i = i0 + k * stride;
+      if constexpr (IN == 4) {
+        const v4u t = i < units ? reinterpret_cast<const v4u*>(q)[i] : v4u{0, 0, 0, 0};
+        w[k][0] = t.x, w[k][1] = t.y, w[k][2] = t.z, w[k][3] = t.w;
+      } else if constexpr (IN == 2) {
+        const v2u t = i < units ? reinterpret_cast<const v2u*>(q)[i] : v2u{0, 0};
+        w[k][0] = t.x, w[k][1] = t.y;
+      } else {
+        w[k][0] = i < units ? q[i] : 0u;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t i = i0 + k * stride;
+      if (i < units) out[i] = pack_bytes<B>(w[k]);
+    }
+  }
+}
+
+/* E5: the blob's padding runs, one wave. */
+__global__ __launch_bounds__(64) void padding_kernel(uint8_t* blob, uint64_t codes_end, uint64_t meta_start,
+                                                     uint64_t meta_end, uint64_t blob_end) {
+  dev::write_padding(blob, codes_end, meta_start, meta_end, blob_end);
+}
+
+/* ---- decode stages ---------------------------------------------------------- */
+
+/* D1: one packed word per unit -> 32/B code bytes. */
+template <int D, int B>
+__global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a, uint8_t* q8) {
+  constexpr int OUT = 32 / B / 4;
+  const int64_t s = slab_of(a);
+  const int64_t units = a.rows * D * B / 32;
+  const uint32_t* in = reinterpret_cast<const uint32_t*>(
+      codes_of(a, const_cast<uint8_t*>(static_cast<const uint8_t*>(a.src)), s));
+  uint32_t* q = reinterpret_cast<uint32_t*>(q8 + s * a.rows * D);
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; i0 < units; i0 += stride * kUnroll) {
+    uint32_t p[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t i = i0 + k * stride;
+      p[k] = i < units ? in[i] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t i = i0 + k * stride;
+      uint32_t w[OUT];
+      unpack_bytes<B>(p[k], w);
+      if (i < units) {
+        if constexpr (OUT == 4)
+          reinterpret_cast<v4u*>(q)[i] = v4u{w[0], w[1], w[2], w[3]};
+        else if constexpr (OUT == 2)
+          reinterpret_cast<v2u*>(q)[i] = v2u{w[0], w[1]};
+        else
+          q[i] = w[0];
+      }
+    }
+  }
+}
+
+/* D2: 4 codes per unit -> 4 fp32 values z = q * scale/sqrt(D) + zero/sqrt(D). */
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const LaunchArgs a, const uint8_t* q8, float* z) {
+  constexpr float RS = dev::Norm<D>::inv_sqrt;
+  constexpr int NG = D / G;
+  const int64_t s = slab_of(a);
+  const int64_t units = a.rows * (D / 4);
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(q8) + s * units;
+  float4* out = reinterpret_cast<float4*>(z) + s * units;
+  const uint32_t* meta =
+      reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.src) + a.meta_offset) + s * a.rows * NG;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; i0 < units; i0 += stride * kUnroll) {
+    uint32_t c[kUnroll], mw[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t i = i0 + k * stride;
+      c[k] = i < units ? q[i] : 0u;
+      mw[k] = i < units ? meta[i * 4 / G] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t i = i0 + k * stride;
+      const float sc = dev::f16_value(mw[k] & 0xffffu) * RS;
+      const float ze = dev::f16_value(mw[k] >> 16) * RS;
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = fmaf(static_cast<float>((c[k] >> (8 * j)) & 0xffu), sc, ze);
+      if (i < units) out[i] = float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+/* D3: one row per D/4 lanes; butterfly, round to the storage type, sign. */
+template <int D, int DT>
+__global__ __launch_bounds__(kThreads) void unrotate_kernel(const LaunchArgs a, const float* z) {
+  constexpr int LPR = D / 4, RPW = 64 / LPR, STEP = RPW * kUnroll;
+  const int lane = threadIdx.x & 63, m = lane % LPR, sub = lane / LPR;
+  const int64_t s = slab_of(a);
+  const float4* y = reinterpret_cast<const float4*>(z) + s * a.rows * LPR;
+  v2u* x = static_cast<v2u*>(a.dst) + s * a.rows * LPR;
+  const uint32_t s0 = a.sign_words[2 * m], s1 = a.sign_words[2 * m + 1];
+  const int64_t wave = int64_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / 64;
+  const int64_t stride = int64_t(gridDim.x) * kWavesPerBlock * STEP;
+  for (int64_t r0 = wave * STEP; r0 < a.rows; r0 += stride) {
+    float4 w[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const int64_t r = r0 + k * RPW + sub;
+      w[k] = r < a.rows ? y[r * LPR + m] : float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      float v[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+      fwht_lanes<D>(v, m);
+      const int64_t r = r0 + k * RPW + sub;
+      if (r < a.rows) x[r * LPR + m] = v2u{dev::pack_pair<DT>(v[0], v[1]) ^ s0, dev::pack_pair<DT>(v[2], v[3]) ^ s1};
+    }
+  }
+}
+
+/* ---- host ---------------------------------------------------------------------- */
+
+/* Blocks in x for a slab of `work` units handled `per_block` at a time. */
+unsigned blocks_x(int64_t work, int64_t per_block, int64_t n_slabs) {
+  const int64_t need = (work + per_block - 1) / per_block;
+  const int64_t cap = std::max<int64_t>(1, kMaxBlocks / std::max<int64_t>(1, n_slabs));
+  return static_cast<unsigned>(std::max<int64_t>(1, std::min(need, cap)));
+}
+
+template <int D>
+constexpr int64_t rows_per_block() {
+  return int64_t(64 / (D / 4)) * kUnroll * kWavesPerBlock;
+}
+constexpr int64_t kUnitsPerBlock = int64_t(kThreads) * kUnroll;
+
+/* Run `fn(args_chunk, grid_y)` over the launch's slabs in chunks of at most
+ * 65535 (the grid's y limit). */
+template <typename F>
+int for_slab_chunks(const LaunchArgs& a, F fn) {
+  for (int64_t first = 0; first < a.n_slabs; first += 65535) {
+    LaunchArgs c = a;
+    c.n_slabs = std::min<int64_t>(65535, a.n_slabs - first);
+    c.slab_first = a.slab_first + first * a.slab_step;
+    fn(c, static_cast<unsigned>(c.n_slabs));
+    if (hipGetLastError() != hipSuccess) return KVC_EHIP;
+  }
+  return KVC_OK;
+}
+
+template <int D, int DT, int B, int G>
+int encode_launch(const LaunchArgs& a, hipStream_t st, uint8_t* q8, float* u) {
+  return for_slab_chunks(a, [&](const LaunchArgs& c, unsigned gy) {
+    const unsigned rx = blocks_x(c.rows, rows_per_block<D>(), c.n_slabs);
+    const unsigned ex = blocks_x(c.rows * (D / 4), kUnitsPerBlock, c.n_slabs);
+    const unsigned px = blocks_x(c.rows * D * B / 32, kUnitsPerBlock, c.n_slabs);
+    hipLaunchKernelGGL((rotate_kernel<D, DT>), dim3(rx, gy), dim3(kThreads), 0, st, c, u);
+    hipLaunchKernelGGL((minmax_kernel<D, B, G>), dim3(rx, gy), dim3(kThreads), 0, st, c, u);
+    hipLaunchKernelGGL((quantize_kernel<D, B, G>), dim3(ex, gy), dim3(kThreads), 0, st, c, u, q8);
+    hipLaunchKernelGGL((pack_kernel<D, B>), dim3(px, gy), dim3(kThreads), 0, st, c, q8);
+  });
+}
+
+template <int D, int DT, int B, int G>
+int decode_launch(const LaunchArgs& a, hipStream_t st, uint8_t* q8, float* z) {
+  return for_slab_chunks(a, [&](const LaunchArgs& c, unsigned gy) {
+    const unsigned rx = blocks_x(c.rows, rows_per_block<D>(), c.n_slabs);
+    const unsigned ex = blocks_x(c.rows * (D / 4), kUnitsPerBlock, c.n_slabs);
+    const unsigned px = blocks_x(c.rows * D * B / 32, kUnitsPerBlock, c.n_slabs);
+    hipLaunchKernelGGL((unpack_kernel<D, B>), dim3(px, gy), dim3(kThreads), 0, st, c, q8);
+    hipLaunchKernelGGL((dequant_kernel<D, G>), dim3(ex, gy), dim3(kThreads), 0, st, c, q8, z);
+    hipLaunchKernelGGL((unrotate_kernel<D, DT>), dim3(rx, gy), dim3(kThreads), 0, st, c, z);
+  });
+}
+
+template <bool ENC, int D, int DT, int B>
+int dispatch_g(int g, const LaunchArgs& a, hipStream_t st, uint8_t* q8, float* f) {
+  switch (g) {
+    case 32: return ENC ? encode_launch<D, DT, B, 32>(a, st, q8, f) : decode_launch<D, DT, B, 32>(a, st, q8, f);
+    case 64: return ENC ? encode_launch<D, DT, B, 64>(a, st, q8, f) : decode_launch<D, DT, B, 64>(a, st, q8, f);
+    case 128:
+      if constexpr (D >= 128)
+        return ENC ? encode_launch<D, DT, B, 128>(a, st, q8, f) : decode_launch<D, DT, B, 128>(a, st, q8, f);
+      return KVC_EGROUP;
+    default: return KVC_EGROUP;
+  }
+}
+
+template <bool ENC, int D, int DT>
+int dispatch_b(int b, int g, const LaunchArgs& a, hipStream_t st, uint8_t* q8, float* f) {
+  switch (b) {
+    case 2: return dispatch_g<ENC, D, DT, 2>(g, a, st, q8, f);
+    case 4: return dispatch_g<ENC, D, DT, 4>(g, a, st, q8, f);
+    case 8: return dispatch_g<ENC, D, DT, 8>(g, a, st, q8, f);
+    default: return KVC_EBITS;
+  }
+}
+
+template <bool ENC>
+int run(const Plan& plan, hipStream_t st, uint8_t* q8, float* f) {
+  for (int i = 0; i < plan.n_launch; ++i) {
+    const LaunchArgs& a = plan.args[i];
+    const int b = plan.bits[i], g = plan.group;
+    int rc;
+    if (plan.head_dim == 64)
+      rc = plan.dtype == KVC_BF16 ? dispatch_b<ENC, 64, 0>(b, g, a, st, q8, f) : dispatch_b<ENC, 64, 1>(b, g, a, st, q8, f);
+    else
+      rc = plan.dtype == KVC_BF16 ? dispatch_b<ENC, 128, 0>(b, g, a, st, q8, f)
+                                  : dispatch_b<ENC, 128, 1>(b, g, a, st, q8, f);
+    if (rc != KVC_OK) return rc;
+  }
+  if (ENC && plan.n_launch > 0) {
+    const LaunchArgs& a = plan.args[0];
+    const uint64_t codes_end = uint64_t(a.layers) * a.rows * (a.row_k + a.row_v);
+    const uint64_t meta_end = a.meta_offset + uint64_t(a.layers) * 2 * a.rows * a.groups * 4;
+    hipLaunchKernelGGL(padding_kernel, dim3(1), dim3(64), 0, st, static_cast<uint8_t*>(a.dst), codes_end,
+                       a.meta_offset, meta_end, a.blob_total);
+    if (hipGetLastError() != hipSuccess) return KVC_EHIP;
+  }
+  return KVC_OK;
+}
+
+/* Validate the workspace and split it: codes bytes first, fp32 after. */
+int split_workspace(const kvc_desc* d, void* ws, uint64_t ws_bytes, uint8_t** q8, float** f) {
+  uint64_t need = 0, fp_off = 0;
+  int st = unfused_workspace(d, &need, &fp_off);
+  if (st != KVC_OK) return st;
+  if (need == 0) return KVC_OK;
+  if (!ws) return KVC_EINVAL;
+  if (reinterpret_cast<uintptr_t>(ws) & 15u) return KVC_EALIGN;
+  if (ws_bytes < need) return KVC_ENOSPC;
+  *q8 = static_cast<uint8_t*>(ws);
+  *f = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + fp_off);
+  return KVC_OK;
+}
+
+}  // namespace uf
+}  // namespace kvc
+
+extern "C" {
+
+kvc_status kvc_encode_unfused(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes, void* workspace,
+                              uint64_t workspace_bytes, void* stream) {
+  kvc::Plan plan;
+  int st = kvc::plan_contiguous(kvc::Op::Encode, desc, kv, out, out_bytes, &plan);
+  uint8_t* q8 = nullptr;
+  float* f = nullptr;
+  if (st == KVC_OK) st = kvc::uf::split_workspace(desc, workspace, workspace_bytes, &q8, &f);
+  if (st == KVC_OK) st = kvc::uf::run<true>(plan, static_cast<hipStream_t>(stream), q8, f);
+  return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_decode_unfused(const kvc_desc* desc, const void* in, uint64_t in_bytes, void* kv_out,
+                              void* workspace, uint64_t workspace_bytes, void* stream) {
+  kvc::Plan plan;
+  int st = kvc::plan_contiguous(kvc::Op::Decode, desc, in, kv_out, in_bytes, &plan);
+  uint8_t* q8 = nullptr;
+  float* f = nullptr;
+  if (st == KVC_OK) st = kvc::uf::split_workspace(desc, workspace, workspace_bytes, &q8, &f);
+  if (st == KVC_OK) st = kvc::uf::run<false>(plan, static_cast<hipStream_t>(stream), q8, f);
+  return static_cast<kvc_status>(st);
+}
+
+}  // extern "C"

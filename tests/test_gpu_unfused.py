@@ -1,0 +1,106 @@
+"""GPU parity of the separate-kernel comparator (kvc_encode_unfused /
+kvc_decode_unfused): its blob and decode are bit-identical to the fused
+path's, and its blob meets the oracle criteria on its own."""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import gpu_util
+import kv_cache_compression_kvc_amd as kvc
+from kv_cache_compression_kvc_amd import _lib, inputs, presets
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _small(D, dtype, bk, bv, G, L=2, T=37, H=3, seed=7):
+    return presets.preset("llama3_8b_4k").with_(
+        name="uf-%d-%s-%d%d-%d" % (D, dtype, bk, bv, G), layers=L, tokens=T, kv_heads=H,
+        head_dim=D, dtype=dtype, bits_k=bk, bits_v=bv, group=G, seed=seed)
+
+
+GRID = [(D, dt, bk, bv, G)
+        for D in (64, 128) for dt in ("bf16", "fp16")
+        for bk, bv in [(2, 2), (4, 4), (8, 8), (4, 2)]
+        for G in (32, 64, 128) if G <= D]
+
+
+def _both(p, x):
+    """(fused blob, unfused blob, fused decode, unfused decode) of x on the GPU."""
+    D = p.head_dim
+    total, _ = kvc.encoded_size(p.layers, p.tokens, p.kv_heads, D, p.bits_k, p.bits_v, p.group, p.dtype)
+    ws_bytes = kvc.unfused_workspace_size(p.layers, p.tokens, p.kv_heads, D, p.bits_k, p.bits_v, p.group, p.dtype)
+    ws_whole, ws = gpu_util.guarded(ws_bytes, DEV)
+    whole, out_u = gpu_util.guarded(total, DEV)
+    out_f = kvc.encode(x, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    kvc.encode_unfused(x, p.bits_k, p.bits_v, p.group, seed=p.seed, out=out_u, workspace=ws)
+    torch.cuda.synchronize()
+    assert gpu_util.canaries_intact(whole) and gpu_util.canaries_intact(ws_whole)
+    dec_f = kvc.decode(out_f, x.shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    dec_u = kvc.decode_unfused(out_u, x.shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed, workspace=ws)
+    torch.cuda.synchronize()
+    assert gpu_util.canaries_intact(ws_whole)
+    return out_f, out_u, dec_f, dec_u
+
+
+@pytest.mark.parametrize("D,dtype,bk,bv,G", GRID)
+def test_unfused_equals_fused_and_oracle(D, dtype, bk, bv, G):
+    p = _small(D, dtype, bk, bv, G)
+    x = inputs.make_kv(p)
+    _say("unfused", p.name)
+    out_f, out_u, dec_f, dec_u = _both(p, x.to(DEV))
+    assert torch.equal(out_f, out_u), "unfused blob differs from the fused blob"
+    assert torch.equal(dec_f.view(torch.int16), dec_u.view(torch.int16)), "unfused decode differs"
+    xb = inputs.as_u16(x)
+    parity.check_blob(xb, out_u.cpu().numpy(), dtype, bk, bv, G, p.seed)
+    oblob, _ = oracle.encode(xb, dtype, bk, bv, G, p.seed)
+    ref, _ = oracle.decode(oblob, x.shape, dtype, bk, bv, G, p.seed)
+    parity.check_decode(inputs.as_u16(dec_u), ref, dtype)
+
+
+@pytest.mark.parametrize("L,T,H", [(1, 1, 1), (3, 1, 5), (1, 65, 1), (2, 33, 3), (2, 0, 8), (0, 16, 8)])
+def test_unfused_edge_shapes(L, T, H):
+    p = _small(128, "bf16", 2, 4, 64, L=L, T=T, H=H)
+    x = inputs.make_kv(p).to(DEV)
+    _say("unfused edge", L, T, H)
+    out_f, out_u, dec_f, dec_u = _both(p, x)
+    assert torch.equal(out_f, out_u)
+    assert torch.equal(dec_f.view(torch.int16), dec_u.view(torch.int16))
+
+
+def test_unfused_workspace_validation():
+    lib = _lib.lib()
+    x = torch.zeros((1, 2, 8, 2, 128), dtype=torch.bfloat16, device=DEV)
+    need = kvc.unfused_workspace_size(1, 8, 2, 128, 4, 4, 32)
+    assert need == 2 * 8 * 2 * 128 * 5          # 4096 code bytes (256-aligned), then fp32
+    with pytest.raises(kvc.KvcError, match="KVC_ENOSPC"):
+        kvc.encode_unfused(x, 4, 4, 32, workspace=torch.zeros(need - 1, dtype=torch.uint8, device=DEV))
+    with pytest.raises(kvc.KvcError, match="KVC_EALIGN"):
+        kvc.encode_unfused(x, 4, 4, 32, workspace=torch.zeros(need + 16, dtype=torch.uint8, device=DEV)[4:])
+    out = torch.zeros(8192, dtype=torch.uint8, device=DEV)
+    d = _lib.KvcDesc(1, 8, 2, 128, 0, 4, 4, 32, 0)
+    assert lib.kvc_encode_unfused(ctypes.byref(d), x.data_ptr(), out.data_ptr(), out.numel(), None, 0, None) == -1
+    assert lib.kvc_decode_unfused(ctypes.byref(d), out.data_ptr(), out.numel(), x.data_ptr(), None, 0, None) == -1
+
+
+@pytest.mark.slow
+def test_unfused_full_size_equals_fused():
+    p = presets.preset("llama3_8b_4k")
+    _say("unfused full size: generate", p.name)
+    x = inputs.make_kv(p, device=DEV)
+    out_f, out_u, dec_f, dec_u = _both(p, x)
+    assert torch.equal(out_f, out_u)
+    assert torch.equal(dec_f.view(torch.int16), dec_u.view(torch.int16))
+    del x, out_f, out_u, dec_f, dec_u
+    torch.cuda.empty_cache()

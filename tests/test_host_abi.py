@@ -137,3 +137,22 @@ def test_host_half_under_sanitizers(tmp_path):
     p = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert p.returncode == 0, p.stdout + p.stderr
     assert p.stdout.strip() == "ok"
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_unfused_workspace_size(host_lib, shape):
+    """One code byte per element (rounded up to 256), then four fp32 bytes per element."""
+    L, T, H, D, bk, bv, G = shape
+    n = ctypes.c_uint64()
+    assert host_lib.kvc_unfused_workspace_size(ctypes.byref(_desc(*shape)), ctypes.byref(n)) == 0
+    elems = L * 2 * T * H * D
+    assert n.value == (elems + 255) // 256 * 256 + 4 * elems
+
+
+def test_unfused_workspace_size_validates(host_lib):
+    n = ctypes.c_uint64()
+    assert host_lib.kvc_unfused_workspace_size(ctypes.byref(_desc(1, 4, 1, 128, 3, 4, 32)), ctypes.byref(n)) == -3
+    assert host_lib.kvc_unfused_workspace_size(ctypes.byref(_desc(1, 4, 1, 96, 4, 4, 32)), ctypes.byref(n)) == -2
+    assert host_lib.kvc_unfused_workspace_size(ctypes.byref(_desc(1, 4, 1, 128, 4, 4, 32)), None) == -1
+    huge = _desc(1 << 40, 1 << 20, 8, 128, 4, 4, 32)
+    assert host_lib.kvc_unfused_workspace_size(ctypes.byref(huge), ctypes.byref(n)) == -2
