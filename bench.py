@@ -17,6 +17,10 @@ Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
                  launch time (HIP events on the launch stream), vs 8 TB/s
   break_even     encode + decode time vs the wire time the compression saves
                  at 100 and 400 Gbit/s
+  pipeline       per-layer chunked encode overlapped with the copy of each
+                 chunk to pinned host memory (PCIe standing in for the link),
+                 and copy-in overlapped with decode, against the raw copy and
+                 the serial encode-then-copy (contiguous workloads)
   unfused        the same encode / decode run as separate kernels that pass
                  fp32 / byte intermediates through HBM (contiguous workloads):
                  times, stage bytes, and the fused kernels' speedup over them
@@ -160,6 +164,91 @@ def unfused_leg(kvc, p, xs, outs, dsts, a, stream, t_enc, t_dec, raw_bytes):
             "stages": "encode: rotate, minmax, quantize, pack, padding; decode: unpack, dequant, unrotate"}
 
 
+# ---------------------------------------------------------------------------
+# Encode overlapped with the transfer (PCIe to pinned host memory as the link)
+
+def pipeline_leg(kvc, p, x, xout, stream, raw_bytes, reps=3, chunk_layers=8):
+    import torch
+    L, T, H, D = p.layers, p.tokens, p.kv_heads, p.head_dim
+    bk, bv, G = p.bits_k, p.bits_v, p.group
+    total, _ = kvc.chunked_size(L, T, H, D, bk, bv, G, chunk_layers, p.dtype)
+    whole, _ = kvc.encoded_size(L, T, H, D, bk, bv, G, p.dtype)
+    host_raw = torch.empty(raw_bytes, dtype=torch.uint8, pin_memory=True)
+    host_blob = torch.empty(max(total, whole), dtype=torch.uint8, pin_memory=True)
+    dev_blob = torch.empty(max(total, whole), dtype=torch.uint8, device=x.device)
+    staging = torch.empty(total, dtype=torch.uint8, device=x.device)
+    copy = torch.cuda.Stream()
+    xr = x.view(torch.uint8).view(-1)
+
+    def timed(fn, end_stream):
+        ts = []
+        for i in range(reps + 1):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            copy.wait_stream(stream)
+            fn()
+            end_stream.wait_stream(copy if end_stream is stream else stream)
+            e1.record(end_stream)
+            torch.cuda.synchronize()
+            if i:
+                ts.append(e0.elapsed_time(e1) / 1e3)
+        return sum(ts) / len(ts)
+
+    def send_raw():
+        with torch.cuda.stream(copy):
+            host_raw.copy_(xr, non_blocking=True)
+
+    def recv_raw():
+        with torch.cuda.stream(copy):
+            xout.view(torch.uint8).view(-1).copy_(host_raw, non_blocking=True)
+
+    def send_serial():
+        kvc.encode(x, bk, bv, G, seed=p.seed, out=dev_blob, stream=stream)
+        copy.wait_stream(stream)
+        with torch.cuda.stream(copy):
+            host_blob[:whole].copy_(dev_blob[:whole], non_blocking=True)
+
+    def recv_serial():
+        with torch.cuda.stream(copy):
+            dev_blob[:whole].copy_(host_blob[:whole], non_blocking=True)
+        stream.wait_stream(copy)
+        kvc.decode(dev_blob, x.shape, p.dtype, bk, bv, G, seed=p.seed, out=xout, stream=stream)
+
+    def send_pipe():
+        kvc.encode_send(x, bk, bv, G, chunk_layers, host_blob, seed=p.seed, out=dev_blob,
+                        compute_stream=stream, copy_stream=copy)
+
+    def recv_pipe():
+        kvc.receive_decode(host_blob, x.shape, p.dtype, bk, bv, G, chunk_layers, seed=p.seed, staging=staging,
+                           out=xout, compute_stream=stream, copy_stream=copy)
+    t_send_raw = timed(send_raw, stream)
+    t_recv_raw = timed(recv_raw, stream)
+    t_send_serial = timed(send_serial, stream)   # whole blob in host_blob
+    t_recv_serial = timed(recv_serial, stream)
+    t_send_pipe = timed(send_pipe, stream)       # chunked blob in host_blob
+    t_recv_pipe = timed(recv_pipe, stream)
+    del host_raw, host_blob, dev_blob, staging
+
+    def rate(t):
+        return raw_bytes / t / 1e9
+    return {
+        "link": "PCIe between device memory and pinned host memory; raw and serial legs copy with "
+                "hipMemcpyAsync, the overlapped legs with the library's link-copy kernel",
+        "chunk_layers": chunk_layers,
+        "link_GBps_d2h": raw_bytes / t_send_raw / 1e9, "link_GBps_h2d": raw_bytes / t_recv_raw / 1e9,
+        "send_ms": {"raw": t_send_raw * 1e3, "encode_then_copy": t_send_serial * 1e3,
+                    "overlapped": t_send_pipe * 1e3},
+        "receive_ms": {"raw": t_recv_raw * 1e3, "copy_then_decode": t_recv_serial * 1e3,
+                       "overlapped": t_recv_pipe * 1e3},
+        "send_raw_GBps_effective": {"raw": rate(t_send_raw), "encode_then_copy": rate(t_send_serial),
+                                    "overlapped": rate(t_send_pipe)},
+        "receive_raw_GBps_effective": {"raw": rate(t_recv_raw), "copy_then_decode": rate(t_recv_serial),
+                                       "overlapped": rate(t_recv_pipe)},
+        "speedup_vs_raw": {"send": t_send_raw / t_send_pipe, "receive": t_recv_raw / t_recv_pipe},
+    }
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -240,9 +329,10 @@ def main():
     t_dec = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps / 1e3
     ms_per_step = wall / a.steps * 1e3
 
-    unfused = None
+    unfused = pipeline = None
     if not p.paged:
         unfused = unfused_leg(kvc, p, xs, outs, dsts, a, stream, t_enc, t_dec, raw_bytes)
+        pipeline = pipeline_leg(kvc, p, xs[0], dsts[0], stream, raw_bytes)
 
     # copy probe: achievable streaming bandwidth in the same run
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -300,6 +390,7 @@ def main():
                      "traffic": counter_traffic(p.name, dominant),
                      "algorithmic_bytes_per_launch": algo_bytes, "launch_ms": t_dom * 1e3},
         "unfused": unfused,
+        "pipeline": pipeline,
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline:

@@ -34,7 +34,8 @@
  *
  * Conventions for every call:
  *   - the caller allocates and owns all buffers; the library allocates no
- *     memory and keeps no state beyond a per-device occupancy cache;
+ *     memory and keeps no state beyond a per-device occupancy cache (and
+ *     the stream-ordering event of the chunked calls below);
  *   - device pointers must be 16-byte aligned and must not overlap;
  *   - GPU work is enqueued on `stream` (a hipStream_t passed as void*,
  *     NULL = the default stream) and the call returns without waiting;
@@ -207,6 +208,48 @@ kvc_status kvc_encode_unfused(const kvc_desc* desc, const void* kv, void* out, u
                               void* workspace, uint64_t workspace_bytes, void* stream);
 kvc_status kvc_decode_unfused(const kvc_desc* desc, const void* in, uint64_t in_bytes, void* kv_out,
                               void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * Chunked encode overlapped with the transfer of its output, and the
+ * receiving side.  The episode notes of "FastKVComp: checking whether
+ * high-throughput KV compression pays off" give the break-even rule
+ * (encode plus decode time below the wire time saved); cutting the cache
+ * into layer chunks lets the encode of one chunk run while the previous one
+ * is on the wire, so the encode hides behind the transfer.
+ *
+ * Chunked blob: the layers are cut into chunks of chunk_layers layers (the
+ * last may be shorter); chunk k is the ordinary blob of layers
+ * [k*chunk_layers, ...) as a [L_k, 2, T, H, D] tensor, at byte offset
+ * k * stride.  kvc_chunked_size (host only) gives *total bytes and the
+ * *stride (may be NULL); chunk_layers must be >= 1.
+ *
+ * Chunks cross the link by a streaming-copy kernel on copy_stream, so the
+ * far buffer (dst / src, >= total bytes, 16-byte aligned) must be device
+ * memory or pinned, mapped host memory (hipHostMalloc; it stands in for a
+ * NIC buffer); pageable host memory is rejected with KVC_EINVAL.
+ *
+ * kvc_encode_send: encodes chunk by chunk on compute_stream into `out`
+ * (device, >= total bytes) and, after each chunk, copies it to the same
+ * offset of `dst` on copy_stream.  Starts only after the work already
+ * enqueued on copy_stream (an earlier call's copies out of `out`).  When
+ * copy_stream has passed the work, dst holds the chunked blob.
+ *
+ * kvc_receive_decode: copies chunk k from `src` into the same offset of
+ * `staging` (device, >= total bytes) on copy_stream, then decodes it into
+ * kv_out [L, 2, T, H, D] on compute_stream, so the decode of chunk k
+ * overlaps the copy of chunk k+1.  Starts only after the work already
+ * enqueued on compute_stream (an earlier call's decodes out of `staging`).
+ *
+ * Both streams must have the default priority.  The two calls keep one
+ * HIP event per (host thread, device) to order the streams.
+ */
+kvc_status kvc_chunked_size(const kvc_desc* desc, int64_t chunk_layers, uint64_t* total, uint64_t* stride);
+kvc_status kvc_encode_send(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes,
+                           int64_t chunk_layers, void* dst, uint64_t dst_bytes, void* compute_stream,
+                           void* copy_stream);
+kvc_status kvc_receive_decode(const kvc_desc* desc, const void* src, uint64_t src_bytes, void* staging,
+                              uint64_t staging_bytes, int64_t chunk_layers, void* kv_out,
+                              void* compute_stream, void* copy_stream);
 
 /*
  * Measurement helper: copy `bytes` (a multiple of 16) from src to dst with

@@ -27,6 +27,7 @@ __all__ = [
     "KvcError", "DTYPE", "abi_version", "encoded_size", "sign_mask", "encode", "decode",
     "paged_layout", "encode_paged", "decode_paged", "debug_rotate", "probe_copy",
     "unfused_workspace_size", "encode_unfused", "decode_unfused",
+    "chunked_size", "encode_send", "receive_decode",
 ]
 
 _TORCH_TO_NAME = {torch.bfloat16: "bf16", torch.float16: "fp16"}
@@ -145,6 +146,54 @@ def decode_unfused(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, 
     d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
     _lib.check(_lib.lib().kvc_decode_unfused(ctypes.byref(d), _ptr(blob), blob.numel(), _ptr(out), _ptr(ws),
                                              ws.numel(), _stream(stream)))
+    return out
+
+
+def chunked_size(layers, tokens, kv_heads, head_dim, bits_k, bits_v, group, chunk_layers, dtype="bf16"):
+    """(total bytes, stride between chunk starts) of a chunked blob."""
+    total, stride = ctypes.c_uint64(), ctypes.c_uint64()
+    d = _desc(layers, tokens, kv_heads, head_dim, dtype, bits_k, bits_v, group)
+    _lib.check(_lib.lib().kvc_chunked_size(ctypes.byref(d), int(chunk_layers), ctypes.byref(total),
+                                           ctypes.byref(stride)))
+    return total.value, stride.value
+
+
+def encode_send(kv, bits_k, bits_v, group, chunk_layers, dst, seed=0, out=None, compute_stream=None,
+                copy_stream=None):
+    """Encode layer chunks on ``compute_stream`` and copy each finished chunk
+    into ``dst`` (pinned host or device uint8 tensor) on ``copy_stream``."""
+    _check_cuda(kv, out)
+    if not dst.is_contiguous():
+        raise ValueError("dst must be contiguous")
+    L, two, T, H, D = kv.shape
+    dt = _TORCH_TO_NAME[kv.dtype]
+    total, _ = chunked_size(L, T, H, D, bits_k, bits_v, group, chunk_layers, dt)
+    if out is None:
+        out = torch.empty(total, dtype=torch.uint8, device=kv.device)
+    d = _desc(L, T, H, D, dt, bits_k, bits_v, group, seed)
+    _lib.check(_lib.lib().kvc_encode_send(ctypes.byref(d), _ptr(kv), _ptr(out), out.numel(), int(chunk_layers),
+                                          _ptr(dst), dst.numel(), _stream(compute_stream),
+                                          _stream(copy_stream)))
+    return out
+
+
+def receive_decode(src, shape, dtype, bits_k, bits_v, group, chunk_layers, seed=0, staging=None, out=None,
+                   compute_stream=None, copy_stream=None):
+    """Copy layer chunks of ``src`` (host or device) into ``staging`` on
+    ``copy_stream`` and decode each on ``compute_stream`` into ``out``."""
+    _check_cuda(staging, out)
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    L, two, T, H, D = shape
+    total, _ = chunked_size(L, T, H, D, bits_k, bits_v, group, chunk_layers, dtype)
+    if staging is None:
+        staging = torch.empty(max(total, 1), dtype=torch.uint8, device="cuda")
+    if out is None:
+        out = torch.empty(tuple(shape), dtype=_NAME_TO_TORCH[dtype], device=staging.device)
+    d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
+    _lib.check(_lib.lib().kvc_receive_decode(ctypes.byref(d), _ptr(src), src.numel(), _ptr(staging),
+                                             staging.numel(), int(chunk_layers), _ptr(out),
+                                             _stream(compute_stream), _stream(copy_stream)))
     return out
 
 

@@ -27,10 +27,10 @@ EXPORTS = [
     "kvc_abi_version", "kvc_strerror", "kvc_encoded_size", "kvc_sign_mask", "kvc_encode",
     "kvc_decode", "kvc_paged_layout", "kvc_encode_paged", "kvc_decode_paged",
     "kvc_debug_rotate", "kvc_unfused_workspace_size", "kvc_encode_unfused", "kvc_decode_unfused",
-    "kvc_probe_copy",
+    "kvc_chunked_size", "kvc_encode_send", "kvc_receive_decode", "kvc_probe_copy",
 ]
 HOST_EXPORTS = ["kvc_abi_version", "kvc_strerror", "kvc_encoded_size", "kvc_sign_mask",
-                "kvc_paged_layout", "kvc_unfused_workspace_size"]
+                "kvc_paged_layout", "kvc_unfused_workspace_size", "kvc_chunked_size"]
 
 
 class KvcDesc(ctypes.Structure):
@@ -93,6 +93,14 @@ def _declare(lib, names):
                                                 ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
         "kvc_decode_unfused": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                                 ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
+        "kvc_chunked_size": (ctypes.c_int32, [P(KvcDesc), ctypes.c_int64, P(ctypes.c_uint64),
+                                              P(ctypes.c_uint64)]),
+        "kvc_encode_send": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                             ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                             ctypes.c_void_p]),
+        "kvc_receive_decode": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                                ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p]),
         "kvc_probe_copy": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                             ctypes.c_void_p]),
     }

@@ -114,6 +114,33 @@ int blob_sizes(const kvc_desc* d, int64_t tokens, BlobSizes* out) {
   return KVC_OK;
 }
 
+int chunking(const kvc_desc* d, int64_t chunk_layers, Chunking* c) {
+  if (!d || !c || chunk_layers <= 0) return KVC_EINVAL;
+  int st = check_desc(d);
+  if (st != KVC_OK) return st;
+  kvc_desc dc = *d;
+  dc.layers = d->layers < chunk_layers ? d->layers : chunk_layers;
+  BlobSizes one, last;
+  if ((st = blob_sizes(&dc, d->tokens, &one)) != KVC_OK) return st;
+  c->n_chunks = d->layers == 0 ? 0 : (d->layers - 1) / chunk_layers + 1;
+  c->stride = one.total;
+  c->total = 0;
+  if (c->n_chunks > 0) {
+    dc.layers = d->layers - (c->n_chunks - 1) * chunk_layers;
+    if ((st = blob_sizes(&dc, d->tokens, &last)) != KVC_OK) return st;
+    uint64_t body;
+    if (!mul_ok(static_cast<uint64_t>(c->n_chunks - 1), one.total, &body) || !add_ok(body, last.total, &c->total) ||
+        c->total > static_cast<uint64_t>(INT64_MAX))
+      return KVC_ESHAPE;
+  }
+  uint64_t kv;
+  if (!mul_ok(static_cast<uint64_t>(d->tokens), static_cast<uint64_t>(d->kv_heads), &kv) ||
+      !mul_ok(kv, static_cast<uint64_t>(d->head_dim) * 4, &kv))
+    return KVC_ESHAPE;
+  c->kv_layer = kv;
+  return KVC_OK;
+}
+
 int unfused_workspace(const kvc_desc* d, uint64_t* bytes, uint64_t* fp32_offset) {
   int st = check_desc(d);
   if (st != KVC_OK) return st;
@@ -266,6 +293,16 @@ kvc_status kvc_sign_mask(uint64_t seed, int64_t head_dim, uint64_t* mask_words) 
   for (int64_t w = 0; w < (head_dim + 63) / 64; ++w) mask_words[w] = 0;
   for (int64_t j = 0; j < head_dim; ++j)
     if (kvc::splitmix64_next(&st) >> 63) mask_words[j / 64] |= 1ull << (j % 64);
+  return KVC_OK;
+}
+
+kvc_status kvc_chunked_size(const kvc_desc* desc, int64_t chunk_layers, uint64_t* total, uint64_t* stride) {
+  if (!total) return KVC_EINVAL;
+  kvc::Chunking c;
+  int st = kvc::chunking(desc, chunk_layers, &c);
+  if (st != KVC_OK) return static_cast<kvc_status>(st);
+  *total = c.total;
+  if (stride) *stride = c.stride;
   return KVC_OK;
 }
 

@@ -85,6 +85,16 @@ struct BlobSizes {
 };
 int blob_sizes(const kvc_desc* d, int64_t tokens, BlobSizes* out);
 
+/* Layer chunks of a chunked blob: chunk k holds layers [k*chunk_layers,
+ * min(L, (k+1)*chunk_layers)) as an ordinary blob at byte k * stride. */
+struct Chunking {
+  int64_t n_chunks;
+  uint64_t stride;    // bytes between chunk starts (blob size of chunk_layers layers)
+  uint64_t total;     // bytes of the chunked blob
+  uint64_t kv_layer;  // bytes of one layer of the KV tensor
+};
+int chunking(const kvc_desc* d, int64_t chunk_layers, Chunking* c);
+
 /* Workspace of the separate-kernel comparator for the contiguous shape in
  * d: one byte per element (codes), then four per element (fp32) at byte
  * *fp32_offset.  *bytes is 0 for an empty tensor. */

@@ -156,3 +156,29 @@ def test_unfused_workspace_size_validates(host_lib):
     assert host_lib.kvc_unfused_workspace_size(ctypes.byref(_desc(1, 4, 1, 128, 4, 4, 32)), None) == -1
     huge = _desc(1 << 40, 1 << 20, 8, 128, 4, 4, 32)
     assert host_lib.kvc_unfused_workspace_size(ctypes.byref(huge), ctypes.byref(n)) == -2
+
+
+@pytest.mark.parametrize("shape", SHAPES[:6])
+@pytest.mark.parametrize("chunk", [1, 3, 1000])
+def test_chunked_size_matches_oracle_layout(host_lib, shape, chunk):
+    """Chunk k is the blob of layers [k*chunk, ...): all chunks but the last
+    take `stride` bytes, the last its own blob size."""
+    L, T, H, D, bk, bv, G = shape
+    total, stride = ctypes.c_uint64(), ctypes.c_uint64()
+    assert host_lib.kvc_chunked_size(ctypes.byref(_desc(*shape)), chunk, ctypes.byref(total),
+                                     ctypes.byref(stride)) == 0
+    sizes = [oracle.blob_layout(min(chunk, L - l0), T, H, D, bk, bv, G).total for l0 in range(0, L, chunk)]
+    assert stride.value == oracle.blob_layout(min(chunk, L), T, H, D, bk, bv, G).total
+    assert total.value == (sum(sizes[:-1]) + sizes[-1] if sizes else 0)
+    assert all(s == stride.value for s in sizes[:-1])
+
+
+def test_chunked_size_validates(host_lib):
+    total = ctypes.c_uint64()
+    d = _desc(4, 16, 2, 128, 4, 4, 32)
+    assert host_lib.kvc_chunked_size(ctypes.byref(d), 0, ctypes.byref(total), None) == -1
+    assert host_lib.kvc_chunked_size(ctypes.byref(d), -2, ctypes.byref(total), None) == -1
+    assert host_lib.kvc_chunked_size(ctypes.byref(d), 1, None, None) == -1
+    assert host_lib.kvc_chunked_size(ctypes.byref(_desc(4, 16, 2, 128, 5, 4, 32)), 1, ctypes.byref(total), None) == -3
+    assert host_lib.kvc_chunked_size(ctypes.byref(_desc(0, 16, 2, 128, 4, 4, 32)), 2, ctypes.byref(total), None) == 0
+    assert total.value == 0
