@@ -27,8 +27,12 @@
  * nearest even in the tensor's dtype.
  *
  * Blob layout (for T tokens):
- *   codes: for l in [0, L), for kv in (K, V): T*H rows, (t, h) order,
- *          D*b_kv/8 bytes each; zero padding to a multiple of 256 bytes;
+ *   codes: for l in [0, L), for kv in (K, V): a slab of T*H rows, (t, h)
+ *          order, RB = D*b_kv/8 bytes each, stored in tiles of 64 rows:
+ *          tile k starts at byte 64*k*RB of the slab, and inside a tile of
+ *          n rows (64, or fewer for the last) the 16-byte piece c of row i
+ *          is at byte (c*n + i)*16 of the tile;
+ *          zero padding to a multiple of 256 bytes;
  *   meta:  [L, 2, T, H, D/group] entries of 4 bytes -- fp16 scale, then
  *          fp16 zero, little endian; zero padding to a multiple of 256.
  *

@@ -198,12 +198,53 @@ __device__ __forceinline__ void unpack_word(uint32_t u, float* q) {
 
 /* ---- work items ------------------------------------------------------------ */
 
+/*
+ * Code rows are stored in tiles of 64 rows per (layer, K/V) slab: tile k of
+ * a slab starts at byte 64 * k * RB, and inside a tile of n rows the
+ * 16-byte piece c of row i sits at byte (c * n + i) * 16, so a wave writes
+ * (and reads back) each piece of its 64 rows as one contiguous KiB.
+ *
+ * A work tile covers `count` vectors; its first one is row i0 of the code
+ * tile that starts at `codes` (n rows).  Contiguous work tiles are the code
+ * tiles themselves (i0 = 0, n = count); a paged one (a block's rows) can
+ * run into the next code tile, of n_next rows, at codes + 64 * RB.  The
+ * three small numbers share one word (`geom`, 8 bits each), which keeps
+ * the paged kernels' scalar registers from spilling.
+ */
 struct Tile {
   const uint8_t* src;  // first byte of the tile's vectors in the KV tensor / pool
-  uint8_t* codes;      // first code row of the tile in the blob
+  uint8_t* codes;      // start of the code tile holding the tile's first row
   uint8_t* meta;       // first meta entry of the tile in the blob
   int count;           // valid vectors, 1..64
+  uint32_t geom;       // paged: i0 | n << 8 | n_next << 16
 };
+
+__device__ __forceinline__ uint32_t code_geom(int64_t i0, int64_t n, int64_t n_next) {
+  return uint32_t(i0) | uint32_t(n) << 8 | uint32_t(n_next > 0 ? n_next : 0) << 16;
+}
+
+/* This lane's code row: pieces at piece_base[c * piece_stride], c < RB/16. */
+template <int RB, bool PAGED>
+__device__ __forceinline__ v4u* code_row(const Tile& t, int lane, int& piece_stride) {
+  v4u* base = reinterpret_cast<v4u*>(t.codes);
+  if constexpr (!PAGED) {
+    piece_stride = t.count;
+    return base + lane;
+  } else {
+    const int i0 = t.geom & 0xffu, n = (t.geom >> 8) & 0xffu;
+    if (i0 + t.count <= kTileVectors) {  // wave-uniform: the tile stays in one code tile
+      piece_stride = n;
+      return base + i0 + lane;
+    }
+    const int i = i0 + lane;
+    if (i < kTileVectors) {
+      piece_stride = n;
+      return base + i;
+    }
+    piece_stride = t.geom >> 16;
+    return base + kTileVectors * (RB / 16) + (i - kTileVectors);
+  }
+}
 
 /* Zero the two padding runs of one blob (one wave, byte stores, < 512 bytes):
  * [codes_end, meta_start) and [meta_end, blob_end). */
@@ -301,6 +342,7 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
     const int64_t l = s >> 1, kv = s & 1;
     const int64_t row = kv ? a.row_v : a.row_k;
     t.count = static_cast<int>(a.rows - v0 < kTileVectors ? a.rows - v0 : kTileVectors);
+    t.geom = 0;
     t.src = tensor + (s * a.rows + v0) * vec_bytes;
     t.codes = blob + l * a.rows * (a.row_k + a.row_v) + kv * a.rows * a.row_k + v0 * row;
     t.meta = blob + a.meta_offset + (s * a.rows + v0) * a.groups * 4;
@@ -336,10 +378,13 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
   const int64_t l = s >> 1, kv = s & 1;
   const int64_t row = kv ? a.row_v : a.row_k;
   const int64_t row0 = int64_t(first_tok) * a.heads + v0;  // t*H + h of the tile's first vector
+  const int64_t tile0 = row0 / kTileVectors * kTileVectors;  // first row of its code tile
   t.count = min(kTileVectors, nvec - v0);
+  t.geom = code_geom(row0 - tile0, min<int64_t>(kTileVectors, rows - tile0),
+                     min<int64_t>(kTileVectors, rows - tile0 - kTileVectors));
   t.src = tensor + ((s * a.num_blocks + blk) * int64_t(a.block_size) * a.heads + v0) * vec_bytes;
   uint8_t* rb = blob + off;
-  t.codes = rb + l * rows * (a.row_k + a.row_v) + kv * rows * a.row_k + row0 * row;
+  t.codes = rb + l * rows * (a.row_k + a.row_v) + kv * rows * a.row_k + tile0 * row;
   t.meta = rb + meta_start + (s * rows + row0) * a.groups * 4;
   if (PAD && c.i == 0 && c.j == 0 && c.sub == 0 && a.slab_first == 0)
     write_padding(rb, codes_bytes, meta_start, meta_end, total);
@@ -518,7 +563,7 @@ __device__ __forceinline__ void quantize_group(const float* y, float A, float Bz
   *words = pack_word<B>(tq);
 }
 
-template <int D, int B, int G>
+template <int D, int B, int G, bool PAGED>
 __device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t) {
   constexpr int NG = D / G;
   constexpr float QMAX = float((1 << B) - 1);
@@ -555,9 +600,11 @@ __device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t) {
   }
   if (static_cast<int>(threadIdx.x) < t.count) {
     constexpr int RB = D * B / 8;
-    v4u* crow = reinterpret_cast<v4u*>(t.codes + threadIdx.x * RB);
+    int stride;
+    v4u* crow = code_row<RB, PAGED>(t, threadIdx.x, stride);
 #pragma unroll
-    for (int c = 0; c < RB / 16; ++c) crow[c] = v4u{words[4 * c], words[4 * c + 1], words[4 * c + 2], words[4 * c + 3]};
+    for (int c = 0; c < RB / 16; ++c)
+      crow[c * stride] = v4u{words[4 * c], words[4 * c + 1], words[4 * c + 2], words[4 * c + 3]};
     uint32_t* mrow = reinterpret_cast<uint32_t*>(t.meta) + threadIdx.x * NG;
     if constexpr (NG == 1) {
       mrow[0] = meta[0];
@@ -598,7 +645,7 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
     const bool more = next_tile<D, true, PAGED>(a, c, tensor, blob, nxt, false);
     if (more) dma_rows<D, !PAGED>(nxt.src, nxt.count, lds);
     KVC_PHASE();
-    encode_vector<D, B, G>(y, cur);
+    encode_vector<D, B, G, PAGED>(y, cur);
     if (!more) break;
     // outstanding: the next tile's DMA, then this tile's code and meta
     // stores (RB / 16 + 1 instructions, issued by the lanes < count)
@@ -621,14 +668,15 @@ struct CodeRegs {
 /* Prefetch of this lane's code row and meta entries (lanes past the tile's
  * count load nothing).  Plain vector loads: their wait counts are tracked per
  * register, so the compiler waits for them only where they are used. */
-template <int D, int B, int G>
+template <int D, int B, int G, bool PAGED>
 __device__ __forceinline__ void load_codes(const Tile& t, CodeRegs<D, B, G>& r) {
   constexpr int RB = D * B / 8, NG = D / G;
   const int lane = threadIdx.x;
   if (lane < t.count) {
-    const v4u* crow = reinterpret_cast<const v4u*>(t.codes + lane * RB);
+    int stride;
+    const v4u* crow = code_row<RB, PAGED>(t, lane, stride);
 #pragma unroll
-    for (int p = 0; p < RB / 16; ++p) r.codes[p] = __builtin_nontemporal_load(crow + p);
+    for (int p = 0; p < RB / 16; ++p) r.codes[p] = __builtin_nontemporal_load(crow + p * stride);
     const uint32_t* mrow = reinterpret_cast<const uint32_t*>(t.meta) + lane * NG;
     if constexpr (NG == 1) {
       r.meta[0] = __builtin_nontemporal_load(mrow);
@@ -673,7 +721,7 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   Tile cur;
   if (!next_tile<D, false, PAGED>(a, c, tensor, blob, cur, true)) return;
   CodeRegs<D, B, G> cr;
-  load_codes<D, B, G>(cur, cr);
+  load_codes<D, B, G, PAGED>(cur, cr);
   for (;;) {
     float y[D];
 #pragma unroll
@@ -693,7 +741,7 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
     KVC_PHASE();
     Tile nxt;
     const bool more = next_tile<D, false, PAGED>(a, c, tensor, blob, nxt, false);
-    if (more) load_codes<D, B, G>(nxt, cr);
+    if (more) load_codes<D, B, G, PAGED>(nxt, cr);
     KVC_PHASE();
     fwht<D>(y);
     KVC_PHASE();

@@ -11,7 +11,8 @@
  *   E1 rotate    x (bf16 / fp16)  -> u  fp32 [rows, D]  sign flip + butterfly
  *   E2 minmax    u                -> meta (the blob's meta section)
  *   E3 quantize  u, meta          -> q  u8 [rows, D]
- *   E4 pack      q                -> codes (the blob's codes section)
+ *   E4 pack      q                -> codes (the blob's codes section, in its
+ *                                     tiled order of 16-byte pieces)
  *   E5 padding   zeroes the blob's two padding runs
  * Decode:
  *   D1 unpack    codes            -> q  u8 [rows, D]
@@ -197,34 +198,48 @@ __device__ __forceinline__ void unpack_bytes(uint32_t p, uint32_t* w) {
   for (int k = 0; k < 32 / B; ++k) w[k / 4] |= ((p >> (B * k)) & ((1u << B) - 1)) << (8 * (k % 4));
 }
 
-/* E4: one packed word per unit (32/B code bytes in). */
+/* Position of packed piece j of a slab (16 bytes of one code row) in the
+ * tiled code order: tiles of 64 rows, and inside a tile of n rows all rows'
+ * piece 0, then all rows' piece 1, ...  Returns the row; *c = the piece. */
+template <int RB>
+__device__ __forceinline__ int64_t piece_row(int64_t j, int64_t rows, int* c) {
+  constexpr int64_t PT = int64_t(kTileVectors) * (RB / 16);  // pieces of a full tile
+  const int64_t t = j / PT;
+  const int64_t w = j - t * PT;
+  const int64_t n = min<int64_t>(kTileVectors, rows - t * kTileVectors);
+  *c = static_cast<int>(w / n);
+  return t * kTileVectors + (w - int64_t(*c) * n);
+}
+
+/* E4: one 16-byte packed piece per unit (128/B code bytes in). */
 template <int D, int B>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, const uint8_t* q8) {
-  constexpr int IN = 32 / B / 4;  // 32-bit words of code bytes per unit
+  constexpr int RB = D * B / 8, IN = 8 / B;  // 16-byte loads of code bytes per piece
   const int64_t s = slab_of(a);
-  const int64_t units = a.rows * D * B / 32;
-  const uint32_t* q = reinterpret_cast<const uint32_t*>(q8 + s * a.rows * D);
-  uint32_t* out = reinterpret_cast<uint32_t*>(codes_of(a, static_cast<uint8_t*>(a.dst), s));
+  const int64_t units = a.rows * (RB / 16);
+  const uint8_t* q = q8 + s * a.rows * D;
+  v4u* out = reinterpret_cast<v4u*>(codes_of(a, static_cast<uint8_t*>(a.dst), s));
   const int64_t stride = int64_t(gridDim.x) * kThreads;
   for (int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; i0 < units; i0 += stride * kUnroll) {
-    uint32_t w[kUnroll][IN];
+    uint32_t w[kUnroll][4 * IN];
 #pragma unroll
     for (int k = 0; k < kUnroll; ++k) {
       const int64_t i = i0 + k * stride;
-      if constexpr (IN == 4) {
-        const v4u t = i < units ? reinterpret_cast<const v4u*>(q)[i] : v4u{0, 0, 0, 0};
-        w[k][0] = t.x, w[k][1] = t.y, w[k][2] = t.z, w[k][3] = t.w;
-      } else if constexpr (IN == 2) {
-        const v2u t = i < units ? reinterpret_cast<const v2u*>(q)[i] : v2u{0, 0};
-        w[k][0] = t.x, w[k][1] = t.y;
-      } else {
-        w[k][0] = i < units ? q[i] : 0u;
+      int c = 0;
+      const int64_t r = i < units ? piece_row<RB>(i, a.rows, &c) : 0;
+      const v4u* src = reinterpret_cast<const v4u*>(q + r * D + c * (128 / B));
+#pragma unroll
+      for (int m = 0; m < IN; ++m) {
+        const v4u t = i < units ? src[m] : v4u{0, 0, 0, 0};
+        w[k][4 * m] = t.x, w[k][4 * m + 1] = t.y, w[k][4 * m + 2] = t.z, w[k][4 * m + 3] = t.w;
       }
     }
 #pragma unroll
     for (int k = 0; k < kUnroll; ++k) {
       const int64_t i = i0 + k * stride;
-      if (i < units) out[i] = pack_bytes<B>(w[k]);
+      if (i < units)
+        out[i] = v4u{pack_bytes<B>(&w[k][0]), pack_bytes<B>(&w[k][IN]), pack_bytes<B>(&w[k][2 * IN]),
+                     pack_bytes<B>(&w[k][3 * IN])};
     }
   }
 }
@@ -237,36 +252,35 @@ __global__ __launch_bounds__(64) void padding_kernel(uint8_t* blob, uint64_t cod
 
 /* ---- decode stages ---------------------------------------------------------- */
 
-/* D1: one packed word per unit -> 32/B code bytes. */
+/* D1: one 16-byte packed piece per unit -> 128/B code bytes of its row. */
 template <int D, int B>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a, uint8_t* q8) {
-  constexpr int OUT = 32 / B / 4;
+  constexpr int RB = D * B / 8, OUT = 8 / B;
   const int64_t s = slab_of(a);
-  const int64_t units = a.rows * D * B / 32;
-  const uint32_t* in = reinterpret_cast<const uint32_t*>(
+  const int64_t units = a.rows * (RB / 16);
+  const v4u* in = reinterpret_cast<const v4u*>(
       codes_of(a, const_cast<uint8_t*>(static_cast<const uint8_t*>(a.src)), s));
-  uint32_t* q = reinterpret_cast<uint32_t*>(q8 + s * a.rows * D);
+  uint8_t* q = q8 + s * a.rows * D;
   const int64_t stride = int64_t(gridDim.x) * kThreads;
   for (int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; i0 < units; i0 += stride * kUnroll) {
-    uint32_t p[kUnroll];
+    v4u p[kUnroll];
 #pragma unroll
     for (int k = 0; k < kUnroll; ++k) {
       const int64_t i = i0 + k * stride;
-      p[k] = i < units ? in[i] : 0u;
+      p[k] = i < units ? in[i] : v4u{0, 0, 0, 0};
     }
 #pragma unroll
     for (int k = 0; k < kUnroll; ++k) {
       const int64_t i = i0 + k * stride;
-      uint32_t w[OUT];
-      unpack_bytes<B>(p[k], w);
-      if (i < units) {
-        if constexpr (OUT == 4)
-          reinterpret_cast<v4u*>(q)[i] = v4u{w[0], w[1], w[2], w[3]};
-        else if constexpr (OUT == 2)
-          reinterpret_cast<v2u*>(q)[i] = v2u{w[0], w[1]};
-        else
-          q[i] = w[0];
-      }
+      if (i >= units) continue;
+      int c = 0;
+      const int64_t r = piece_row<RB>(i, a.rows, &c);
+      v4u* dst = reinterpret_cast<v4u*>(q + r * D + c * (128 / B));
+      uint32_t w[4 * OUT];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) unpack_bytes<B>(p[k][m], &w[m * OUT]);
+#pragma unroll
+      for (int m = 0; m < OUT; ++m) dst[m] = v4u{w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]};
     }
   }
 }
@@ -366,7 +380,7 @@ int encode_launch(const LaunchArgs& a, hipStream_t st, uint8_t* q8, float* u) {
   return for_slab_chunks(a, [&](const LaunchArgs& c, unsigned gy) {
     const unsigned rx = blocks_x(c.rows, rows_per_block<D>(), c.n_slabs);
     const unsigned ex = blocks_x(c.rows * (D / 4), kUnitsPerBlock, c.n_slabs);
-    const unsigned px = blocks_x(c.rows * D * B / 32, kUnitsPerBlock, c.n_slabs);
+    const unsigned px = blocks_x(c.rows * D * B / 128, kUnitsPerBlock, c.n_slabs);
     hipLaunchKernelGGL((rotate_kernel<D, DT>), dim3(rx, gy), dim3(kThreads), 0, st, c, u);
     hipLaunchKernelGGL((minmax_kernel<D, B, G>), dim3(rx, gy), dim3(kThreads), 0, st, c, u);
     hipLaunchKernelGGL((quantize_kernel<D, B, G>), dim3(ex, gy), dim3(kThreads), 0, st, c, u, q8);
@@ -379,7 +393,7 @@ int decode_launch(const LaunchArgs& a, hipStream_t st, uint8_t* q8, float* z) {
   return for_slab_chunks(a, [&](const LaunchArgs& c, unsigned gy) {
     const unsigned rx = blocks_x(c.rows, rows_per_block<D>(), c.n_slabs);
     const unsigned ex = blocks_x(c.rows * (D / 4), kUnitsPerBlock, c.n_slabs);
-    const unsigned px = blocks_x(c.rows * D * B / 32, kUnitsPerBlock, c.n_slabs);
+    const unsigned px = blocks_x(c.rows * D * B / 128, kUnitsPerBlock, c.n_slabs);
     hipLaunchKernelGGL((unpack_kernel<D, B>), dim3(px, gy), dim3(kThreads), 0, st, c, q8);
     hipLaunchKernelGGL((dequant_kernel<D, G>), dim3(ex, gy), dim3(kThreads), 0, st, c, q8, z);
     hipLaunchKernelGGL((unrotate_kernel<D, DT>), dim3(rx, gy), dim3(kThreads), 0, st, c, z);

@@ -38,7 +38,7 @@ from .rht import hadamard, rotate_raw, rotate, unrotate
 from .quant import fl, div_f32, group_meta, code_values, quantize, pack_codes, unpack_codes, \
     dequantize
 from .blob import BlobLayout, blob_layout, encode, decode, EncodeTrace, \
-    paged_layout, gather_request, encode_paged, decode_paged
+    paged_layout, gather_request, encode_paged, decode_paged, tile_codes, untile_codes, code_offsets
 
 __all__ = [
     "splitmix64_outputs", "sign_vector", "sign_bits_mask",
@@ -49,4 +49,5 @@ __all__ = [
     "dequantize",
     "BlobLayout", "blob_layout", "encode", "decode", "EncodeTrace",
     "paged_layout", "gather_request", "encode_paged", "decode_paged",
+    "tile_codes", "untile_codes", "code_offsets",
 ]

@@ -8,8 +8,9 @@ link and decoding it on the other side; they define no byte format.  The
 layout used here, for a KV tensor [L, 2, T, H, D] (2 = K then V) with b_K
 and b_V bits per code and group size G:
 
-  codes section  for l in 0..L-1, for kv in (K, V): T*H rows in (t, h)
-                 order, each D*b_kv/8 bytes of packed codes
+  codes section  for l in 0..L-1, for kv in (K, V): the slab of T*H rows in
+                 (t, h) order, each row D*b_kv/8 bytes of packed codes,
+                 stored in tiles of 64 rows (see ``tile_codes``)
   padding        zero bytes up to a multiple of 256
   meta section   [L, 2, T, H, D/G] entries of 4 bytes: fp16 scale (bytes
                  0-1) then fp16 zero (bytes 2-3), little endian
@@ -37,6 +38,52 @@ from .quant import group_meta, quantize, pack_codes, unpack_codes, dequantize
 
 def _align256(n: int) -> int:
     return (n + 255) // 256 * 256
+
+
+TILE_ROWS = 64   # rows of one code tile
+PIECE = 16       # bytes of one piece of a code row
+
+# Order of the code bytes inside a slab (this build's own reading; the pages
+# fix no byte format).  Rows are cut into tiles of TILE_ROWS consecutive rows
+# (the last tile may be shorter, n rows); tile k starts at byte
+# k * TILE_ROWS * RB of the slab.  Inside a tile each row's RB bytes are cut
+# into RB / PIECE pieces of PIECE bytes, and piece c of the tile's row i sits
+# at byte (c * n + i) * PIECE of the tile: all rows' piece 0, then all rows'
+# piece 1, and so on.  The slab keeps its size, rows * RB bytes.
+
+
+def tile_codes(rows: np.ndarray) -> np.ndarray:
+    """[R, RB] packed code rows -> the slab's R * RB bytes in tiled order."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    R, RB = rows.shape
+    if RB % PIECE:
+        raise ValueError("row bytes must be a multiple of the piece size")
+    out = np.empty(R * RB, dtype=np.uint8)
+    for t0 in range(0, R, TILE_ROWS):
+        n = min(TILE_ROWS, R - t0)
+        pieces = rows[t0:t0 + n].reshape(n, RB // PIECE, PIECE)     # [row, piece, byte]
+        out[t0 * RB:(t0 + n) * RB] = pieces.transpose(1, 0, 2).reshape(-1)
+    return out
+
+
+def untile_codes(data: np.ndarray, R: int, RB: int) -> np.ndarray:
+    """Inverse of :func:`tile_codes`: R * RB slab bytes -> [R, RB] rows."""
+    data = np.asarray(data, dtype=np.uint8)[:R * RB]
+    rows = np.empty((R, RB), dtype=np.uint8)
+    for t0 in range(0, R, TILE_ROWS):
+        n = min(TILE_ROWS, R - t0)
+        pieces = data[t0 * RB:(t0 + n) * RB].reshape(RB // PIECE, n, PIECE)   # [piece, row, byte]
+        rows[t0:t0 + n] = pieces.transpose(1, 0, 2).reshape(n, RB)
+    return rows
+
+
+def code_offsets(rows_idx, R: int, RB: int) -> np.ndarray:
+    """Byte offsets inside a slab of the RB code bytes of each row in rows_idx ([k, RB])."""
+    r = np.asarray(rows_idx, dtype=np.int64)[:, None]
+    t0 = r // TILE_ROWS * TILE_ROWS
+    n = np.minimum(TILE_ROWS, R - t0)
+    j = np.arange(RB, dtype=np.int64)[None, :]
+    return t0 * RB + ((j // PIECE) * n + (r - t0)) * PIECE + j % PIECE
 
 
 @dataclass(frozen=True)
@@ -133,9 +180,9 @@ def encode(x_bits: np.ndarray, dtype: str, bits_k: int, bits_v: int, group: int,
             ul = u[l, kv].reshape(T * H, D)
             scale, zero = group_meta(ul, G, b)
             q, t = quantize(ul, scale, zero, G, b)
-            packed = pack_codes(q, b)
+            packed = tile_codes(pack_codes(q, b))
             off = lay.codes_slab(l, kv)
-            blob[off:off + packed.size] = packed.reshape(-1)
+            blob[off:off + packed.size] = packed
             meta = np.stack([scale.view(np.uint16), zero.view(np.uint16)], axis=-1)
             mbytes = meta.astype("<u2").view(np.uint8).reshape(-1)
             moff = lay.meta_slab(l, kv)
@@ -166,7 +213,7 @@ def decode(blob: np.ndarray, shape, dtype: str, bits_k: int, bits_v: int, group:
             b = bits_k if kv == 0 else bits_v
             rb = lay.row_bytes(kv)
             off = lay.codes_slab(l, kv)
-            packed = blob[off:off + T * H * rb].reshape(T * H, rb)
+            packed = untile_codes(blob[off:off + T * H * rb], T * H, rb)
             q = unpack_codes(packed, b, D)
             moff = lay.meta_slab(l, kv)
             m = blob[moff:moff + T * H * (D // G) * 4].view("<u2").reshape(T * H, D // G, 2)

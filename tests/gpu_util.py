@@ -54,10 +54,11 @@ def check_sampled_encode(p, x_gpu, blob_gpu, idx):
         b = p.bits_k if kv == 0 else p.bits_v
         rb = lay.row_bytes(kv)
         ng = lay.groups
-        code_off = torch.from_numpy(np.array([lay.codes_slab(int(li), kv) for li in l]) + r * rb)
+        code_off = torch.from_numpy(np.array([lay.codes_slab(int(li), kv) for li in l])[:, None] +
+                                    oracle.code_offsets(r, rows, rb))
         meta_off = torch.from_numpy(np.array([lay.meta_slab(int(li), kv) for li in l]) + r * ng * 4)
         dev = blob_gpu.device
-        ci = (code_off[:, None] + torch.arange(rb)[None, :]).to(dev)
+        ci = code_off.to(dev)
         mi = (meta_off[:, None] + torch.arange(ng * 4)[None, :]).to(dev)
         codes = blob_gpu[ci].cpu().numpy()
         meta = blob_gpu[mi].cpu().numpy().view("<u2").reshape(len(v), ng, 2)

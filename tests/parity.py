@@ -117,7 +117,7 @@ def blob_rows(blob, lay, l, kv, rows_idx):
     c0 = lay.codes_slab(l, kv)
     m0 = lay.meta_slab(l, kv)
     idx = np.asarray(rows_idx, dtype=np.int64)
-    codes = blob[c0:c0 + lay.rows * rb].reshape(lay.rows, rb)[idx]
+    codes = blob[c0 + oracle.code_offsets(idx, lay.rows, rb)]
     meta = blob[m0:m0 + lay.rows * ng * 4].view("<u2").reshape(lay.rows, ng, 2)[idx]
     return codes, meta
 

@@ -179,9 +179,9 @@ def test_full_size_sampled(name):
         s, r = divmod(int(v), rows)
         l, kv = divmod(s, 2)
         b = p.bits_k if kv == 0 else p.bits_v
-        c0 = lay.codes_slab(l, kv) + r * lay.row_bytes(kv)
+        ci = lay.codes_slab(l, kv) + oracle.code_offsets([r], rows, lay.row_bytes(kv))[0]
         m0 = lay.meta_slab(l, kv) + r * lay.groups * 4
-        codes = out[c0:c0 + lay.row_bytes(kv)].cpu().numpy()
+        codes = out[torch.from_numpy(ci).to(out.device)].cpu().numpy()
         meta = out[m0:m0 + lay.groups * 4].cpu().numpy().view("<u2").reshape(lay.groups, 2)
         q = oracle.unpack_codes(codes[None], b, D)
         yhat = oracle.dequantize(q, meta[None, :, 0].view(np.float16), meta[None, :, 1].view(np.float16), p.group)

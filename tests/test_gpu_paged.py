@@ -46,6 +46,10 @@ CASES = [
     (128, "bf16", 4, 4, 128, 8, [17, 64, 3]),
     (64, "fp16", 8, 2, 32, 2, [15, 16, 31, 2]),
     (128, "fp16", 4, 8, 32, 1, [100, 7]),
+    # 48 and 80 rows per block: block tiles start inside a 64-row code tile
+    # and run into the next one
+    (128, "bf16", 4, 2, 32, 3, [50, 17, 100, 1]),
+    (64, "fp16", 2, 8, 64, 5, [33, 16, 1, 70]),
 ]
 
 

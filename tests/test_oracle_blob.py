@@ -43,8 +43,9 @@ def test_blob_places_each_slab_where_the_layout_says():
             b = p.bits_k if kv == 0 else p.bits_v
             rows = tr.q[l, kv].reshape(-1, p.head_dim)
             off = lay.codes_slab(l, kv)
-            got = blob[off:off + rows.shape[0] * p.head_dim * b // 8]
-            assert np.array_equal(got, oracle.pack_codes(rows, b).reshape(-1))
+            rb = p.head_dim * b // 8
+            got = oracle.untile_codes(blob[off:off + rows.shape[0] * rb], rows.shape[0], rb)
+            assert np.array_equal(got, oracle.pack_codes(rows, b))
             m = blob[lay.meta_slab(l, kv):][: rows.shape[0] * (p.head_dim // p.group) * 4]
             m = m.view("<u2").reshape(-1, 2)
             assert np.array_equal(m[:, 0], tr.scale[l, kv].reshape(-1).view(np.uint16))
@@ -79,7 +80,7 @@ def test_tiny_preset_matches_scalar_twin():
         pick = np.arange(0, x.shape[0], x.shape[0] // rows_per)
         sp, sm, sc = scalar.encode_rows(x[pick].tolist(), p.head_dim, p.group, p.bits_k, p.seed)
         rb = p.head_dim * p.bits_k // 8
-        codes = blob[lay.codes_slab(0, kv):][: x.shape[0] * rb].reshape(-1, rb)
+        codes = oracle.untile_codes(blob[lay.codes_slab(0, kv):], x.shape[0], rb)
         assert np.array_equal(codes[pick], np.array(sp, dtype=np.uint8))
         assert np.array_equal(tr.scale[0, kv].reshape(-1)[pick].view(np.uint16), [m[0][0] for m in sm])
         assert np.array_equal(tr.zero[0, kv].reshape(-1)[pick].view(np.uint16), [m[0][1] for m in sm])
@@ -113,3 +114,38 @@ def test_paged_equals_contiguous_per_request():
             used[table[r][t // 16], t % 16] = True
     assert np.array_equal(out[:, :, ~used], pool[:, :, ~used])
     assert not np.array_equal(out[:, :, used], pool[:, :, used])
+
+
+def test_code_tiles_by_hand():
+    """Tiles of 64 rows; inside a tile, piece c (16 bytes) of row i at (c * n + i) * 16."""
+    R, RB = 67, 32
+    rows = (np.arange(R * RB) % 251).astype(np.uint8).reshape(R, RB)
+    out = oracle.tile_codes(rows)
+    assert out.size == R * RB
+    # first tile, n = 64: piece 0 of rows 0..63, then piece 1 of rows 0..63
+    assert np.array_equal(out[0:16], rows[0, 0:16])
+    assert np.array_equal(out[16:32], rows[1, 0:16])
+    assert np.array_equal(out[63 * 16:64 * 16], rows[63, 0:16])
+    assert np.array_equal(out[64 * 16:65 * 16], rows[0, 16:32])
+    # last tile, n = 3 rows, starts at byte 64 * RB
+    base = 64 * RB
+    assert np.array_equal(out[base:base + 16], rows[64, 0:16])
+    assert np.array_equal(out[base + 32:base + 48], rows[66, 0:16])
+    assert np.array_equal(out[base + 48:base + 64], rows[64, 16:32])
+    assert np.array_equal(out[base + 80:base + 96], rows[66, 16:32])
+    # a single 16-byte piece per row is the plain row-major order
+    one = rows[:, :16].copy()
+    assert np.array_equal(oracle.tile_codes(one), one.reshape(-1))
+
+
+@pytest.mark.parametrize("R,RB", [(1, 16), (63, 64), (64, 32), (65, 128), (200, 64), (129, 16)])
+def test_code_tiles_invert_and_offsets_agree(R, RB):
+    rng = np.random.default_rng(R * 1000 + RB)
+    rows = rng.integers(0, 256, (R, RB), dtype=np.uint8)
+    out = oracle.tile_codes(rows)
+    assert np.array_equal(oracle.untile_codes(out, R, RB), rows)
+    idx = np.arange(R)
+    offs = oracle.code_offsets(idx, R, RB)
+    assert np.array_equal(out[offs], rows)
+    # the offsets are a permutation of the slab's bytes
+    assert np.array_equal(np.sort(offs.reshape(-1)), np.arange(R * RB))
