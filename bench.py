@@ -47,8 +47,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b_4k")
-    ap.add_argument("--cpu-sample-chunks", type=int, default=192)
+    ap.add_argument("--cpu-sample-chunks", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true", help="skip the separate-kernel comparator")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="skip the transfer legs (they launch the fused kernels on layer chunks)")
     return ap.parse_args()
 
 
@@ -330,8 +333,9 @@ def main():
     ms_per_step = wall / a.steps * 1e3
 
     unfused = pipeline = None
-    if not p.paged:
+    if not p.paged and not a.no_unfused:
         unfused = unfused_leg(kvc, p, xs, outs, dsts, a, stream, t_enc, t_dec, raw_bytes)
+    if not p.paged and not a.no_pipeline:
         pipeline = pipeline_leg(kvc, p, xs[0], dsts[0], stream, raw_bytes)
 
     # copy probe: achievable streaming bandwidth in the same run

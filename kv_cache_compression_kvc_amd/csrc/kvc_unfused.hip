@@ -198,48 +198,46 @@ __device__ __forceinline__ void unpack_bytes(uint32_t p, uint32_t* w) {
   for (int k = 0; k < 32 / B; ++k) w[k / 4] |= ((p >> (B * k)) & ((1u << B) - 1)) << (8 * (k % 4));
 }
 
-/* Position of packed piece j of a slab (16 bytes of one code row) in the
- * tiled code order: tiles of 64 rows, and inside a tile of n rows all rows'
- * piece 0, then all rows' piece 1, ...  Returns the row; *c = the piece. */
-template <int RB>
-__device__ __forceinline__ int64_t piece_row(int64_t j, int64_t rows, int* c) {
-  constexpr int64_t PT = int64_t(kTileVectors) * (RB / 16);  // pieces of a full tile
-  const int64_t t = j / PT;
-  const int64_t w = j - t * PT;
-  const int64_t n = min<int64_t>(kTileVectors, rows - t * kTileVectors);
-  *c = static_cast<int>(w / n);
-  return t * kTileVectors + (w - int64_t(*c) * n);
-}
+/*
+ * Pack and unpack move one 64-row code tile per block iteration through
+ * LDS, so that both sides are contiguous: the code bytes of the tile's n
+ * rows (n * D bytes in the byte tensor) and its packed pieces (n * RB bytes
+ * in the blob, piece-major: all rows' piece 0, then piece 1, ...).  LDS rows
+ * are padded by 16 bytes so that consecutive rows fall in different banks.
+ */
+template <int D>
+struct TileStage {
+  static constexpr int kRowV4 = D / 16 + 1;  // LDS row pitch in 16-byte units
+  v4u rows[kTileVectors * kRowV4];
+};
 
-/* E4: one 16-byte packed piece per unit (128/B code bytes in). */
+/* E4: code bytes -> packed pieces, one code tile per block iteration. */
 template <int D, int B>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, const uint8_t* q8) {
-  constexpr int RB = D * B / 8, IN = 8 / B;  // 16-byte loads of code bytes per piece
+  constexpr int RB = D * B / 8, NP = RB / 16, IN = 8 / B, RV = D / 16;  // RV: 16-byte units per code row
+  __shared__ TileStage<D> st;
   const int64_t s = slab_of(a);
-  const int64_t units = a.rows * (RB / 16);
-  const uint8_t* q = q8 + s * a.rows * D;
+  const v4u* q = reinterpret_cast<const v4u*>(q8 + s * a.rows * D);
   v4u* out = reinterpret_cast<v4u*>(codes_of(a, static_cast<uint8_t*>(a.dst), s));
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
-  for (int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; i0 < units; i0 += stride * kUnroll) {
-    uint32_t w[kUnroll][4 * IN];
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int64_t i = i0 + k * stride;
-      int c = 0;
-      const int64_t r = i < units ? piece_row<RB>(i, a.rows, &c) : 0;
-      const v4u* src = reinterpret_cast<const v4u*>(q + r * D + c * (128 / B));
+  const int64_t tiles = (a.rows + kTileVectors - 1) / kTileVectors;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t r0 = t * kTileVectors;
+    const int n = static_cast<int>(min<int64_t>(kTileVectors, a.rows - r0));
+    __syncthreads();  // the previous tile's reads of LDS are done
+    for (int k = threadIdx.x; k < n * RV; k += kThreads)
+      st.rows[(k / RV) * TileStage<D>::kRowV4 + k % RV] = q[r0 * RV + k];
+    __syncthreads();
+    for (int k = threadIdx.x; k < n * NP; k += kThreads) {
+      const int c = k / n, i = k - c * n;
+      const v4u* src = &st.rows[i * TileStage<D>::kRowV4 + c * IN];
+      uint32_t w[4 * IN];
 #pragma unroll
       for (int m = 0; m < IN; ++m) {
-        const v4u t = i < units ? src[m] : v4u{0, 0, 0, 0};
-        w[k][4 * m] = t.x, w[k][4 * m + 1] = t.y, w[k][4 * m + 2] = t.z, w[k][4 * m + 3] = t.w;
+        const v4u v = src[m];
+        w[4 * m] = v.x, w[4 * m + 1] = v.y, w[4 * m + 2] = v.z, w[4 * m + 3] = v.w;
       }
-    }
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int64_t i = i0 + k * stride;
-      if (i < units)
-        out[i] = v4u{pack_bytes<B>(&w[k][0]), pack_bytes<B>(&w[k][IN]), pack_bytes<B>(&w[k][2 * IN]),
-                     pack_bytes<B>(&w[k][3 * IN])};
+      out[r0 * NP + k] =
+          v4u{pack_bytes<B>(&w[0]), pack_bytes<B>(&w[IN]), pack_bytes<B>(&w[2 * IN]), pack_bytes<B>(&w[3 * IN])};
     }
   }
 }
@@ -252,36 +250,33 @@ __global__ __launch_bounds__(64) void padding_kernel(uint8_t* blob, uint64_t cod
 
 /* ---- decode stages ---------------------------------------------------------- */
 
-/* D1: one 16-byte packed piece per unit -> 128/B code bytes of its row. */
+/* D1: packed pieces -> code bytes, one code tile per block iteration. */
 template <int D, int B>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const LaunchArgs a, uint8_t* q8) {
-  constexpr int RB = D * B / 8, OUT = 8 / B;
+  constexpr int RB = D * B / 8, NP = RB / 16, OUT = 8 / B, RV = D / 16;
+  __shared__ TileStage<D> st;
   const int64_t s = slab_of(a);
-  const int64_t units = a.rows * (RB / 16);
   const v4u* in = reinterpret_cast<const v4u*>(
       codes_of(a, const_cast<uint8_t*>(static_cast<const uint8_t*>(a.src)), s));
-  uint8_t* q = q8 + s * a.rows * D;
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
-  for (int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; i0 < units; i0 += stride * kUnroll) {
-    v4u p[kUnroll];
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int64_t i = i0 + k * stride;
-      p[k] = i < units ? in[i] : v4u{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int64_t i = i0 + k * stride;
-      if (i >= units) continue;
-      int c = 0;
-      const int64_t r = piece_row<RB>(i, a.rows, &c);
-      v4u* dst = reinterpret_cast<v4u*>(q + r * D + c * (128 / B));
+  v4u* q = reinterpret_cast<v4u*>(q8 + s * a.rows * D);
+  const int64_t tiles = (a.rows + kTileVectors - 1) / kTileVectors;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t r0 = t * kTileVectors;
+    const int n = static_cast<int>(min<int64_t>(kTileVectors, a.rows - r0));
+    __syncthreads();
+    for (int k = threadIdx.x; k < n * NP; k += kThreads) {
+      const int c = k / n, i = k - c * n;
+      const v4u p = in[r0 * NP + k];
       uint32_t w[4 * OUT];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) unpack_bytes<B>(p[k][m], &w[m * OUT]);
+      for (int m = 0; m < 4; ++m) unpack_bytes<B>(p[m], &w[m * OUT]);
+      v4u* dst = &st.rows[i * TileStage<D>::kRowV4 + c * OUT];
 #pragma unroll
       for (int m = 0; m < OUT; ++m) dst[m] = v4u{w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]};
     }
+    __syncthreads();
+    for (int k = threadIdx.x; k < n * RV; k += kThreads)
+      q[r0 * RV + k] = st.rows[(k / RV) * TileStage<D>::kRowV4 + k % RV];
   }
 }
 
@@ -380,7 +375,7 @@ int encode_launch(const LaunchArgs& a, hipStream_t st, uint8_t* q8, float* u) {
   return for_slab_chunks(a, [&](const LaunchArgs& c, unsigned gy) {
     const unsigned rx = blocks_x(c.rows, rows_per_block<D>(), c.n_slabs);
     const unsigned ex = blocks_x(c.rows * (D / 4), kUnitsPerBlock, c.n_slabs);
-    const unsigned px = blocks_x(c.rows * D * B / 128, kUnitsPerBlock, c.n_slabs);
+    const unsigned px = blocks_x(c.rows, kTileVectors, c.n_slabs);
     hipLaunchKernelGGL((rotate_kernel<D, DT>), dim3(rx, gy), dim3(kThreads), 0, st, c, u);
     hipLaunchKernelGGL((minmax_kernel<D, B, G>), dim3(rx, gy), dim3(kThreads), 0, st, c, u);
     hipLaunchKernelGGL((quantize_kernel<D, B, G>), dim3(ex, gy), dim3(kThreads), 0, st, c, u, q8);
@@ -393,7 +388,7 @@ int decode_launch(const LaunchArgs& a, hipStream_t st, uint8_t* q8, float* z) {
   return for_slab_chunks(a, [&](const LaunchArgs& c, unsigned gy) {
     const unsigned rx = blocks_x(c.rows, rows_per_block<D>(), c.n_slabs);
     const unsigned ex = blocks_x(c.rows * (D / 4), kUnitsPerBlock, c.n_slabs);
-    const unsigned px = blocks_x(c.rows * D * B / 128, kUnitsPerBlock, c.n_slabs);
+    const unsigned px = blocks_x(c.rows, kTileVectors, c.n_slabs);
     hipLaunchKernelGGL((unpack_kernel<D, B>), dim3(px, gy), dim3(kThreads), 0, st, c, q8);
     hipLaunchKernelGGL((dequant_kernel<D, G>), dim3(ex, gy), dim3(kThreads), 0, st, c, q8, z);
     hipLaunchKernelGGL((unrotate_kernel<D, DT>), dim3(rx, gy), dim3(kThreads), 0, st, c, z);
