@@ -491,21 +491,129 @@ __device__ __forceinline__ void dma_rows(const uint8_t* src, int count, v4u* lds
   dma_rows_policy<D, STREAM ? kCacheStream : kCacheDefault>(src, count, lds);
 }
 
-/* Own LDS row -> D fp32 values with the sign flip applied (an exact xor of
- * the sign bit on each packed pair, before widening).  Chunk p of this
- * lane's row v is at slot v * CH + (p ^ (v % CH)) = base ^ p. */
-template <int D, int DT>
-__device__ __forceinline__ void read_row_signed(const v4u* lds, const uint32_t* signs, float (&y)[D]) {
+/* Own LDS row -> its D storage elements, packed (chunk p = elements 8p ..
+ * 8p+7), with the sign flip applied as an exact xor of each sign bit.
+ * Chunk p of this lane's row v is at slot v * CH + (p ^ (v % CH)) = base ^ p. */
+template <int D>
+__device__ __forceinline__ void read_row_signed(const v4u* lds, const uint32_t* signs, v4u (&xc)[D / 8]) {
   constexpr int CH = D / 8;
   const int v = opaque_lane();
   const int base = v * CH + (v % CH);
   const v4u* sg = reinterpret_cast<const v4u*>(signs);
 #pragma unroll
-  for (int p = 0; p < CH; ++p) {
-    const v4u w = lds[base ^ p];
-    const v4u s = sg[p];
+  for (int p = 0; p < CH; ++p) xc[p] = lds[base ^ p] ^ sg[p];
+}
+
+/* ---- transform on the matrix cores ------------------------------------------
+ *
+ * u = H (s * x) for the 64 vectors of a tile as a matrix product on the
+ * MFMA units: U = H X, H the D x D Sylvester matrix, X the D x 64 matrix
+ * whose column j is vector j (lane j's row).  Every product is exact: the
+ * inputs are the stored bf16 / fp16 values and H holds +-1, both exact in
+ * the MFMA operand type, and the sums are kept in fp32.
+ *
+ * v_mfma_f32_32x32x16_{bf16,f16} computes a 32 x 32 block of U from a 32 x
+ * 16 block of H (operand A) and a 16 x 32 block of X (operand B): lane l
+ * supplies A[l % 32][8*(l/32) + e] and B[8*(l/32) + e][l % 32], e < 8, and
+ * receives D[8*(r/4) + 4*(l/32) + r%4][l % 32] in accumulator r < 16.
+ *
+ * Operand B: K-block b of X (rows 16b .. 16b+15) is the lane's chunks 2b
+ * and 2b+1.  Lanes 0-31 must supply the first 8 of those rows for vectors
+ * 0-31 and lanes 32-63 the last 8 of the same vectors; one
+ * v_permlane32_swap per register exchanges chunk 2b+1 of vectors 0-31
+ * with chunk 2b of vectors 32-63, after which chunk 2b is operand B of the
+ * vectors 0-31 and chunk 2b+1 that of the vectors 32-63.
+ *
+ * Operand A: with output block a (rows 32a + i) and K-block b (columns
+ * 16b + k, k = 8*(l/32) + e), the sign of H[32a + i][16b + k] is the parity
+ * of popcount(i & k & 15) + (bit 4 of i)(bit 0 of b) + popcount(a & (b >> 1)).
+ * The first term depends only on the lane and e, the second only on the
+ * lane and whether b is odd, the third is one sign per (a, b): four
+ * operand registers cover every block -- even / odd b, each also negated.
+ *
+ * Results: the accumulators of output block a for vectors 0-31 and for
+ * vectors 32-63 are exchanged the same way (one swap per register), after
+ * which lane j holds element 32a + 8*(r/4) + r%4 of its own vector in the
+ * first and element 32a + 8*(r/4) + 4 + r%4 in the second.
+ *
+ * The compiler shares the partial sums that several output blocks have in
+ * common (the first K-blocks of a and a+1 carry the same signs), so the
+ * 2 * (D/32) * (D/16) products of a D = 128 tile issue as 44 instructions.
+ */
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+struct HadamardA {
+  v4u w[4];  // [even b, odd b, even b negated, odd b negated], 8 values each
+};
+
+template <int DT>
+__device__ __forceinline__ void hadamard_operands(HadamardA& A) {
+  const int l = threadIdx.x;
+  const int i = l & 15, h = (l >> 5) & 1, i4 = (l >> 4) & 1;
+  const uint32_t one = DT == KVC_BF16 ? 0x3F80u : 0x3C00u;  // +1.0 in the storage type
 #pragma unroll
-    for (int i = 0; i < 4; ++i) unpack_pair<DT>(w[i] ^ s[i], y[8 * p + 2 * i], y[8 * p + 2 * i + 1]);
+  for (int m = 0; m < 4; ++m) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int e = 2 * m + half;
+      const uint32_t odd = __builtin_popcount(i & (8 * h + e)) & 1;
+      w |= (one | (odd << 15)) << (16 * half);
+    }
+    A.w[0][m] = w;
+    A.w[1][m] = w ^ (i4 ? 0x80008000u : 0u);
+    A.w[2][m] = A.w[0][m] ^ 0x80008000u;
+    A.w[3][m] = A.w[1][m] ^ 0x80008000u;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16_t mfma_32x32x16(v4u a, v4u b, f32x16_t c) {
+  if constexpr (DT == KVC_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+}
+
+/* Signed packed row chunks of every lane -> u = H (s * x) of the lane's own
+ * vector, D fp32 values in element order.  `xc` is consumed. */
+template <int D, int DT>
+__device__ __forceinline__ void hadamard_mfma(v4u (&xc)[D / 8], const HadamardA& A, float (&u)[D]) {
+  constexpr int KB = D / 16, OB = D / 32;
+#pragma unroll
+  for (int b = 0; b < KB; ++b) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const auto r = __builtin_amdgcn_permlane32_swap(xc[2 * b][m], xc[2 * b + 1][m], false, false);
+      xc[2 * b][m] = r[0];
+      xc[2 * b + 1][m] = r[1];
+    }
+  }
+  f32x16_t acc[OB][2];
+#pragma unroll
+  for (int a = 0; a < OB; ++a) {
+    acc[a][0] = f32x16_t{};
+    acc[a][1] = f32x16_t{};
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      const int sel = ((__builtin_popcount(a & (b >> 1)) & 1) << 1) | (b & 1);
+      acc[a][0] = mfma_32x32x16<DT>(A.w[sel], xc[2 * b], acc[a][0]);
+      acc[a][1] = mfma_32x32x16<DT>(A.w[sel], xc[2 * b + 1], acc[a][1]);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < OB; ++a) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const auto s =
+          __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[a][0][r]), __float_as_uint(acc[a][1][r]), false, false);
+      u[32 * a + 8 * (r / 4) + (r % 4)] = __uint_as_float(s[0]);
+      u[32 * a + 8 * (r / 4) + 4 + (r % 4)] = __uint_as_float(s[1]);
+    }
   }
 }
 
@@ -563,14 +671,13 @@ __device__ __forceinline__ void quantize_group(const float* y, float A, float Bz
   *words = pack_word<B>(tq);
 }
 
+/* Meta, codes and stores of one vector from its unnormalized rotated values u. */
 template <int D, int B, int G, bool PAGED>
 __device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t) {
   constexpr int NG = D / G;
   constexpr float QMAX = float((1 << B) - 1);
   constexpr int WPG = G * B / 32;  // code words per group
   constexpr int VPW = 32 / B;      // values per code word
-  fwht<D>(y);
-  KVC_PHASE();
   uint32_t meta[NG];
   uint32_t words[D * B / 32];
 #pragma unroll
@@ -636,14 +743,19 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
   dma_rows<D, !PAGED>(cur.src, cur.count, lds);
   wait_vmem<0>();
   lds_order();
+  HadamardA had;
+  hadamard_operands<DT>(had);
   for (;;) {
-    float y[D];
-    read_row_signed<D, DT>(lds, signs, y);
+    v4u xc[D / 8];
+    read_row_signed<D>(lds, signs, xc);
     KVC_PHASE();
     lds_done();  // every lane's row is in registers: the buffer is free
     Tile nxt;
     const bool more = next_tile<D, true, PAGED>(a, c, tensor, blob, nxt, false);
     if (more) dma_rows<D, !PAGED>(nxt.src, nxt.count, lds);
+    KVC_PHASE();
+    float y[D];
+    hadamard_mfma<D, DT>(xc, had, y);
     KVC_PHASE();
     encode_vector<D, B, G, PAGED>(y, cur);
     if (!more) break;
@@ -781,17 +893,28 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   }
 }
 
-/* ---- rotate (test hook) ---------------------------------------------------- */
+/* ---- rotate ------------------------------------------------------------------ */
 
-template <int D, int DT>
-KVC_KERNEL void rotate_kernel(const LaunchArgs a) {
+/*
+ * The transform of the encode alone: per tile the same DMA, row read and
+ * MFMA transform, then the D fp32 values of every vector to `out`
+ * ([vectors, D], the tensor's vector order): u = H (s * x) when RAW, else
+ * the rotated values y = u / sqrt(D).  The tile's rows go out through LDS
+ * a quarter row at a time (the tile buffer, free once the rows are in
+ * registers), as coalesced 16-byte stores.
+ */
+template <int D, int DT, bool RAW>
+__device__ __forceinline__ void rotate_tiles(const LaunchArgs& a, float* out) {
   constexpr int CH = D / 8;
+  constexpr int QC = D / 16;  // 16-byte chunks of fp32 per quarter row
   constexpr float RS = Norm<D>::inv_sqrt;
   __shared__ v4u lds[kTileVectors * CH];
   __shared__ uint32_t signs[64];
   const uint8_t* tensor = static_cast<const uint8_t*>(a.src);
-  float* yout = static_cast<float*>(a.dst);
+  const int lane = threadIdx.x;
   load_signs(a, signs);
+  HadamardA had;
+  hadamard_operands<DT>(had);
   Cursor c;
   cursor_init<false>(a, c);
   Tile t;
@@ -801,17 +924,40 @@ KVC_KERNEL void rotate_kernel(const LaunchArgs a) {
     dma_rows<D, false>(t.src, t.count, lds);
     wait_vmem<0>();
     lds_order();
-    float y[D];
-    read_row_signed<D, DT>(lds, signs, y);
-    fwht<D>(y);
-    if (static_cast<int>(threadIdx.x) < t.count) {
-      const int64_t vec = (t.src - tensor) / (2 * D) + threadIdx.x;
-      float4* o = reinterpret_cast<float4*>(yout + vec * D);
+    v4u xc[CH];
+    read_row_signed<D>(lds, signs, xc);
+    float u[D];
+    hadamard_mfma<D, DT>(xc, had, u);
+    const int64_t vec0 = (t.src - tensor) / (2 * D);
+    v4u* dst = reinterpret_cast<v4u*>(out + vec0 * D);
 #pragma unroll
-      for (int q = 0; q < D / 4; ++q)
-        o[q] = float4(y[4 * q] * RS, y[4 * q + 1] * RS, y[4 * q + 2] * RS, y[4 * q + 3] * RS);
+    for (int h = 0; h < 4; ++h) {
+      // chunk q of this lane's quarter row h goes to LDS column q ^ (lane % QC)
+      lds_done();
+      lds_order();
+#pragma unroll
+      for (int q = 0; q < QC; ++q) {
+        const int e = h * (D / 4) + 4 * q;
+        v4u w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = __float_as_uint(RAW ? u[e + k] : u[e + k] * RS);
+        lds[lane * QC + (q ^ (lane % QC))] = w;
+      }
+      lds_order();
+#pragma unroll
+      for (int k = 0; k < QC; ++k) {
+        const int slot = k * 64 + lane;
+        const int v = slot / QC;
+        const int q = (slot % QC) ^ (v % QC);
+        if (v < t.count) dst[v * (D / 4) + h * QC + q] = lds[slot];
+      }
     }
   }
+}
+
+template <int D, int DT>
+KVC_KERNEL void rotate_kernel(const LaunchArgs a) {
+  rotate_tiles<D, DT, false>(a, static_cast<float*>(a.dst));
 }
 
 }  // namespace dev

@@ -8,7 +8,7 @@
  * removing the intermediate tensor and the repeated memory accesses.
  *
  * Encode (contiguous [L, 2, T, H, D] tensors), per (layer, K/V) slab:
- *   E1 rotate    x (bf16 / fp16)  -> u  fp32 [rows, D]  sign flip + butterfly
+ *   E1 rotate    x (bf16 / fp16)  -> u  fp32 [rows, D]  sign flip + transform
  *   E2 minmax    u                -> meta (the blob's meta section)
  *   E3 quantize  u, meta          -> q  u8 [rows, D]
  *   E4 pack      q                -> codes (the blob's codes section, in its
@@ -19,10 +19,11 @@
  *   D2 dequant   q, meta          -> z  fp32 [rows, D]  (1/sqrt(D) folded in)
  *   D3 unrotate  z                -> x  butterfly, sign flip, round to dtype
  *
- * Each stage makes the same binary32 decisions as the fused kernels (same
- * butterfly order and operand order, the same meta and code arithmetic), so
- * the blob and the decoded tensor are bit-identical to theirs; only the
- * memory traffic differs.  The stages are written to run near the HBM
+ * Each stage makes the same binary32 decisions as the fused kernels (E1 is
+ * the fused encode's transform code; the inverse butterfly runs in the same
+ * stage and operand order; the meta and code arithmetic are the same
+ * functions), so the blob and the decoded tensor are bit-identical to
+ * theirs; only the memory traffic differs.  The stages are written to run near the HBM
  * bound on their own: 256-thread blocks, vector loads and stores that are
  * contiguous across the wave, butterfly stages across lanes by shuffles.
  */
@@ -44,6 +45,7 @@ constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
 constexpr int kUnroll = 4;           // independent rows / units per thread per iteration
 constexpr int64_t kMaxBlocks = 8192;  // blocks per launch (all slabs together)
+constexpr int64_t kRotateBlocks = 2048;  // one-wave blocks of E1: 256 CUs x 8 resident
 
 __device__ __forceinline__ int64_t slab_of(const LaunchArgs& a) {
   return int64_t(blockIdx.y) * a.slab_step + a.slab_first;
@@ -74,34 +76,12 @@ __device__ __forceinline__ void fwht_lanes(float (&v)[4], int m) {
 
 /* ---- encode stages ---------------------------------------------------------- */
 
-/* E1: one row per D/4 lanes, 4 elements per lane. */
+/* E1: the fused encode's own transform stage (tile DMA, matrix-core
+ * Hadamard) writing u = H (s * x) in fp32, so that the later stages see
+ * exactly the values the fused kernel quantizes. */
 template <int D, int DT>
-__global__ __launch_bounds__(kThreads) void rotate_kernel(const LaunchArgs a, float* u) {
-  constexpr int LPR = D / 4, RPW = 64 / LPR, STEP = RPW * kUnroll;
-  const int lane = threadIdx.x & 63, m = lane % LPR, sub = lane / LPR;
-  const int64_t s = slab_of(a);
-  const v2u* x = static_cast<const v2u*>(a.src) + s * a.rows * LPR;
-  float4* y = reinterpret_cast<float4*>(u) + s * a.rows * LPR;
-  const uint32_t s0 = a.sign_words[2 * m], s1 = a.sign_words[2 * m + 1];
-  const int64_t wave = int64_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / 64;
-  const int64_t stride = int64_t(gridDim.x) * kWavesPerBlock * STEP;
-  for (int64_t r0 = wave * STEP; r0 < a.rows; r0 += stride) {  // wave-uniform
-    v2u w[kUnroll];
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int64_t r = r0 + k * RPW + sub;
-      w[k] = r < a.rows ? x[r * LPR + m] : v2u{0, 0};
-    }
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      float v[4];
-      dev::unpack_pair<DT>(w[k].x ^ s0, v[0], v[1]);
-      dev::unpack_pair<DT>(w[k].y ^ s1, v[2], v[3]);
-      fwht_lanes<D>(v, m);
-      const int64_t r = r0 + k * RPW + sub;
-      if (r < a.rows) y[r * LPR + m] = float4(v[0], v[1], v[2], v[3]);
-    }
-  }
+KVC_KERNEL void rotate_kernel(const LaunchArgs a, float* u) {
+  dev::rotate_tiles<D, DT, true>(a, u);
 }
 
 /* E2: min / max per group across G/4 lanes, then the meta word. */
@@ -372,11 +352,16 @@ int for_slab_chunks(const LaunchArgs& a, F fn) {
 
 template <int D, int DT, int B, int G>
 int encode_launch(const LaunchArgs& a, hipStream_t st, uint8_t* q8, float* u) {
+  // E1 walks the launch's tiles on a persistent grid of one-wave blocks
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(a.total_items, kRotateBlocks));
+  if (grid > 0) {
+    hipLaunchKernelGGL((rotate_kernel<D, DT>), dim3(grid), dim3(64), 0, st, a, u);
+    if (hipGetLastError() != hipSuccess) return KVC_EHIP;
+  }
   return for_slab_chunks(a, [&](const LaunchArgs& c, unsigned gy) {
     const unsigned rx = blocks_x(c.rows, rows_per_block<D>(), c.n_slabs);
     const unsigned ex = blocks_x(c.rows * (D / 4), kUnitsPerBlock, c.n_slabs);
     const unsigned px = blocks_x(c.rows, kTileVectors, c.n_slabs);
-    hipLaunchKernelGGL((rotate_kernel<D, DT>), dim3(rx, gy), dim3(kThreads), 0, st, c, u);
     hipLaunchKernelGGL((minmax_kernel<D, B, G>), dim3(rx, gy), dim3(kThreads), 0, st, c, u);
     hipLaunchKernelGGL((quantize_kernel<D, B, G>), dim3(ex, gy), dim3(kThreads), 0, st, c, u, q8);
     hipLaunchKernelGGL((pack_kernel<D, B>), dim3(px, gy), dim3(kThreads), 0, st, c, q8);
