@@ -31,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -59,12 +60,20 @@ def parse():
 FUSED_SOURCES = ["kvc_device.h", "kvc_host.cpp", "kvc_inst.hip", "kvc_launch.hip", "kvc_pick.h", "kvc_plan.h"]
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed, so that
+    editing a comment does not count as changing the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_compression_kvc_amd", "csrc")
     for name in FUSED_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

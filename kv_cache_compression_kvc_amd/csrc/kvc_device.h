@@ -20,11 +20,16 @@
  *     instruction, fully coalesced, no register staging), laid out with an
  *     XOR swizzle so that the per-lane row reads are free of bank conflicts;
  *     every lane then owns one whole vector in registers;
- *   - the Walsh-Hadamard butterfly, the group min/max, the fp16 meta, the
- *     quantization and the packing all run inside the lane: no cross-lane
- *     traffic, no intermediate in memory;
- *   - as soon as the rows are in registers the DMA of the wave's next tile
- *     starts into the same buffer, so HBM reads overlap the arithmetic.
+ *   - encode: the Walsh-Hadamard transform of the tile runs on the matrix
+ *     cores (exact bf16 / fp16 products against +-1, fp32 sums), after
+ *     which every lane again holds its own vector; the group min/max, the
+ *     fp16 meta, the quantization and the packing run inside the lane;
+ *   - decode: dequantization, the fp32 butterfly and the rounding to the
+ *     storage type run inside the lane; the rows leave through LDS as
+ *     coalesced stores;
+ *   - no intermediate touches memory, and as soon as a tile's rows (or
+ *     codes) are in registers the wave's next tile is requested, so HBM
+ *     traffic overlaps the arithmetic.
  */
 #ifndef KVC_DEVICE_H
 #define KVC_DEVICE_H
