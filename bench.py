@@ -364,8 +364,10 @@ def main():
         e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_enc = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps / 1e3   # s per encode
-    t_dec = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps / 1e3
+    enc_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    t_enc = sum(enc_ms) / a.steps / 1e3   # s per encode (mean)
+    t_dec = sum(dec_ms) / a.steps / 1e3
     ms_per_step = wall / a.steps * 1e3
 
     unfused = pipeline = None
@@ -404,10 +406,10 @@ def main():
         "config": workload,
         "encode": {"raw_GBps": raw_bytes / t_enc / 1e9, "hbm_GBps": enc_alg,
                    "frac_hbm_peak": enc_alg / HBM_PEAK_GBPS, "frac_copy_probe": enc_alg / copy_gbps,
-                   "ms": t_enc * 1e3},
+                   "ms": t_enc * 1e3, "ms_median": enc_ms[len(enc_ms) // 2], "ms_min": enc_ms[0]},
         "decode": {"raw_GBps": raw_bytes / t_dec / 1e9, "hbm_GBps": dec_alg,
                    "frac_hbm_peak": dec_alg / HBM_PEAK_GBPS, "frac_copy_probe": dec_alg / copy_gbps,
-                   "ms": t_dec * 1e3},
+                   "ms": t_dec * 1e3, "ms_median": dec_ms[len(dec_ms) // 2], "ms_min": dec_ms[0]},
         "bytes": {"raw": raw_bytes, "encoded": enc_bytes, "ratio": raw_bytes / enc_bytes},
         "copy_probe_GBps": copy_gbps,
         "break_even": be,
