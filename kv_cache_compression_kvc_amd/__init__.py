@@ -49,6 +49,10 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _check_cuda(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
@@ -89,7 +93,7 @@ def encode(kv, bits_k, bits_v, group, seed=0, out=None, stream=None):
     if out is None:
         out = torch.empty(total, dtype=torch.uint8, device=kv.device)
     d = _desc(L, T, H, D, dt, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_encode(ctypes.byref(d), _ptr(kv), _ptr(out), out.numel(), _stream(stream)))
+    _lib.check(_lib.lib().kvc_encode(ctypes.byref(d), _ptr(kv), _ptr(out), _nbytes(out), _stream(stream)))
     return out
 
 
@@ -100,7 +104,7 @@ def decode(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, stream=N
     if out is None:
         out = torch.empty(tuple(shape), dtype=_NAME_TO_TORCH[dtype], device=blob.device)
     d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_decode(ctypes.byref(d), _ptr(blob), blob.numel(), _ptr(out), _stream(stream)))
+    _lib.check(_lib.lib().kvc_decode(ctypes.byref(d), _ptr(blob), _nbytes(blob), _ptr(out), _stream(stream)))
     return out
 
 
@@ -131,8 +135,8 @@ def encode_unfused(kv, bits_k, bits_v, group, seed=0, out=None, workspace=None, 
         out = torch.empty(total, dtype=torch.uint8, device=kv.device)
     ws = _workspace(workspace, unfused_workspace_size(L, T, H, D, bits_k, bits_v, group, dt), kv.device)
     d = _desc(L, T, H, D, dt, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_encode_unfused(ctypes.byref(d), _ptr(kv), _ptr(out), out.numel(), _ptr(ws),
-                                             ws.numel(), _stream(stream)))
+    _lib.check(_lib.lib().kvc_encode_unfused(ctypes.byref(d), _ptr(kv), _ptr(out), _nbytes(out), _ptr(ws),
+                                             _nbytes(ws), _stream(stream)))
     return out
 
 
@@ -144,8 +148,8 @@ def decode_unfused(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, 
         out = torch.empty(tuple(shape), dtype=_NAME_TO_TORCH[dtype], device=blob.device)
     ws = _workspace(workspace, unfused_workspace_size(L, T, H, D, bits_k, bits_v, group, dtype), blob.device)
     d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_decode_unfused(ctypes.byref(d), _ptr(blob), blob.numel(), _ptr(out), _ptr(ws),
-                                             ws.numel(), _stream(stream)))
+    _lib.check(_lib.lib().kvc_decode_unfused(ctypes.byref(d), _ptr(blob), _nbytes(blob), _ptr(out), _ptr(ws),
+                                             _nbytes(ws), _stream(stream)))
     return out
 
 
@@ -161,7 +165,7 @@ def chunked_size(layers, tokens, kv_heads, head_dim, bits_k, bits_v, group, chun
 def encode_send(kv, bits_k, bits_v, group, chunk_layers, dst, seed=0, out=None, compute_stream=None,
                 copy_stream=None):
     """Encode layer chunks on ``compute_stream`` and copy each finished chunk
-    into ``dst`` (pinned host or device uint8 tensor) on ``copy_stream``."""
+    into ``dst`` (a pinned host or device tensor) on ``copy_stream``."""
     _check_cuda(kv, out)
     if not dst.is_contiguous():
         raise ValueError("dst must be contiguous")
@@ -171,28 +175,30 @@ def encode_send(kv, bits_k, bits_v, group, chunk_layers, dst, seed=0, out=None, 
     if out is None:
         out = torch.empty(total, dtype=torch.uint8, device=kv.device)
     d = _desc(L, T, H, D, dt, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_encode_send(ctypes.byref(d), _ptr(kv), _ptr(out), out.numel(), int(chunk_layers),
-                                          _ptr(dst), dst.numel(), _stream(compute_stream),
+    _lib.check(_lib.lib().kvc_encode_send(ctypes.byref(d), _ptr(kv), _ptr(out), _nbytes(out), int(chunk_layers),
+                                          _ptr(dst), _nbytes(dst), _stream(compute_stream),
                                           _stream(copy_stream)))
     return out
 
 
 def receive_decode(src, shape, dtype, bits_k, bits_v, group, chunk_layers, seed=0, staging=None, out=None,
                    compute_stream=None, copy_stream=None):
-    """Copy layer chunks of ``src`` (host or device) into ``staging`` on
-    ``copy_stream`` and decode each on ``compute_stream`` into ``out``."""
+    """Copy layer chunks of ``src`` (a pinned host or device tensor) into
+    ``staging`` on ``copy_stream`` and decode each on ``compute_stream``
+    into ``out``."""
     _check_cuda(staging, out)
     if not src.is_contiguous():
         raise ValueError("src must be contiguous")
     L, two, T, H, D = shape
     total, _ = chunked_size(L, T, H, D, bits_k, bits_v, group, chunk_layers, dtype)
     if staging is None:
-        staging = torch.empty(max(total, 1), dtype=torch.uint8, device="cuda")
+        device = src.device if src.is_cuda else torch.device("cuda", torch.cuda.current_device())
+        staging = torch.empty(max(total, 1), dtype=torch.uint8, device=device)
     if out is None:
         out = torch.empty(tuple(shape), dtype=_NAME_TO_TORCH[dtype], device=staging.device)
     d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_receive_decode(ctypes.byref(d), _ptr(src), src.numel(), _ptr(staging),
-                                             staging.numel(), int(chunk_layers), _ptr(out),
+    _lib.check(_lib.lib().kvc_receive_decode(ctypes.byref(d), _ptr(src), _nbytes(src), _ptr(staging),
+                                             _nbytes(staging), int(chunk_layers), _ptr(out),
                                              _stream(compute_stream), _stream(copy_stream)))
     return out
 
@@ -230,7 +236,7 @@ def encode_paged(pool, block_table, seq_lens, out_offsets, total, bits_k, bits_v
     pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag)
     d = _desc(L, 0, H, D, dt, bits_k, bits_v, group, seed)
     _lib.check(_lib.lib().kvc_encode_paged(ctypes.byref(d), _ptr(pool), ctypes.byref(pg), _ptr(out),
-                                           out.numel(), _stream(stream)))
+                                           _nbytes(out), _stream(stream)))
     return out
 
 
@@ -242,7 +248,7 @@ def decode_paged(blob, pool, block_table, seq_lens, out_offsets, bits_k, bits_v,
     dt = _TORCH_TO_NAME[pool.dtype]
     pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag)
     d = _desc(L, 0, H, D, dt, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_decode_paged(ctypes.byref(d), _ptr(blob), blob.numel(), ctypes.byref(pg),
+    _lib.check(_lib.lib().kvc_decode_paged(ctypes.byref(d), _ptr(blob), _nbytes(blob), ctypes.byref(pg),
                                            _ptr(pool), _stream(stream)))
     return pool
 
@@ -261,8 +267,8 @@ def debug_rotate(kv, seed=0, out=None, stream=None):
 def probe_copy(src, dst, stream=None):
     """Streaming device copy of src into dst (same byte size)."""
     _check_cuda(src, dst)
-    nbytes = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() < nbytes:
+    nbytes = _nbytes(src)
+    if _nbytes(dst) < nbytes:
         raise ValueError("destination too small")
     _lib.check(_lib.lib().kvc_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
     return dst
