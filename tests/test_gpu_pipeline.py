@@ -107,3 +107,18 @@ def test_pipeline_validation():
         kvc.encode_send(x, 4, 4, 32, 1, torch.zeros((1 << 16) + 16, dtype=torch.uint8, pin_memory=True)[4:])
     with pytest.raises(kvc.KvcError, match="KVC_EINVAL"):
         kvc.receive_decode(torch.zeros(1 << 16, dtype=torch.uint8), x.shape, "bf16", 4, 4, 32, 1)
+
+
+def test_documented_usage():
+    """The Python usage shown in the design document runs as written (smaller shape)."""
+    kv = torch.randn(4, 2, 256, 8, 128, device=DEV).to(torch.bfloat16)
+    blob = kvc.encode(kv, bits_k=4, bits_v=4, group=128, seed=0)
+    back = kvc.decode(blob, kv.shape, "bf16", 4, 4, 128, seed=0)
+    total, _ = kvc.chunked_size(4, 256, 8, 128, 4, 4, 128, chunk_layers=2)
+    host = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+    copy = torch.cuda.Stream()
+    kvc.encode_send(kv, 4, 4, 128, 2, host, seed=0, copy_stream=copy)
+    torch.cuda.synchronize()
+    rel = ((back.float() - kv.float()).norm() / kv.float().norm()).item()
+    assert rel < 0.15, rel           # 4-bit codes: about 8% relative error on Gaussian data
+    assert torch.equal(host.to(DEV), _per_chunk_blob(_preset(4, 256, 8, 4, 4, 128).with_(seed=0), kv, 2))
