@@ -284,7 +284,7 @@ def copy_probe(kvc, dev, stream, reps=40):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: this library has no multi-GPU path "
               "(every tile is independent; see the sharding note in the design document).",
               file=sys.stderr)
         sys.exit(2)

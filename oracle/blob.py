@@ -43,7 +43,7 @@ def _align256(n: int) -> int:
 TILE_ROWS = 64   # rows of one code tile
 PIECE = 16       # bytes of one piece of a code row
 
-# Order of the code bytes inside a slab (this build's own reading; the pages
+# Order of the code bytes inside a slab (this library's own reading; the pages
 # fix no byte format).  Rows are cut into tiles of TILE_ROWS consecutive rows
 # (the last tile may be shorter, n rows); tile k starts at byte
 # k * TILE_ROWS * RB of the slab.  Inside a tile each row's RB bytes are cut
