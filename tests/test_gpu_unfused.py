@@ -95,8 +95,9 @@ def test_unfused_workspace_validation():
 
 
 @pytest.mark.slow
-def test_unfused_full_size_equals_fused():
-    p = presets.preset("llama3_8b_4k")
+@pytest.mark.parametrize("name", ["llama3_8b_4k", "llama3_8b_32k"])
+def test_unfused_full_size_equals_fused(name):
+    p = presets.preset(name)
     _say("unfused full size: generate", p.name)
     x = inputs.make_kv(p, device=DEV)
     out_f, out_u, dec_f, dec_u = _both(p, x)
