@@ -189,3 +189,23 @@ def test_full_size_sampled(name):
     parity.check_decode(got, np.stack(refs), p.dtype, axis_slices=(1,))
     del x, xd, whole, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_subnormal_and_tiny_inputs(dtype):
+    """Subnormal storage values go through the matrix-core transform exactly like
+    ordinary ones (criterion 1 on rows made only of them), and encode to valid blobs."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    g = torch.Generator().manual_seed(0)
+    tiny = torch.finfo(tdt).tiny
+    x = torch.zeros(1, 2, 64, 1, 128, dtype=tdt)
+    x[0, 0, :32] = (torch.randn(32, 1, 128, generator=g) * tiny * 0.25).to(tdt)
+    x[0, 0, 32:] = (torch.randn(32, 1, 128, generator=g) * tiny * 4).to(tdt)
+    x[0, 1] = torch.randn(64, 1, 128, generator=g).to(tdt)
+    xb = inputs.as_u16(x)
+    _say("subnormal inputs", dtype)
+    y = kvc.debug_rotate(x.to(DEV), seed=1).cpu().numpy()
+    yref = oracle.rotate(oracle.storage_to_f64(xb, dtype), oracle.sign_vector(1, 128))
+    parity.check_rotation(y, yref)
+    blob = kvc.encode(x.to(DEV), 4, 4, 128, seed=1)
+    parity.check_blob(xb, blob.cpu().numpy(), dtype, 4, 4, 128, 1)
