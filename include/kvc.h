@@ -49,7 +49,10 @@
  *   - launch failures are reported as KVC_EHIP.
  *
  * Supported: head_dim 64 or 128; bits 2, 4 or 8; group 32, 64 or 128 with
- * group <= head_dim; dtype bf16 or fp16.
+ * group <= head_dim; dtype bf16 or fp16.  Input values must be finite, and
+ * the rotated values y must fit the fp16 range of the meta (|y| <= 65504);
+ * a group that breaks this gets unspecified meta and codes (nothing is read
+ * or written out of bounds).  Subnormal inputs are handled exactly.
  */
 #ifndef KVC_H
 #define KVC_H
