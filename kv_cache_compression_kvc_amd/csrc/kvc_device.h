@@ -445,6 +445,18 @@ __device__ __forceinline__ void lds_done() { asm volatile("s_waitcnt lgkmcnt(0)"
 
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
+/* s_waitcnt immediate for vmcnt(0) with the other counters left alone
+ * (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8). */
+constexpr int kWaitVmem0 = 0x0f70;
+
+/* Raw buffer resource over `bytes` bytes from `base` (stride 0): a vector
+ * store at a byte offset of `bytes` or more is dropped, a load there reads
+ * zero.  0x00020000 in the last word is data format 32, which raw buffer
+ * accesses need to be valid at all. */
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
+}
+
 /* This lane's index as a value the compiler cannot see through: address
  * arithmetic derived from it stays inside the loop that uses it instead of
  * being hoisted out and held in registers (or spilled) across the loop. */
@@ -817,17 +829,29 @@ __device__ __forceinline__ void load_codes(const Tile& t, CodeRegs<D, B, G>& r) 
 /*
  * Decode: per tile, each lane dequantizes its own vector from the prefetched
  * codes, runs the butterfly, packs to the storage type with the sign flip and
- * writes its row to LDS, half a row at a time; the wave then stores the half
- * rows with coalesced 16-byte stores.  The next tile's codes are loaded into
- * registers while the current one is computed.
+ * writes its row to LDS one 128-byte line (8 chunks) at a time; the wave then
+ * stores those lines with coalesced 16-byte stores, every store instruction
+ * covering 8 whole lines (a pass that wrote half lines, as half rows of a
+ * D = 64 tile are, left each line to be finished by a later instruction and
+ * ran 1.4x slower).  The next tile's codes are loaded into registers while
+ * the current one is computed.
+ *
+ * The stores go through a buffer resource that spans the tile's `count`
+ * rows, so the stores of rows past the count are dropped by the hardware
+ * instead of being skipped by a branch around each store (those branches,
+ * with their exec-mask saves and restores, cost 3% at 16k-32k tokens).
+ * Each tile starts once the previous tile's stores have completed: letting
+ * them overlap the next tile measured no faster at 16k-32k tokens and up to
+ * 2% slower at 4k.
  */
 template <int D, int DT, int B, int G, bool PAGED>
 KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   constexpr int CH = D / 8, NG = D / G;
   constexpr float RS = Norm<D>::inv_sqrt;
   constexpr int WPG = G * B / 32, VPW = 32 / B;
-  constexpr int HALF = CH / 2;                    // chunks per row staged at a time
-  __shared__ v4u lds_out[kTileVectors * HALF];    // half of every row of the tile
+  constexpr int HALF = 8;                         // chunks per row staged at a time: one line
+  constexpr int NPASS = CH / HALF;
+  __shared__ v4u lds_out[kTileVectors * HALF];    // one line of every row of the tile
   __shared__ uint32_t signs[64];
   uint8_t* tensor = static_cast<uint8_t*>(a.dst);
   uint8_t* blob = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.src));
@@ -840,6 +864,7 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   CodeRegs<D, B, G> cr;
   load_codes<D, B, G, PAGED>(cur, cr);
   for (;;) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this tile's codes, the last tile's stores
     float y[D];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -863,11 +888,11 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
     fwht<D>(y);
     KVC_PHASE();
     const v4u* sg = reinterpret_cast<const v4u*>(signs);
-    v4u* out = reinterpret_cast<v4u*>(const_cast<uint8_t*>(cur.src));
+    const __amdgpu_buffer_rsrc_t out = tile_rsrc(cur.src, cur.count * CH * 16);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // chunks [h*HALF, h*HALF + HALF) of every row through LDS; half-row
-      // chunk q of row v sits in column q ^ (v % HALF)
+    for (int h = 0; h < NPASS; ++h) {
+      // chunks [h*HALF, h*HALF + HALF) of every row through LDS; chunk q of
+      // line h of row v sits in column q ^ (v % HALF)
       lds_order();
 #pragma unroll
       for (int q = 0; q < HALF; ++q) {
@@ -885,12 +910,8 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
         const int slot = k * 64 + lane;
         const int v = slot / HALF;
         const int q = (slot % HALF) ^ (v % HALF);
-        if (v < cur.count) {
-          if constexpr (!PAGED)
-            __builtin_nontemporal_store(lds_out[slot], out + v * CH + h * HALF + q);
-          else
-            out[v * CH + h * HALF + q] = lds_out[slot];
-        }
+        __builtin_amdgcn_raw_buffer_store_b128(lds_out[slot], out, uint32_t((v * CH + h * HALF + q) * 16), 0,
+                                               PAGED ? kCacheDefault : kCacheStream);
       }
     }
     if (!more) break;
@@ -905,13 +926,15 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
  * MFMA transform, then the D fp32 values of every vector to `out`
  * ([vectors, D], the tensor's vector order): u = H (s * x) when RAW, else
  * the rotated values y = u / sqrt(D).  The tile's rows go out through LDS
- * a quarter row at a time (the tile buffer, free once the rows are in
- * registers), as coalesced 16-byte stores.
+ * one 128-byte line (32 values) of every row at a time (in the tile buffer,
+ * free once the rows are in registers), as coalesced 16-byte stores that
+ * each cover 8 whole lines.
  */
 template <int D, int DT, bool RAW>
 __device__ __forceinline__ void rotate_tiles(const LaunchArgs& a, float* out) {
   constexpr int CH = D / 8;
-  constexpr int QC = D / 16;  // 16-byte chunks of fp32 per quarter row
+  constexpr int QC = 8;       // 16-byte chunks of fp32 per line
+  constexpr int NPASS = D / 32;
   constexpr float RS = Norm<D>::inv_sqrt;
   __shared__ v4u lds[kTileVectors * CH];
   __shared__ uint32_t signs[64];
@@ -936,13 +959,13 @@ __device__ __forceinline__ void rotate_tiles(const LaunchArgs& a, float* out) {
     const int64_t vec0 = (t.src - tensor) / (2 * D);
     v4u* dst = reinterpret_cast<v4u*>(out + vec0 * D);
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      // chunk q of this lane's quarter row h goes to LDS column q ^ (lane % QC)
+    for (int h = 0; h < NPASS; ++h) {
+      // chunk q of this lane's line h goes to LDS column q ^ (lane % QC)
       lds_done();
       lds_order();
 #pragma unroll
       for (int q = 0; q < QC; ++q) {
-        const int e = h * (D / 4) + 4 * q;
+        const int e = h * 32 + 4 * q;
         v4u w;
 #pragma unroll
         for (int k = 0; k < 4; ++k) w[k] = __float_as_uint(RAW ? u[e + k] : u[e + k] * RS);

@@ -61,7 +61,11 @@ def test_encode_decode_small(D, dtype, bk, bv, G):
     # decode of the GPU blob, checked against the oracle's decode of the same blob
     # (decoupled from encode) and of its own blob (criterion 4)
     _say("decode", p.name)
-    xd = kvc.decode(out, x.shape, dtype, bk, bv, G, seed=p.seed)
+    dwhole, draw = gpu_util.guarded(x.numel() * 2, DEV)
+    xd = draw.view(x.dtype).view(x.shape)
+    kvc.decode(out, x.shape, dtype, bk, bv, G, seed=p.seed, out=xd)
+    torch.cuda.synchronize()
+    assert gpu_util.canaries_intact(dwhole), "decode wrote outside its output"
     xd_b = inputs.as_u16(xd)
     ref_same, _ = oracle.decode(blob, x.shape, dtype, bk, bv, G, p.seed)
     parity.check_decode(xd_b, ref_same, dtype)
@@ -97,8 +101,11 @@ def test_edge_shapes(L, T, H):
     x = inputs.make_kv(p).to(DEV)
     _say("edge", L, T, H)
     blob = kvc.encode(x, 4, 2, 64, seed=p.seed)
-    xd = kvc.decode(blob, x.shape, "bf16", 4, 2, 64, seed=p.seed)
+    dwhole, draw = gpu_util.guarded(x.numel() * 2, DEV)
+    xd = draw.view(x.dtype).view(x.shape)
+    kvc.decode(blob, x.shape, "bf16", 4, 2, 64, seed=p.seed, out=xd)
     torch.cuda.synchronize()
+    assert gpu_util.canaries_intact(dwhole), "decode wrote outside its output"
     if x.numel() == 0:
         assert blob.numel() == 0 or not blob.cpu().numpy().any()
         return
