@@ -152,10 +152,20 @@ def test_probe_copy():
     assert torch.equal(a, b)
 
 
+# full-size workloads: the presets, and the 8B-4k byte count at head_dim 64 in fp16
+FULL = {
+    "llama3_8b_4k": ("llama3_8b_4k", {}),
+    "llama3_8b_32k": ("llama3_8b_32k", {}),
+    "llama3_70b_16k": ("llama3_70b_16k", {}),
+    "llama3_8b_4k_d64_fp16": ("llama3_8b_4k", dict(head_dim=64, tokens=8192, group=64, dtype="fp16")),
+}
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["llama3_8b_4k", "llama3_8b_32k", "llama3_70b_16k"])
+@pytest.mark.parametrize("name", list(FULL))
 def test_full_size_sampled(name):
-    p = presets.preset(name)
+    base, over = FULL[name]
+    p = presets.preset(base).with_(name=name, **over)
     rng = np.random.default_rng(7)
     _say("full size", name, "generate")
     x = inputs.make_kv(p, device=DEV)
