@@ -840,9 +840,10 @@ __device__ __forceinline__ void load_codes(const Tile& t, CodeRegs<D, B, G>& r) 
  * rows, so the stores of rows past the count are dropped by the hardware
  * instead of being skipped by a branch around each store (those branches,
  * with their exec-mask saves and restores, cost 3% at 16k-32k tokens).
- * Each tile starts once the previous tile's stores have completed: letting
- * them overlap the next tile measured no faster at 16k-32k tokens and up to
- * 2% slower at 4k.
+ * Whether a tile starts once the previous tile's stores have completed, or
+ * with them still in flight, is the launch's choice (LaunchArgs::overlap): a
+ * wave that shares its SIMD with another one does better waiting, a wave
+ * alone on its SIMD better overlapping.
  */
 template <int D, int DT, int B, int G, bool PAGED>
 KVC_KERNEL void decode_kernel(const LaunchArgs a) {
@@ -863,8 +864,11 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   if (!next_tile<D, false, PAGED>(a, c, tensor, blob, cur, true)) return;
   CodeRegs<D, B, G> cr;
   load_codes<D, B, G, PAGED>(cur, cr);
+  // nothing outstanding on entry, so inside the loop the compiler's own wait
+  // for the codes counts the loop's loads and stores only
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   for (;;) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this tile's codes, the last tile's stores
+    if (PAGED || !a.overlap) __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the last tile's stores too
     float y[D];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {

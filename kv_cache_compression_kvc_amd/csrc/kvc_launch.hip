@@ -1,7 +1,7 @@
 /*
  * kvc_launch.hip -- GPU entry points of the C ABI (include/kvc.h): pick the
  * kernel instance for a validated plan and launch it on the caller's stream
- * with a persistent grid (compute units x resident workgroups per unit).
+ * with a persistent grid (one or all resident waves per SIMD, per kernel).
  */
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -44,7 +44,8 @@ Kernel pick(Op op, int d, int dt, int b, int g, bool paged) {
   return nullptr;
 }
 
-/* Resident workgroups per device for a kernel: CUs x occupancy, cached. */
+/* Resident workgroups per device for a kernel (CUs x occupancy) and the
+ * device's CU count, cached. */
 struct GridCache {
   std::mutex mu;
   static constexpr int kMax = 512;
@@ -52,10 +53,11 @@ struct GridCache {
   int dev[kMax];
   const void* fn[kMax];
   int64_t grid[kMax];
+  int cus[kMax];
 };
 GridCache g_grid;
 
-int resident_groups(Kernel k, int threads, int64_t* out) {
+int resident_groups(Kernel k, int threads, int64_t* out, int* cus_out = nullptr) {
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return KVC_EHIP;
   {
@@ -63,6 +65,7 @@ int resident_groups(Kernel k, int threads, int64_t* out) {
     for (int i = 0; i < g_grid.n; ++i)
       if (g_grid.dev[i] == device && g_grid.fn[i] == reinterpret_cast<const void*>(k)) {
         *out = g_grid.grid[i];
+        if (cus_out) *cus_out = g_grid.cus[i];
         return KVC_OK;
       }
   }
@@ -77,10 +80,52 @@ int resident_groups(Kernel k, int threads, int64_t* out) {
     g_grid.dev[g_grid.n] = device;
     g_grid.fn[g_grid.n] = reinterpret_cast<const void*>(k);
     g_grid.grid[g_grid.n] = g;
+    g_grid.cus[g_grid.n] = cus;
     ++g_grid.n;
   }
   *out = g;
+  if (cus_out) *cus_out = cus;
   return KVC_OK;
+}
+
+constexpr int kSimdsPerCu = 4;
+
+/* Blob size above which the contiguous decode runs one wave per SIMD with
+ * overlapped stores: 3/4 of the 256 MB memory-side cache. */
+constexpr uint64_t kDecodeLargeBlob = uint64_t(192) << 20;
+
+/*
+ * How a launch fills the chip: waves per SIMD (0: every resident wave) and,
+ * for the decode, whether a tile starts with the last tile's stores still in
+ * flight.  Every tile is streamed once, so extra waves only add independent
+ * access streams once enough bytes are in flight.  Measured on 8B-shaped
+ * caches, each kernel alone and alternating with the other:
+ *   - encode: one wave per SIMD is as fast or faster (1-2% at 4k tokens,
+ *     5-6% at 32k, about 4% at head_dim 64, 3% on the paged pool), except on
+ *     a paged pool at head_dim 64, 5% slower there: 8 KiB tiles, each behind
+ *     a dependent table load, keep too few bytes in flight;
+ *   - contiguous decode of a blob larger than kDecodeLargeBlob (the blob an
+ *     encode just wrote then no longer sits in the memory-side cache): one
+ *     wave per SIMD with overlapped stores, 3-10% faster from 6k tokens up
+ *     at head_dim 128 and 5-6% at 64, than two waves per SIMD that wait;
+ *   - a smaller blob: two waves per SIMD that wait, 2-3% faster than the
+ *     above at 4k tokens, and 5-10% faster than four at head_dim 64;
+ *   - paged decode: two waves per SIMD that wait (one wave lost 13%; its
+ *     tiles carry dependent table loads).
+ * One wave that waits for its stores, or two that overlap them, measured
+ * slower than the pairings above.  Grids between one and two waves per SIMD
+ * leave some SIMDs with a wave more than others; with a static tile split
+ * those finish last, and such grids measured slower than either.
+ */
+struct LaunchShape {
+  int waves_per_simd;
+  int overlap;
+};
+
+LaunchShape launch_shape(Op op, const LaunchArgs& a, int head_dim) {
+  if (op == Op::Encode) return (a.paged && head_dim == 64) ? LaunchShape{0, 0} : LaunchShape{1, 0};
+  if (op == Op::Decode) return (!a.paged && a.blob_total > kDecodeLargeBlob) ? LaunchShape{1, 1} : LaunchShape{2, 0};
+  return {0, 0};
 }
 
 int run_plan(Op op, const Plan& plan, void* stream) {
@@ -88,12 +133,18 @@ int run_plan(Op op, const Plan& plan, void* stream) {
     Kernel k = pick(op, plan.head_dim, plan.dtype, plan.bits[i], plan.group, plan.args[i].paged != 0);
     if (!k) return KVC_ESHAPE;
     int64_t resident = 0;
-    int st = resident_groups(k, 64, &resident);
+    int cus = 0;
+    int st = resident_groups(k, 64, &resident, &cus);
     if (st != KVC_OK) return st;
-    const int64_t grid = std::min<int64_t>(plan.args[i].total_items, resident);
+    LaunchArgs args = plan.args[i];
+    const LaunchShape shape = launch_shape(op, args, plan.head_dim);
+    args.overlap = shape.overlap;
+    const int64_t waves =
+        shape.waves_per_simd > 0 ? std::min<int64_t>(resident, int64_t(cus) * kSimdsPerCu * shape.waves_per_simd)
+                                 : resident;
+    const int64_t grid = std::min<int64_t>(args.total_items, waves);
     if (grid <= 0) continue;
-    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64), 0,
-                       static_cast<hipStream_t>(stream), plan.args[i]);
+    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64), 0, static_cast<hipStream_t>(stream), args);
     if (hipGetLastError() != hipSuccess) return KVC_EHIP;
   }
   return KVC_OK;

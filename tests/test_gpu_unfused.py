@@ -105,3 +105,27 @@ def test_unfused_full_size_equals_fused(name):
     assert torch.equal(dec_f.view(torch.int16), dec_u.view(torch.int16))
     del x, out_f, out_u, dec_f, dec_u
     torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+def test_large_ragged_blob_fused_equals_unfused():
+    """A blob above 192 MiB (the decode then keeps a tile's stores in flight
+    while it starts the next one) with slabs of 500015 rows, so every slab
+    ends in a 47-row tile: fused and separate-kernel results bit-identical,
+    nothing written outside the decode output."""
+    p = _small(128, "bf16", 8, 8, 64, L=2, T=100003, H=5)
+    _say("large ragged: generate")
+    x = inputs.make_kv(p, device=DEV)
+    total, _ = kvc.encoded_size(p.layers, p.tokens, p.kv_heads, 128, 8, 8, 64, "bf16")
+    assert total > 192 << 20
+    out_f, out_u, dec_f, dec_u = _both(p, x)
+    assert torch.equal(out_f, out_u)
+    assert torch.equal(dec_f.view(torch.int16), dec_u.view(torch.int16))
+    dwhole, draw = gpu_util.guarded(x.numel() * 2, DEV)
+    xd = draw.view(x.dtype).view(x.shape)
+    kvc.decode(out_f, x.shape, "bf16", 8, 8, 64, seed=p.seed, out=xd)
+    torch.cuda.synchronize()
+    assert gpu_util.canaries_intact(dwhole)
+    assert torch.equal(xd.view(torch.int16), dec_f.view(torch.int16))
+    del x, out_f, out_u, dec_f, dec_u, dwhole, draw, xd
+    torch.cuda.empty_cache()
