@@ -24,7 +24,12 @@
  *      scale == 0), packed LSB-first: code j at bits [b*j, b*j + b) of the
  *      vector's D*b/8 bytes.
  * Decode: yhat = zero + q * scale, x = s * (H yhat) / sqrt(D), rounded to
- * nearest even in the tensor's dtype.
+ * nearest even in the tensor's dtype.  Computed as H = H_{D/G} (x) H_G: the
+ * integer codes are transformed within each group exactly, then scaled (the
+ * zero term reaches each group's first element only, as zero * G), then
+ * combined across groups in binary32; the result does not depend on the
+ * launch (kvc_decode, kvc_decode_paged and the chunked receive agree to the
+ * bit on every vector).
  *
  * Blob layout (for T tokens):
  *   codes: for l in [0, L), for kv in (K, V): a slab of T*H rows, (t, h)
@@ -193,10 +198,12 @@ kvc_status kvc_debug_rotate(const kvc_desc* desc, const void* kv, float* y_out,
 
 /*
  * Comparator for the fused kernels: the same encode / decode as kvc_encode
- * and kvc_decode (bit-identical blob and output), computed by separate
- * kernels -- rotate, group min/max, quantize, pack (decode: unpack,
- * dequantize, inverse rotate) -- that pass fp32 and byte intermediates
- * through `workspace`.  The arxivlens summary of "Beyond Compression Ratio:
+ * and kvc_decode, computed by separate kernels -- rotate, group min/max,
+ * quantize, pack (decode: unpack, dequantize, inverse rotate) -- that pass
+ * fp32 and byte intermediates through `workspace`.  The blob is bit-identical
+ * to kvc_encode's; the decoded tensor differs from kvc_decode's in rounding
+ * only (this one dequantizes before the whole inverse transform, kvc_decode
+ * transforms the integer codes within their groups first).  The arxivlens summary of "Beyond Compression Ratio:
  * High-Throughput KV Compression for Disaggregated LLM Serving" (key
  * results) compares its fused kernel with such separate kernels; its
  * abstract names the intermediate tensor and the repeated memory accesses

@@ -24,9 +24,10 @@
  *     cores (exact bf16 / fp16 products against +-1, fp32 sums), after
  *     which every lane again holds its own vector; the group min/max, the
  *     fp16 meta, the quantization and the packing run inside the lane;
- *   - decode: dequantization, the fp32 butterfly and the rounding to the
- *     storage type run inside the lane; the rows leave through LDS as
- *     coalesced stores;
+ *   - decode: the codes are transformed within their groups (exactly, on
+ *     the matrix cores or as a butterfly), scaled, combined across groups
+ *     and rounded to the storage type inside the lane; the rows leave
+ *     through LDS as coalesced stores;
  *   - no intermediate touches memory, and as soon as a tile's rows (or
  *     codes) are in registers the wave's next tile is requested, so HBM
  *     traffic overlaps the arithmetic.
@@ -120,23 +121,6 @@ __device__ __forceinline__ uint32_t ru16(float v) {
 }
 
 /* ---- transform ------------------------------------------------------------ */
-
-/* In-place unnormalized Walsh-Hadamard butterfly (Sylvester order). */
-template <int D>
-__device__ __forceinline__ void fwht(float (&y)[D]) {
-#pragma unroll
-  for (int h = 1; h < D; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < D; i += 2 * h) {
-#pragma unroll
-      for (int j = i; j < i + h; ++j) {
-        float a = y[j], b = y[j + h];
-        y[j] = a + b;
-        y[j + h] = a - b;
-      }
-    }
-  }
-}
 
 /* ---- quantization and packing ------------------------------------------ */
 
@@ -556,6 +540,13 @@ __device__ __forceinline__ void read_row_signed(const v4u* lds, const uint32_t* 
  * The compiler shares the partial sums that several output blocks have in
  * common (the first K-blocks of a and a+1 carry the same signs), so the
  * 2 * (D/32) * (D/16) products of a D = 128 tile issue as 44 instructions.
+ *
+ * With G < D the same code computes (I_{D/G} (x) H_G) x, the transform
+ * within each group of G elements: H_D = H_{D/G} (x) H_G in Sylvester
+ * order, and the block-diagonal part keeps only the blocks whose rows and
+ * columns lie in one group (32a / G == 16b / G), with the third sign term
+ * restricted to the in-group bits of a and b >> 1.  At G = 32 that is 16
+ * products per D = 128 tile.
  */
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -596,9 +587,10 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(v4u a, v4u b, f32x16_t c) {
                                                   0, 0, 0);
 }
 
-/* Signed packed row chunks of every lane -> u = H (s * x) of the lane's own
- * vector, D fp32 values in element order.  `xc` is consumed. */
-template <int D, int DT>
+/* Packed row chunks of every lane -> u = (I_{D/G} (x) H_G) x of the lane's
+ * own vector (u = H x at G = D), D fp32 values in element order.  `xc` is
+ * consumed. */
+template <int D, int DT, int G = D>
 __device__ __forceinline__ void hadamard_mfma(v4u (&xc)[D / 8], const HadamardA& A, float (&u)[D]) {
   constexpr int KB = D / 16, OB = D / 32;
 #pragma unroll
@@ -617,7 +609,8 @@ __device__ __forceinline__ void hadamard_mfma(v4u (&xc)[D / 8], const HadamardA&
     acc[a][1] = f32x16_t{};
 #pragma unroll
     for (int b = 0; b < KB; ++b) {
-      const int sel = ((__builtin_popcount(a & (b >> 1)) & 1) << 1) | (b & 1);
+      if ((32 * a) / G != (16 * b) / G) continue;  // block outside every group
+      const int sel = ((__builtin_popcount(a & (b >> 1) & (G / 32 - 1)) & 1) << 1) | (b & 1);
       acc[a][0] = mfma_32x32x16<DT>(A.w[sel], xc[2 * b], acc[a][0]);
       acc[a][1] = mfma_32x32x16<DT>(A.w[sel], xc[2 * b + 1], acc[a][1]);
     }
@@ -826,30 +819,105 @@ __device__ __forceinline__ void load_codes(const Tile& t, CodeRegs<D, B, G>& r) 
   }
 }
 
+/* Chunk p (elements 8p .. 8p+7) of a lane's codes as fp16 pairs 1024 + q,
+ * element 2m in the low half: exact for every code (q < 1024, and fp16 has
+ * unit spacing on [1024, 2048)), at one byte permute and one or per pair.
+ * `w` holds the lane's D * B / 32 code words. */
+template <int B, int NW>
+__device__ __forceinline__ v4u code_chunk_f16(const uint32_t (&w)[NW], int p) {
+  constexpr uint32_t kBias = 0x64006400u;  // fp16 1024.0 in both halves
+  v4u r;
+  if constexpr (B == 8) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t x = w[2 * p + h];
+      r[2 * h] = __builtin_amdgcn_perm(x, x, 0x0C010C00u) | kBias;
+      r[2 * h + 1] = __builtin_amdgcn_perm(x, x, 0x0C030C02u) | kBias;
+    }
+  } else if constexpr (B == 4) {
+    // codes 2m and 2m+1 are the low and high nibble of byte m
+    const uint32_t x = w[p];
+    const uint32_t e = x & 0x0F0F0F0Fu, o = (x >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) r[m] = __builtin_amdgcn_perm(o, e, 0x0C000C00u | m | ((4 + m) << 16)) | kBias;
+  } else {
+    // the chunk is half a word; codes 2k and 2k+1 are the two halves of nibble k
+    const uint32_t x = w[p / 2];
+    const int h = p & 1;
+    const uint32_t e = x & 0x33333333u, o = (x >> 2) & 0x33333333u;
+    const uint32_t ee = e & 0x0F0F0F0Fu, eo = (e >> 4) & 0x0F0F0F0Fu;  // even / odd nibbles to bytes
+    const uint32_t oe = o & 0x0F0F0F0Fu, oo = (o >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t sel = 0x0C000C00u | uint32_t(2 * h + m / 2) | (uint32_t(4 + 2 * h + m / 2) << 16);
+      r[m] = ((m & 1) ? __builtin_amdgcn_perm(oo, eo, sel) : __builtin_amdgcn_perm(oe, ee, sel)) | kBias;
+    }
+  }
+  return r;
+}
+
+/* Butterfly stages h = H0, 2 H0, ... < H1 of the in-place Sylvester
+ * transform: stages below G stay inside groups of G elements, the others
+ * combine groups. */
+template <int D, int H0, int H1>
+__device__ __forceinline__ void butterfly_stages(float (&y)[D]) {
+#pragma unroll
+  for (int h = H0; h < H1; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < D; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float p0 = y[j], p1 = y[j + h];
+        y[j] = p0 + p1;
+        y[j + h] = p0 - p1;
+      }
+    }
+  }
+}
+
 /*
- * Decode: per tile, each lane dequantizes its own vector from the prefetched
- * codes, runs the butterfly, packs to the storage type with the sign flip and
- * writes its row to LDS one 128-byte line (8 chunks) at a time; the wave then
- * stores those lines with coalesced 16-byte stores, every store instruction
- * covering 8 whole lines (a pass that wrote half lines, as half rows of a
- * D = 64 tile are, left each line to be finished by a later instruction and
- * ran 1.4x slower).  The next tile's codes are loaded into registers while
- * the current one is computed.
+ * Decode.  With q the codes of a vector, group g holding elements
+ * [gG, gG + G), and H_D = H_{D/G} (x) H_G in Sylvester order:
+ *   H_D yhat = (H_{D/G} (x) I_G) (I_{D/G} (x) H_G) yhat,
+ *   H_G (zero_g 1 + scale_g q_g) = scale_g (H_G q_g) + zero_g G e_0.
+ * So each lane first transforms its integer codes within each group, which
+ * is exact (integers below 2^24 in fp32), then scales every element and adds
+ * the zero term at each group's first element (one rounding each), runs the
+ * log2(D/G) butterfly stages across groups in fp32, and packs to the storage
+ * type with the sign flip: x = s * (H_D yhat) / sqrt(D), 1/sqrt(D) folded
+ * into scale and zero.
+ *
+ * The in-group transform runs either on the matrix cores (the codes enter as
+ * fp16 1024 + q; the bias adds exactly 1024 G to each group's first element,
+ * which is subtracted exactly) or as the in-register butterfly on the codes
+ * as fp32.  Both give the same integers, so the two kinds of decode agree to
+ * the bit; which one runs is part of the launch shape (LARGE, below).
+ *
+ * Each lane's row goes to LDS one 128-byte line (8 chunks) at a time; the
+ * wave then stores those lines with coalesced 16-byte stores, every store
+ * instruction covering 8 whole lines (a pass that wrote half lines, as half
+ * rows of a D = 64 tile are, left each line to be finished by a later
+ * instruction and ran 1.4x slower).  The next tile's codes are loaded into
+ * registers while the current one is computed.
  *
  * The stores go through a buffer resource that spans the tile's `count`
  * rows, so the stores of rows past the count are dropped by the hardware
  * instead of being skipped by a branch around each store (those branches,
  * with their exec-mask saves and restores, cost 3% at 16k-32k tokens).
- * Whether a tile starts once the previous tile's stores have completed, or
- * with them still in flight, is the launch's choice (LaunchArgs::overlap): a
- * wave that shares its SIMD with another one does better waiting, a wave
- * alone on its SIMD better overlapping.
+ *
+ * LARGE (one wave per SIMD, for a blob larger than the memory-side cache):
+ * the butterfly, and a tile starts with the last tile's stores still in
+ * flight.  Otherwise (two waves per SIMD): the matrix cores, and a tile
+ * starts once the last tile's stores have completed.  Measured, the matrix
+ * cores make the two-wave decode 6-9% faster at 4k tokens and the paged one
+ * 2-5% faster, but a lone wave per SIMD cannot hide their latency: at 32k
+ * tokens they made it 13% slower.
  */
-template <int D, int DT, int B, int G, bool PAGED>
+template <int D, int DT, int B, int G, bool PAGED, bool LARGE>
 KVC_KERNEL void decode_kernel(const LaunchArgs a) {
-  constexpr int CH = D / 8, NG = D / G;
+  static_assert(!(PAGED && LARGE), "paged decodes use the two-wave shape");
+  constexpr int CH = D / 8, NG = D / G, NW = D * B / 32, VPW = 32 / B;
   constexpr float RS = Norm<D>::inv_sqrt;
-  constexpr int WPG = G * B / 32, VPW = 32 / B;
   constexpr int HALF = 8;                         // chunks per row staged at a time: one line
   constexpr int NPASS = CH / HALF;
   __shared__ v4u lds_out[kTileVectors * HALF];    // one line of every row of the tile
@@ -858,6 +926,8 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   uint8_t* blob = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.src));
   const int lane = threadIdx.x;
   load_signs(a, signs);
+  HadamardA had;
+  if constexpr (!LARGE) hadamard_operands<KVC_FP16>(had);
   Cursor c;
   cursor_init<PAGED>(a, c);
   Tile cur;
@@ -868,28 +938,44 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   // for the codes counts the loop's loads and stores only
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   for (;;) {
-    if (PAGED || !a.overlap) __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the last tile's stores too
-    float y[D];
+    if constexpr (!LARGE) __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the last tile's stores too
+    float sc[NG], ze[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      // dequantize with 1/sqrt(D) folded into scale and zero
-      const float sc = f16_value(cr.meta[g] & 0xffffu) * RS;
-      const float ze = f16_value(cr.meta[g] >> 16) * RS;
+      sc[g] = f16_value(cr.meta[g] & 0xffffu) * RS;
+      ze[g] = f16_value(cr.meta[g] >> 16) * RS;
+    }
+    float y[D];
+    v4u xq[LARGE ? 1 : CH];
+    if constexpr (LARGE) {
 #pragma unroll
-      for (int w = 0; w < WPG; ++w) {
-        const int wi = g * WPG + w;
-        float q[VPW];
-        unpack_word<B>(cr.codes[wi / 4][wi % 4], q);
+      for (int wi = 0; wi < NW; ++wi) unpack_word<B>(cr.codes[wi / 4][wi % 4], y + wi * VPW);
+    } else {
+      uint32_t wds[NW];
 #pragma unroll
-        for (int k = 0; k < VPW; ++k) y[g * G + w * VPW + k] = fmaf(q[k], sc, ze);
-      }
+      for (int wi = 0; wi < NW; ++wi) wds[wi] = cr.codes[wi / 4][wi % 4];
+#pragma unroll
+      for (int p = 0; p < CH; ++p) xq[p] = code_chunk_f16<B, NW>(wds, p);
     }
     KVC_PHASE();
     Tile nxt;
     const bool more = next_tile<D, false, PAGED>(a, c, tensor, blob, nxt, false);
     if (more) load_codes<D, B, G, PAGED>(nxt, cr);
     KVC_PHASE();
-    fwht<D>(y);
+    if constexpr (LARGE) {
+      butterfly_stages<D, 1, G>(y);
+    } else {
+      hadamard_mfma<D, KVC_FP16, G>(xq, had, y);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) y[g * G] -= 1024.0f * G;
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      y[g * G] = fmaf(y[g * G], sc[g], ze[g] * G);
+#pragma unroll
+      for (int j = 1; j < G; ++j) y[g * G + j] *= sc[g];
+    }
+    butterfly_stages<D, G, D>(y);
     KVC_PHASE();
     const v4u* sg = reinterpret_cast<const v4u*>(signs);
     const __amdgpu_buffer_rsrc_t out = tile_rsrc(cur.src, cur.count * CH * 16);

@@ -48,7 +48,7 @@ struct LaunchArgs {
   int32_t num_reqs;
   int32_t max_blocks;
   int32_t subtiles;       // ceil(block_size * H / 64)
-  int32_t overlap;        // decode: 1 = a tile starts with the last tile's stores in flight
+  int32_t pad0;
   const int32_t* table;
   const int32_t* lens;
   const int64_t* offsets;

@@ -19,11 +19,14 @@
  *   D2 dequant   q, meta          -> z  fp32 [rows, D]  (1/sqrt(D) folded in)
  *   D3 unrotate  z                -> x  butterfly, sign flip, round to dtype
  *
- * Each stage makes the same binary32 decisions as the fused kernels (E1 is
- * the fused encode's transform code; the inverse butterfly runs in the same
- * stage and operand order; the meta and code arithmetic are the same
- * functions), so the blob and the decoded tensor are bit-identical to
- * theirs; only the memory traffic differs.  The stages are written to run near the HBM
+ * The encode stages make the same binary32 decisions as the fused encode
+ * (E1 is its transform code; the meta and code arithmetic are the same
+ * functions), so the blob is bit-identical to the fused one; only the memory
+ * traffic differs.  The decode stages take the textbook order -- dequantize,
+ * then the whole inverse transform -- where the fused decode transforms the
+ * integer codes within their groups first and scales afterwards, so the two
+ * decoded tensors differ in rounding only (both well inside the decode
+ * criterion against the oracle).  The stages are written to run near the HBM
  * bound on their own: 256-thread blocks, vector loads and stores that are
  * contiguous across the wave, butterfly stages across lanes by shuffles.
  */

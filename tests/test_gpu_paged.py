@@ -89,6 +89,18 @@ def test_paged_matches_oracle(D, dtype, bk, bv, G, H, lens):
             used[table[r][t // p.block_size], t % p.block_size] = True
     assert np.array_equal(got[:, :, ~used], ref[:, :, ~used])
     parity.check_decode(got[:, :, used], ref[:, :, used], dtype)
+    # every request's tokens decode to the same bits as the same tokens
+    # encoded and decoded as a contiguous tensor
+    pool_t = torch.from_numpy(pool_b.view(np.int16))
+    got_t = torch.from_numpy(got.view(np.int16))
+    for r, n in enumerate(lens):
+        if n == 0:
+            continue
+        blocks = [int(table[r][t // p.block_size]) for t in range(int(n))]
+        offs_in = [t % p.block_size for t in range(int(n))]
+        xr = pool_t[:, :, blocks, offs_in].to(DEV).view(pool.dtype).contiguous()  # [L, 2, n, H, D]
+        dr = kvc.decode(kvc.encode(xr, bk, bv, G, seed=p.seed), xr.shape, dtype, bk, bv, G, seed=p.seed)
+        assert torch.equal(dr.view(torch.int16).cpu(), got_t[:, :, blocks, offs_in]), "request %d" % r
 
 
 def test_paged_bad_table_entry_is_flagged_not_faulted():

@@ -1,6 +1,9 @@
 """GPU parity of the separate-kernel comparator (kvc_encode_unfused /
-kvc_decode_unfused): its blob and decode are bit-identical to the fused
-path's, and its blob meets the oracle criteria on its own."""
+kvc_decode_unfused): its blob is bit-identical to the fused path's, its
+decode agrees with the fused decode within the decode criterion (the two
+round in different places: the comparator dequantizes and then runs the
+whole inverse transform, the fused decode transforms the integer codes
+within their groups first), and both meet the oracle criteria on their own."""
 import ctypes
 import sys
 
@@ -36,6 +39,18 @@ GRID = [(D, dt, bk, bv, G)
         for G in (32, 64, 128) if G <= D]
 
 
+def _decodes_agree(dec_a, dec_b):
+    """Relative RMS per (layer, K/V) slice within the decode criterion, on the GPU."""
+    if dec_a.numel() == 0:
+        return
+    a = dec_a.double().flatten(2)
+    b = dec_b.double().flatten(2)
+    num = (a - b).norm(dim=2)
+    den = b.norm(dim=2)
+    rel = torch.where(den > 0, num / den.clamp_min(1e-300), num)
+    assert float(rel.max()) <= parity.DECODE_RRMS, "fused and separate-kernel decodes differ by %.3g" % float(rel.max())
+
+
 def _both(p, x):
     """(fused blob, unfused blob, fused decode, unfused decode) of x on the GPU."""
     D = p.head_dim
@@ -61,7 +76,7 @@ def test_unfused_equals_fused_and_oracle(D, dtype, bk, bv, G):
     _say("unfused", p.name)
     out_f, out_u, dec_f, dec_u = _both(p, x.to(DEV))
     assert torch.equal(out_f, out_u), "unfused blob differs from the fused blob"
-    assert torch.equal(dec_f.view(torch.int16), dec_u.view(torch.int16)), "unfused decode differs"
+    _decodes_agree(dec_u, dec_f)
     xb = inputs.as_u16(x)
     parity.check_blob(xb, out_u.cpu().numpy(), dtype, bk, bv, G, p.seed)
     oblob, _ = oracle.encode(xb, dtype, bk, bv, G, p.seed)
@@ -76,7 +91,7 @@ def test_unfused_edge_shapes(L, T, H):
     _say("unfused edge", L, T, H)
     out_f, out_u, dec_f, dec_u = _both(p, x)
     assert torch.equal(out_f, out_u)
-    assert torch.equal(dec_f.view(torch.int16), dec_u.view(torch.int16))
+    _decodes_agree(dec_u, dec_f)
 
 
 def test_unfused_workspace_validation():
@@ -102,17 +117,19 @@ def test_unfused_full_size_equals_fused(name):
     x = inputs.make_kv(p, device=DEV)
     out_f, out_u, dec_f, dec_u = _both(p, x)
     assert torch.equal(out_f, out_u)
-    assert torch.equal(dec_f.view(torch.int16), dec_u.view(torch.int16))
+    _decodes_agree(dec_u, dec_f)
     del x, out_f, out_u, dec_f, dec_u
     torch.cuda.empty_cache()
 
 
 @pytest.mark.slow
-def test_large_ragged_blob_fused_equals_unfused():
-    """A blob above 192 MiB (the decode then keeps a tile's stores in flight
-    while it starts the next one) with slabs of 500015 rows, so every slab
-    ends in a 47-row tile: fused and separate-kernel results bit-identical,
-    nothing written outside the decode output."""
+def test_large_ragged_blob_both_decodes():
+    """A 272 MB blob (above 192 MiB: decoded by the butterfly variant, one
+    wave per SIMD, stores overlapped) with slabs of 500015 rows, so every slab
+    ends in a 47-row tile.  Each layer encoded on its own gives a 136 MB blob,
+    decoded by the matrix-core variant; the two decodes must agree to the
+    bit, the encodes must match the separate-kernel comparator's blob, and
+    nothing may be written outside the decode output."""
     p = _small(128, "bf16", 8, 8, 64, L=2, T=100003, H=5)
     _say("large ragged: generate")
     x = inputs.make_kv(p, device=DEV)
@@ -120,12 +137,21 @@ def test_large_ragged_blob_fused_equals_unfused():
     assert total > 192 << 20
     out_f, out_u, dec_f, dec_u = _both(p, x)
     assert torch.equal(out_f, out_u)
-    assert torch.equal(dec_f.view(torch.int16), dec_u.view(torch.int16))
+    _decodes_agree(dec_u, dec_f)
     dwhole, draw = gpu_util.guarded(x.numel() * 2, DEV)
     xd = draw.view(x.dtype).view(x.shape)
     kvc.decode(out_f, x.shape, "bf16", 8, 8, 64, seed=p.seed, out=xd)
     torch.cuda.synchronize()
     assert gpu_util.canaries_intact(dwhole)
     assert torch.equal(xd.view(torch.int16), dec_f.view(torch.int16))
+    for l in range(p.layers):
+        xl = x[l:l + 1].contiguous()
+        tl, _ = kvc.encoded_size(1, p.tokens, p.kv_heads, 128, 8, 8, 64, "bf16")
+        assert tl < 192 << 20
+        bl = kvc.encode(xl, 8, 8, 64, seed=p.seed)
+        dl = kvc.decode(bl, xl.shape, "bf16", 8, 8, 64, seed=p.seed)
+        torch.cuda.synchronize()
+        _say("  layer %d: per-layer decode vs whole decode" % l)
+        assert torch.equal(dl.view(torch.int16), dec_f[l:l + 1].view(torch.int16))
     del x, out_f, out_u, dec_f, dec_u, dwhole, draw, xd
     torch.cuda.empty_cache()
