@@ -43,8 +43,9 @@
 namespace kvc {
 namespace dev {
 
-/* Register budget: at least this many waves per SIMD (512 / N registers per
- * lane), so that other waves can issue while one waits on LDS or memory. */
+/* Register budget: room for at least this many waves per SIMD (512 / N
+ * registers per lane).  The launches use one or two waves per SIMD, chosen
+ * per kernel and size (kvc_launch.hip); two must always fit. */
 #ifndef KVC_WAVES_PER_EU
 #define KVC_WAVES_PER_EU 2
 #endif
