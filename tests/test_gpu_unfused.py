@@ -122,34 +122,40 @@ def test_unfused_full_size_equals_fused(name):
     torch.cuda.empty_cache()
 
 
+# (head_dim, dtype, bits, group, tokens, heads): blobs above 192 MiB whose
+# slabs end in a partial tile (rows per slab 500015 = 47 mod 64, 1000015 = 15)
+LARGE_RAGGED = [(128, "bf16", 8, 64, 100003, 5), (64, "fp16", 8, 32, 200003, 5)]
+
+
 @pytest.mark.slow
-def test_large_ragged_blob_both_decodes():
-    """A 272 MB blob (above 192 MiB: decoded by the butterfly variant, one
-    wave per SIMD, stores overlapped) with slabs of 500015 rows, so every slab
-    ends in a 47-row tile.  Each layer encoded on its own gives a 136 MB blob,
-    decoded by the matrix-core variant; the two decodes must agree to the
-    bit, the encodes must match the separate-kernel comparator's blob, and
-    nothing may be written outside the decode output."""
-    p = _small(128, "bf16", 8, 8, 64, L=2, T=100003, H=5)
-    _say("large ragged: generate")
+@pytest.mark.parametrize("D,dtype,b,G,T,H", LARGE_RAGGED)
+def test_large_ragged_blob_both_decodes(D, dtype, b, G, T, H):
+    """A blob above 192 MiB (decoded by the butterfly variant, one wave per
+    SIMD, stores overlapped) whose slabs end in a partial tile.  Each layer
+    encoded on its own gives a blob below 192 MiB, decoded by the matrix-core
+    variant; the two decodes must agree to the bit, the encode must match the
+    separate-kernel comparator's blob, and nothing may be written outside the
+    decode output."""
+    p = _small(D, dtype, b, b, G, L=2, T=T, H=H)
+    _say("large ragged: generate", D, dtype)
     x = inputs.make_kv(p, device=DEV)
-    total, _ = kvc.encoded_size(p.layers, p.tokens, p.kv_heads, 128, 8, 8, 64, "bf16")
+    total, _ = kvc.encoded_size(p.layers, p.tokens, p.kv_heads, D, b, b, G, dtype)
     assert total > 192 << 20
     out_f, out_u, dec_f, dec_u = _both(p, x)
     assert torch.equal(out_f, out_u)
     _decodes_agree(dec_u, dec_f)
     dwhole, draw = gpu_util.guarded(x.numel() * 2, DEV)
     xd = draw.view(x.dtype).view(x.shape)
-    kvc.decode(out_f, x.shape, "bf16", 8, 8, 64, seed=p.seed, out=xd)
+    kvc.decode(out_f, x.shape, dtype, b, b, G, seed=p.seed, out=xd)
     torch.cuda.synchronize()
     assert gpu_util.canaries_intact(dwhole)
     assert torch.equal(xd.view(torch.int16), dec_f.view(torch.int16))
     for l in range(p.layers):
         xl = x[l:l + 1].contiguous()
-        tl, _ = kvc.encoded_size(1, p.tokens, p.kv_heads, 128, 8, 8, 64, "bf16")
+        tl, _ = kvc.encoded_size(1, p.tokens, p.kv_heads, D, b, b, G, dtype)
         assert tl < 192 << 20
-        bl = kvc.encode(xl, 8, 8, 64, seed=p.seed)
-        dl = kvc.decode(bl, xl.shape, "bf16", 8, 8, 64, seed=p.seed)
+        bl = kvc.encode(xl, b, b, G, seed=p.seed)
+        dl = kvc.decode(bl, xl.shape, dtype, b, b, G, seed=p.seed)
         torch.cuda.synchronize()
         _say("  layer %d: per-layer decode vs whole decode" % l)
         assert torch.equal(dl.view(torch.int16), dec_f[l:l + 1].view(torch.int16))
