@@ -226,3 +226,39 @@ def test_subnormal_and_tiny_inputs(dtype):
     parity.check_rotation(y, yref)
     blob = kvc.encode(x.to(DEV), 4, 4, 128, seed=1)
     parity.check_blob(xb, blob.cpu().numpy(), dtype, 4, 4, 128, 1)
+
+
+def _tokens_for(D, bk, bv, G, H, target):
+    """Tokens giving a one-layer blob of about `target` bytes, 3 past a multiple of 64."""
+    per_token = H * (D * bk // 8 + D * bv // 8 + 8 * D // G)
+    return (target // per_token) // 64 * 64 + 3
+
+
+# every (head_dim, bits_k, bits_v, group), plus K and V at different widths
+LARGE_GRID = [(D, b, b, G) for D in (64, 128) for b in (2, 4, 8) for G in (32, 64, 128) if G <= D]
+LARGE_GRID.append((128, 2, 4, 64))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("D,bk,bv,G", LARGE_GRID)
+def test_large_blob_decode_matches_per_layer(D, bk, bv, G):
+    """Two layers whose blob is above 192 MiB decode with the butterfly variant
+    (one wave per SIMD); each layer alone (about 120 MiB) decodes on the
+    matrix cores.  Both must give the same bits; the slabs end in a partial
+    tile (8 heads, tokens 3 past a multiple of 64)."""
+    dtype = "bf16" if G != 64 else "fp16"
+    T = _tokens_for(D, bk, bv, G, 8, 120 << 20)
+    p = _small(D, dtype, bk, bv, G, L=2, T=T, H=8)
+    _say("large blob", D, bk, bv, G, dtype, T)
+    x = inputs.make_kv(p, device=DEV)
+    total, _ = kvc.encoded_size(2, T, 8, D, bk, bv, G, dtype)
+    one, _ = kvc.encoded_size(1, T, 8, D, bk, bv, G, dtype)
+    assert total > 192 << 20 and one < 192 << 20
+    xd = kvc.decode(kvc.encode(x, bk, bv, G, seed=p.seed), x.shape, dtype, bk, bv, G, seed=p.seed)
+    for l in range(2):
+        xl = x[l:l + 1].contiguous()
+        dl = kvc.decode(kvc.encode(xl, bk, bv, G, seed=p.seed), xl.shape, dtype, bk, bv, G, seed=p.seed)
+        assert torch.equal(dl.view(torch.int16), xd[l:l + 1].view(torch.int16)), "layer %d" % l
+    torch.cuda.synchronize()
+    del x, xd
+    torch.cuda.empty_cache()
