@@ -152,12 +152,15 @@ def test_probe_copy():
     assert torch.equal(a, b)
 
 
-# full-size workloads: the presets, and the 8B-4k byte count at head_dim 64 in fp16
+# full-size workloads: the presets, the 8B-4k byte count at head_dim 64 in
+# fp16, and a 70B-shaped cache whose blob is larger than 4 GiB
 FULL = {
     "llama3_8b_4k": ("llama3_8b_4k", {}),
     "llama3_8b_32k": ("llama3_8b_32k", {}),
     "llama3_70b_16k": ("llama3_70b_16k", {}),
     "llama3_8b_4k_d64_fp16": ("llama3_8b_4k", dict(head_dim=64, tokens=8192, group=64, dtype="fp16")),
+    # a blob past 4 GiB (6.6 GB of 8-bit codes): 64-bit code and meta offsets
+    "llama3_70b_40k_8bit": ("llama3_70b_16k", dict(tokens=40000, bits_k=8, bits_v=8)),
 }
 
 
