@@ -58,3 +58,24 @@ def test_closed_forms(D):
     expect = np.zeros(D)
     expect[0] = c * np.sqrt(D)
     assert np.allclose(y, expect, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("D,G", [(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)])
+def test_group_factorization(D, G):
+    """H_D = H_{D/G} (x) H_G in Sylvester order, and the decode's reordering:
+    transforming zero + scale * q equals transforming the integer codes within
+    each group, scaling, adding zero * G at each group's first element, then
+    combining groups with H_{D/G} (x) I_G.  Exact in fp64 on these values."""
+    H = oracle.hadamard(D)
+    assert np.array_equal(H, np.kron(oracle.hadamard(D // G), oracle.hadamard(G)))
+    rng = np.random.default_rng(D + G)
+    for bits in (2, 4, 8):
+        q = rng.integers(0, 2 ** bits, size=(5, D)).astype(np.float64)
+        scale = rng.integers(1, 64, size=(5, D // G)) / 1024.0
+        zero = rng.integers(-512, 512, size=(5, D // G)) / 256.0
+        yhat = oracle.dequantize(q, scale, zero, G)
+        direct = yhat @ H.T
+        inner = (q.reshape(5, D // G, G) @ oracle.hadamard(G).T) * scale[..., None]
+        inner[..., 0] += zero * G
+        outer = np.kron(oracle.hadamard(D // G), np.eye(G))
+        assert np.array_equal(direct, inner.reshape(5, D) @ outer.T)
