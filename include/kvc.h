@@ -51,7 +51,12 @@
  *     buffers must stay alive until the stream has passed the work;
  *   - arguments are validated on the host before anything is enqueued; a
  *     negative kvc_status is returned and nothing runs on the GPU;
- *   - launch failures are reported as KVC_EHIP.
+ *   - launch failures are reported as KVC_EHIP;
+ *   - kvc_encode, kvc_decode and their paged forms enqueue kernel launches
+ *     only, so they may be captured into a HIP graph and replayed; make one
+ *     call of the same kind on the device first, outside the capture (it
+ *     fills the occupancy cache).  The chunked send / receive calls record
+ *     events and are not meant for capture.
  *
  * Supported: head_dim 64 or 128; bits 2, 4 or 8; group 32, 64 or 128 with
  * group <= head_dim; dtype bf16 or fp16.  Input values must be finite, and
