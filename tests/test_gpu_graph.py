@@ -60,3 +60,43 @@ def test_encode_decode_graph_replays(bk, bv, G):
         torch.cuda.synchronize()
         assert torch.equal(z.view(torch.int16), refs[1 - k][1].view(torch.int16))
     del g
+
+
+def test_paged_graph_replays():
+    p = presets.preset("qwen7b_paged").with_(name="graph-paged", layers=2, num_requests=5,
+                                              len_min=1, len_max=200, seed=4)
+    lens = inputs.request_lengths(p)
+    table, nb = inputs.block_table(p, lens)
+    offs, total = kvc.paged_layout(lens, p.layers, p.kv_heads, p.head_dim, p.bits_k, p.bits_v, p.group, p.dtype)
+    bt, sl, of = (torch.from_numpy(a).to(DEV) for a in (table, lens, offs))
+    pools = [inputs.make_pool(p, nb, device=DEV), inputs.make_pool(p.with_(k_sigma=2.0), nb, device=DEV)]
+    refs = []
+    for pool in pools:
+        b = kvc.encode_paged(pool, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed)
+        d = torch.full_like(pool, 3.0)
+        kvc.decode_paged(b, d, bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed)
+        refs.append((b, d))
+    pool_in = pools[0].clone()
+    blob = torch.zeros(total, dtype=torch.uint8, device=DEV)
+    out = torch.full_like(pool_in, 3.0)
+    kvc.encode_paged(pool_in, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=blob)
+    kvc.decode_paged(blob, out, bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    _say("graph: capture paged")
+    with torch.cuda.graph(g, stream=side):
+        kvc.encode_paged(pool_in, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=blob)
+        kvc.decode_paged(blob, out, bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    for r in range(6):
+        k = r % 2
+        pool_in.copy_(pools[k])
+        blob.fill_(0xA5)
+        out.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say("  replay", r)
+        assert torch.equal(blob, refs[k][0]), "replay %d: blob" % r
+        assert torch.equal(out.view(torch.int16), refs[k][1].view(torch.int16)), "replay %d: decode" % r
+    del g
