@@ -284,8 +284,9 @@ def copy_probe(kvc, dev, stream, reps=40):
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this library has no multi-GPU path "
-              "(every tile is independent; see the sharding note in the design document).",
+        print("bench.py measures one GPU: this library has no multi-GPU path. Every head_dim "
+              "vector is encoded and decoded on its own, so a cache shards by layer, head, "
+              "request or token range with no exchange between GPUs.",
               file=sys.stderr)
         sys.exit(2)
 

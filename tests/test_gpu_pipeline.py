@@ -110,7 +110,8 @@ def test_pipeline_validation():
 
 
 def test_documented_usage():
-    """The Python usage shown in the design document runs as written (smaller shape)."""
+    """The usage pattern of the Python binding -- encode and decode, then the
+    chunked send to pinned host memory and the receive back -- at a small shape."""
     kv = torch.randn(4, 2, 256, 8, 128, device=DEV).to(torch.bfloat16)
     blob = kvc.encode(kv, bits_k=4, bits_v=4, group=128, seed=0)
     back = kvc.decode(blob, kv.shape, "bf16", 4, 4, 128, seed=0)
