@@ -430,9 +430,10 @@ __device__ __forceinline__ void lds_done() { asm volatile("s_waitcnt lgkmcnt(0)"
 
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
-/* s_waitcnt immediate for vmcnt(0) with the other counters left alone
+/* s_waitcnt immediate for vmcnt(N) with the other counters left alone
  * (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8). */
-constexpr int kWaitVmem0 = 0x0f70;
+constexpr int wait_vmem_imm(int n) { return 0x0f70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitVmem0 = wait_vmem_imm(0);
 
 /* Raw buffer resource over `bytes` bytes from `base` (stride 0): a vector
  * store at a byte offset of `bytes` or more is dropped, a load there reads
@@ -891,8 +892,8 @@ __device__ __forceinline__ void butterfly_stages(float (&y)[D]) {
  * The in-group transform runs either on the matrix cores (the codes enter as
  * fp16 1024 + q; the bias adds exactly 1024 G to each group's first element,
  * which is subtracted exactly) or as the in-register butterfly on the codes
- * as fp32.  Both give the same integers, so the two kinds of decode agree to
- * the bit; which one runs is part of the launch shape (LARGE, below).
+ * as fp32.  Both give the same integers, so every kind of decode agrees to
+ * the bit; which one runs is part of the launch shape (MODE, below).
  *
  * Each lane's row goes to LDS one 128-byte line (8 chunks) at a time; the
  * wave then stores those lines with coalesced 16-byte stores, every store
@@ -906,17 +907,24 @@ __device__ __forceinline__ void butterfly_stages(float (&y)[D]) {
  * instead of being skipped by a branch around each store (those branches,
  * with their exec-mask saves and restores, cost 3% at 16k-32k tokens).
  *
- * LARGE (one wave per SIMD, for a blob larger than the memory-side cache):
- * the butterfly, and a tile starts with the last tile's stores still in
- * flight.  Otherwise (two waves per SIMD): the matrix cores, and a tile
- * starts once the last tile's stores have completed.  Measured, the matrix
- * cores make the two-wave decode 6-9% faster at 4k tokens and the paged one
- * 2-5% faster, but a lone wave per SIMD cannot hide their latency: at 32k
- * tokens they made it 13% slower.
+ * MODE, with the number of waves per SIMD it runs at (kvc_launch.hip):
+ *   kDecodeWaitTop (two waves): matrix cores; a tile starts once the last
+ *     tile's stores have completed, while the other wave computes.
+ *   kDecodeWaitStores (one wave): matrix cores; the tile's compute overlaps
+ *     the last tile's stores, which must complete before this tile's are
+ *     issued.  At most one tile of stores per wave is then in flight: with
+ *     two (the compiler's own waits allow that) the wider window of writes
+ *     ran 12-13% slower.
+ *   kDecodeLarge (one wave, blobs larger than the memory-side cache): the
+ *     butterfly, stores overlapped with no extra wait; its arithmetic spaces
+ *     the stores by itself, and it measured up to 2.5% faster there than the
+ *     matrix cores.
  */
-template <int D, int DT, int B, int G, bool PAGED, bool LARGE>
+constexpr int kDecodeWaitTop = 0, kDecodeWaitStores = 1, kDecodeLarge = 2;
+
+template <int D, int DT, int B, int G, bool PAGED, int MODE>
 KVC_KERNEL void decode_kernel(const LaunchArgs a) {
-  static_assert(!(PAGED && LARGE), "paged decodes use the two-wave shape");
+  constexpr bool LARGE = MODE == kDecodeLarge;
   constexpr int CH = D / 8, NG = D / G, NW = D * B / 32, VPW = 32 / B;
   constexpr float RS = Norm<D>::inv_sqrt;
   constexpr int HALF = 8;                         // chunks per row staged at a time: one line
@@ -939,7 +947,7 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   // for the codes counts the loop's loads and stores only
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   for (;;) {
-    if constexpr (!LARGE) __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the last tile's stores too
+    if constexpr (MODE == kDecodeWaitTop) __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the last tile's stores too
     float sc[NG], ze[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -978,6 +986,16 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
     }
     butterfly_stages<D, G, D>(y);
     KVC_PHASE();
+    if constexpr (MODE == kDecodeWaitStores) {
+      // outstanding: the last tile's stores, then the next tile's code and
+      // meta loads (NL instructions, none after the last tile)
+      constexpr int NL = D * B / 128 + 1;
+      static_assert(NL < 64, "vmcnt range");
+      if (more)
+        __builtin_amdgcn_s_waitcnt(wait_vmem_imm(NL));
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    }
     const v4u* sg = reinterpret_cast<const v4u*>(signs);
     const __amdgpu_buffer_rsrc_t out = tile_rsrc(cur.src, cur.count * CH * 16);
 #pragma unroll

@@ -19,22 +19,27 @@ namespace kvc {
 namespace {
 
 template <int D, int DT, int B, int G, bool PAGED>
-Kernel pick_op(Op op, bool large) {
+Kernel pick_op(Op op, int mode) {
   if (op == Op::Encode) return dev::encode_kernel<D, DT, B, G, PAGED>;
-  if constexpr (!PAGED)
-    if (large) return dev::decode_kernel<D, DT, B, G, false, true>;
-  return dev::decode_kernel<D, DT, B, G, PAGED, false>;
+  if constexpr (!PAGED) {
+    if (mode == dev::kDecodeLarge) return dev::decode_kernel<D, DT, B, G, false, dev::kDecodeLarge>;
+    if (mode == dev::kDecodeWaitStores) return dev::decode_kernel<D, DT, B, G, false, dev::kDecodeWaitStores>;
+  } else {
+    constexpr int M = D == 64 ? dev::kDecodeWaitTop : dev::kDecodeWaitStores;
+    if (mode == M) return dev::decode_kernel<D, DT, B, G, true, M>;
+  }
+  return nullptr;
 }
 
 template <int D, int DT, int B, bool PAGED>
-Kernel pick_g(Op op, int g, bool large) {
+Kernel pick_g(Op op, int g, int mode) {
   switch (g) {
     case 32:
-      return pick_op<D, DT, B, 32, PAGED>(op, large);
+      return pick_op<D, DT, B, 32, PAGED>(op, mode);
     case 64:
-      return pick_op<D, DT, B, 64, PAGED>(op, large);
+      return pick_op<D, DT, B, 64, PAGED>(op, mode);
     case 128:
-      if constexpr (D >= 128) return pick_op<D, DT, B, 128, PAGED>(op, large);
+      if constexpr (D >= 128) return pick_op<D, DT, B, 128, PAGED>(op, mode);
       return nullptr;
     default:
       return nullptr;
@@ -42,20 +47,20 @@ Kernel pick_g(Op op, int g, bool large) {
 }
 
 template <int D, int DT, bool PAGED>
-Kernel pick_b(Op op, int b, int g, bool large) {
+Kernel pick_b(Op op, int b, int g, int mode) {
   switch (b) {
-    case 2: return pick_g<D, DT, 2, PAGED>(op, g, large);
-    case 4: return pick_g<D, DT, 4, PAGED>(op, g, large);
-    case 8: return pick_g<D, DT, 8, PAGED>(op, g, large);
+    case 2: return pick_g<D, DT, 2, PAGED>(op, g, mode);
+    case 4: return pick_g<D, DT, 4, PAGED>(op, g, mode);
+    case 8: return pick_g<D, DT, 8, PAGED>(op, g, mode);
     default: return nullptr;
   }
 }
 
 }  // namespace
 
-Kernel KVC_PICK_NAME(KVC_D, KVC_DT)(Op op, int b, int g, bool paged, bool large) {
+Kernel KVC_PICK_NAME(KVC_D, KVC_DT)(Op op, int b, int g, bool paged, int mode) {
   if (op == Op::Rotate) return paged ? nullptr : dev::rotate_kernel<KVC_D, KVC_DT>;
-  return paged ? pick_b<KVC_D, KVC_DT, true>(op, b, g, false) : pick_b<KVC_D, KVC_DT, false>(op, b, g, large);
+  return paged ? pick_b<KVC_D, KVC_DT, true>(op, b, g, mode) : pick_b<KVC_D, KVC_DT, false>(op, b, g, mode);
 }
 
 }  // namespace kvc

@@ -38,10 +38,10 @@ __global__ __launch_bounds__(256) void copy_kernel(const v4u* __restrict__ src, 
 
 namespace {
 
-Kernel pick(Op op, int d, int dt, int b, int g, bool paged, bool large) {
-  if (d == 64) return dt == KVC_BF16 ? pick_d64_t0(op, b, g, paged, large) : pick_d64_t1(op, b, g, paged, large);
+Kernel pick(Op op, int d, int dt, int b, int g, bool paged, int mode) {
+  if (d == 64) return dt == KVC_BF16 ? pick_d64_t0(op, b, g, paged, mode) : pick_d64_t1(op, b, g, paged, mode);
   if (d == 128)
-    return dt == KVC_BF16 ? pick_d128_t0(op, b, g, paged, large) : pick_d128_t1(op, b, g, paged, large);
+    return dt == KVC_BF16 ? pick_d128_t0(op, b, g, paged, mode) : pick_d128_t1(op, b, g, paged, mode);
   return nullptr;
 }
 
@@ -91,53 +91,51 @@ int resident_groups(Kernel k, int threads, int64_t* out, int* cus_out = nullptr)
 
 constexpr int kSimdsPerCu = 4;
 
-/* Blob size above which the contiguous decode runs its LARGE variant, one
- * wave per SIMD: 3/4 of the 256 MB memory-side cache. */
+/* Blob size above which the contiguous decode runs in kDecodeLarge mode:
+ * 3/4 of the 256 MB memory-side cache. */
 constexpr uint64_t kDecodeLargeBlob = uint64_t(192) << 20;
 
 /*
  * How a launch fills the chip: waves per SIMD (0: every resident wave) and,
- * for the decode, the LARGE variant (butterfly, tiles start with the last
- * tile's stores in flight) or the other one (matrix cores, tiles wait for
- * them).  Every tile is streamed once, so extra waves only add independent
- * access streams once enough bytes are in flight.  Measured on 8B-shaped
- * caches, each kernel alone and alternating with the other:
+ * for the decode, its mode (kvc_device.h: the in-group transform and where a
+ * tile waits for the last tile's stores).  Every tile is streamed once, so
+ * extra waves only add independent access streams once enough bytes are in
+ * flight.  Measured on 8B-shaped caches, each kernel alone and alternating
+ * with the other:
  *   - encode: one wave per SIMD is as fast or faster (1-2% at 4k tokens,
  *     5-6% at 32k, about 4% at head_dim 64, 3% on the paged pool), except on
  *     a paged pool at head_dim 64, 5% slower there: 8 KiB tiles, each behind
  *     a dependent table load, keep too few bytes in flight;
  *   - contiguous decode of a blob larger than kDecodeLargeBlob (the blob an
- *     encode just wrote then no longer sits in the memory-side cache): the
- *     LARGE variant at one wave per SIMD; with the butterfly it was 3-10%
- *     faster from 6k tokens up at head_dim 128 and 5-6% at 64 than two
- *     waves that wait, and 4-7% faster than the matrix-core variant at two;
- *   - a smaller blob: the matrix-core variant at two waves per SIMD, 6-9%
- *     faster than the butterfly at 4k tokens (which was itself 2-3% faster
- *     at two waves than at one), and 5-10% faster than four waves at
- *     head_dim 64;
- *   - paged decode: the matrix-core variant at two waves per SIMD (one wave
- *     lost 13%; its tiles carry dependent table loads).
- * One wave that waits for its stores, or two that overlap them, measured
- * slower than the pairings above.  Grids between one and two waves per SIMD
- * leave some SIMDs with a wave more than others; with a static tile split
- * those finish last, and such grids measured slower than either.
+ *     encode just wrote then no longer sits in the memory-side cache):
+ *     kDecodeLarge at one wave per SIMD, 3-10% faster from 6k tokens up than
+ *     two waves that wait, and up to 2.5% faster than kDecodeWaitStores;
+ *   - a smaller blob: kDecodeWaitStores at one wave per SIMD, 5.6-6.6%
+ *     faster than kDecodeWaitTop at two waves (8B-4k, and head_dim 64 at 8k
+ *     tokens);
+ *   - paged decode: kDecodeWaitStores at one wave per SIMD at head_dim 128
+ *     (1.5% faster than kDecodeWaitTop at two); kDecodeWaitTop at two waves
+ *     at head_dim 64, where one wave lost 16%.
+ * Grids between one and two waves per SIMD leave some SIMDs with a wave more
+ * than others; with a static tile split those finish last, and such grids
+ * measured slower than either.
  */
 struct LaunchShape {
   int waves_per_simd;
-  bool large;
+  int mode;
 };
 
 LaunchShape launch_shape(Op op, const LaunchArgs& a, int head_dim) {
-  if (op == Op::Encode) return (a.paged && head_dim == 64) ? LaunchShape{0, false} : LaunchShape{1, false};
-  if (op == Op::Decode)
-    return (!a.paged && a.blob_total > kDecodeLargeBlob) ? LaunchShape{1, true} : LaunchShape{2, false};
-  return {0, false};
+  if (op == Op::Encode) return {(a.paged && head_dim == 64) ? 0 : 1, 0};
+  if (op != Op::Decode) return {0, 0};
+  if (a.paged) return head_dim == 64 ? LaunchShape{2, dev::kDecodeWaitTop} : LaunchShape{1, dev::kDecodeWaitStores};
+  return a.blob_total > kDecodeLargeBlob ? LaunchShape{1, dev::kDecodeLarge} : LaunchShape{1, dev::kDecodeWaitStores};
 }
 
 int run_plan(Op op, const Plan& plan, void* stream) {
   for (int i = 0; i < plan.n_launch; ++i) {
     const LaunchShape shape = launch_shape(op, plan.args[i], plan.head_dim);
-    Kernel k = pick(op, plan.head_dim, plan.dtype, plan.bits[i], plan.group, plan.args[i].paged != 0, shape.large);
+    Kernel k = pick(op, plan.head_dim, plan.dtype, plan.bits[i], plan.group, plan.args[i].paged != 0, shape.mode);
     if (!k) return KVC_ESHAPE;
     int64_t resident = 0;
     int cus = 0;

@@ -11,12 +11,14 @@ using Kernel = void (*)(LaunchArgs);
 #define KVC_PICK_CAT(D, DT) pick_d##D##_t##DT
 #define KVC_PICK_NAME(D, DT) KVC_PICK_CAT(D, DT)
 
-/* `large`: the decode variant for a contiguous blob larger than the
- * memory-side cache (one wave per SIMD; ignored for other kernels). */
-Kernel pick_d64_t0(Op op, int bits, int group, bool paged, bool large);
-Kernel pick_d64_t1(Op op, int bits, int group, bool paged, bool large);
-Kernel pick_d128_t0(Op op, int bits, int group, bool paged, bool large);
-Kernel pick_d128_t1(Op op, int bits, int group, bool paged, bool large);
+/* `mode`: the decode kernel's mode (kDecodeWaitTop / kDecodeWaitStores /
+ * kDecodeLarge in kvc_device.h; ignored for other kernels).  Only the modes
+ * the launcher uses are instantiated: contiguous WaitStores and Large, paged
+ * WaitTop at head_dim 64 and WaitStores at 128; others return nullptr. */
+Kernel pick_d64_t0(Op op, int bits, int group, bool paged, int mode);
+Kernel pick_d64_t1(Op op, int bits, int group, bool paged, int mode);
+Kernel pick_d128_t0(Op op, int bits, int group, bool paged, int mode);
+Kernel pick_d128_t1(Op op, int bits, int group, bool paged, int mode);
 
 }  // namespace kvc
 
