@@ -32,14 +32,18 @@
  * bit on every vector).
  *
  * Blob layout (for T tokens):
- *   codes: for l in [0, L), for kv in (K, V): a slab of T*H rows, (t, h)
- *          order, RB = D*b_kv/8 bytes each, stored in tiles of 64 rows:
- *          tile k starts at byte 64*k*RB of the slab, and inside a tile of
- *          n rows (64, or fewer for the last) the 16-byte piece c of row i
- *          is at byte (c*n + i)*16 of the tile;
- *          zero padding to a multiple of 256 bytes;
- *   meta:  [L, 2, T, H, D/group] entries of 4 bytes -- fp16 scale, then
- *          fp16 zero, little endian; zero padding to a multiple of 256.
+ *   codes: for l in [0, L), for kv in (K, V): a code slab of T*H rows,
+ *          (t, h) order, RB = D*b_kv/8 bytes each, stored in tiles of 64
+ *          rows: tile k starts at byte 64*k*RB of the slab, and inside a
+ *          tile of n rows (64, or fewer for the last) the 16-byte piece c
+ *          of row i is at byte (c*n + i)*16 of the tile; then zero padding
+ *          to a multiple of 256 bytes;
+ *   meta:  for l in [0, L), for kv in (K, V): a meta slab of T*H*(D/group)
+ *          entries of 4 bytes in (t, h, group) order -- fp16 scale, then
+ *          fp16 zero, little endian; then zero padding to a multiple of 256.
+ *   Every slab starts on a 256-byte boundary, so every full tile of 64 rows
+ *   (codes and meta) covers whole 128-byte lines; where T*H*RB and
+ *   T*H*(D/group)*4 are multiples of 256 there is no padding at all.
  *
  * Conventions for every call:
  *   - the caller allocates and owns all buffers; the library allocates no
@@ -74,7 +78,8 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+/* 2: every code and meta slab of the blob padded to a multiple of 256 bytes. */
+#define KVC_ABI_VERSION 2
 
 typedef enum kvc_status {
   KVC_OK = 0,

@@ -236,12 +236,11 @@ __device__ __forceinline__ v4u* code_row(const Tile& t, int lane, int& piece_str
   }
 }
 
-/* Zero the two padding runs of one blob (one wave, byte stores, < 512 bytes):
- * [codes_end, meta_start) and [meta_end, blob_end). */
-__device__ __noinline__ void write_padding(uint8_t* blob, uint64_t codes_end, uint64_t meta_start,
-                                           uint64_t meta_end, uint64_t blob_end) {
-  for (uint64_t p = codes_end + threadIdx.x; p < meta_start; p += 64) blob[p] = 0;
-  for (uint64_t p = meta_end + threadIdx.x; p < blob_end; p += 64) blob[p] = 0;
+/* Zero the padding after a slab's codes or meta: n < 256 bytes, a multiple
+ * of 4, from a 4-byte aligned address (one dword store per lane). */
+__device__ __forceinline__ void zero_tail(uint8_t* p, uint64_t n) {
+  typedef __attribute__((address_space(1))) uint32_t global_u32;
+  if (threadIdx.x * 4u < n) ((global_u32*)p)[threadIdx.x] = 0;
 }
 
 __device__ __forceinline__ uint64_t align256(uint64_t n) { return (n + 255u) & ~uint64_t(255); }
@@ -319,8 +318,9 @@ __device__ __forceinline__ void cursor_next(const LaunchArgs& a, Cursor& c) {
  * skipped (false), as are items whose table entry, length or blob extent is
  * invalid (bit 0 of *err is then set).  `tensor` is the KV side (source of
  * an encode, destination of a decode), `blob` the encoded side.  With PAD,
- * the first tile of each blob (of the launch that owns slab 0) also zeroes
- * that blob's padding, right when it is found.
+ * the last tile of each slab also zeroes the padding that follows the slab's
+ * codes and its meta (each is padded to a multiple of 256 bytes), right when
+ * it is found.
  */
 template <int D, bool PAD, bool PAGED>
 __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c, const uint8_t* tensor,
@@ -334,11 +334,14 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
     t.count = static_cast<int>(a.rows - v0 < kTileVectors ? a.rows - v0 : kTileVectors);
     t.geom = 0;
     t.src = tensor + (s * a.rows + v0) * vec_bytes;
-    t.codes = blob + l * a.rows * (a.row_k + a.row_v) + kv * a.rows * a.row_k + v0 * row;
-    t.meta = blob + a.meta_offset + (s * a.rows + v0) * a.groups * 4;
-    if (PAD && c.item == 0 && a.slab_first == 0)
-      write_padding(blob, uint64_t(a.layers) * a.rows * (a.row_k + a.row_v), a.meta_offset,
-                    a.meta_offset + uint64_t(a.layers) * 2 * a.rows * a.groups * 4, a.blob_total);
+    uint8_t* cs = blob + l * (a.code_slab_k + a.code_slab_v) + (kv ? a.code_slab_k : 0);
+    uint8_t* ms = blob + a.meta_offset + s * a.meta_slab;
+    t.codes = cs + v0 * row;
+    t.meta = ms + v0 * a.groups * 4;
+    if (PAD && v0 + t.count == a.rows) {  // the slab's last tile also zeroes its padding
+      zero_tail(cs + a.rows * row, (kv ? a.code_slab_v : a.code_slab_k) - a.rows * row);
+      zero_tail(ms + a.rows * a.groups * 4, a.meta_slab - a.rows * a.groups * 4);
+    }
     return true;
   }
   const int32_t len = ld_const(a.lens + c.r);
@@ -355,10 +358,10 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
   const int32_t blk = ld_const(a.table + int64_t(c.r) * a.max_blocks + c.j);
   const int64_t off = ld_const(a.offsets + c.r);
   const int64_t rows = int64_t(len) * a.heads;
-  const uint64_t codes_bytes = uint64_t(a.layers) * rows * (a.row_k + a.row_v);
-  const uint64_t meta_start = align256(codes_bytes);
-  const uint64_t meta_end = meta_start + uint64_t(a.layers) * 2 * rows * a.groups * 4;
-  const uint64_t total = align256(meta_end);
+  const uint64_t ck = align256(uint64_t(rows) * a.row_k), cv = align256(uint64_t(rows) * a.row_v);
+  const uint64_t mslab = align256(uint64_t(rows) * a.groups * 4);
+  const uint64_t meta_start = uint64_t(a.layers) * (ck + cv);
+  const uint64_t total = meta_start + uint64_t(a.layers) * 2 * mslab;
   if (blk < 0 || blk >= a.num_blocks || off < 0 || (off & 15) || uint64_t(off) > a.blob_bytes ||
       total > a.blob_bytes - uint64_t(off)) {
     if (a.err) atomicOr(a.err, 1);
@@ -373,11 +376,14 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
   t.geom = code_geom(row0 - tile0, min<int64_t>(kTileVectors, rows - tile0),
                      min<int64_t>(kTileVectors, rows - tile0 - kTileVectors));
   t.src = tensor + ((s * a.num_blocks + blk) * int64_t(a.block_size) * a.heads + v0) * vec_bytes;
-  uint8_t* rb = blob + off;
-  t.codes = rb + l * rows * (a.row_k + a.row_v) + kv * rows * a.row_k + tile0 * row;
-  t.meta = rb + meta_start + (s * rows + row0) * a.groups * 4;
-  if (PAD && c.i == 0 && c.j == 0 && c.sub == 0 && a.slab_first == 0)
-    write_padding(rb, codes_bytes, meta_start, meta_end, total);
+  uint8_t* cs = blob + off + l * (ck + cv) + (kv ? ck : 0);
+  uint8_t* ms = blob + off + meta_start + s * mslab;
+  t.codes = cs + tile0 * row;
+  t.meta = ms + row0 * a.groups * 4;
+  if (PAD && row0 + t.count == rows) {  // the slab's last tile also zeroes its padding
+    zero_tail(cs + rows * row, (kv ? cv : ck) - rows * row);
+    zero_tail(ms + rows * a.groups * 4, mslab - rows * a.groups * 4);
+  }
   return true;
 }
 
@@ -396,6 +402,10 @@ __device__ __forceinline__ bool next_tile(const LaunchArgs& a, Cursor& c, const 
 /* ---- LDS staging ------------------------------------------------------------- */
 
 typedef __attribute__((address_space(3))) void lds_void;
+/* A tile buffer as an LDS-space pointer.  The kernels cast their __shared__
+ * array once at the call (a cast of the array itself, which folds); a cast
+ * of a generic pointer inside the DMA helper would carry a null check. */
+typedef __attribute__((address_space(3))) v4u lds_v4u;
 
 /* Cache policy of the streaming accesses (the NT bit of the DMA loads and
  * the decode's output stores).  A contiguous tensor is read or written once,
@@ -467,7 +477,7 @@ __device__ __forceinline__ int opaque_lane() {
  * l / CH < VPI) this is L0 ^ (16 * ((k * VPI) % CH)), L0 the k = 0 offset.
  */
 template <int D, int AUX>
-__device__ __forceinline__ void dma_rows_policy(const uint8_t* src, int count, v4u* lds) {
+__device__ __forceinline__ void dma_rows_policy(const uint8_t* src, int count, lds_v4u* lds) {
   constexpr int CH = D / 8, VPI = 64 / CH;
   const int lane = opaque_lane();
   const int vin = lane / CH, col = lane % CH;
@@ -490,7 +500,7 @@ __device__ __forceinline__ void dma_rows_policy(const uint8_t* src, int count, v
 }
 
 template <int D, bool STREAM>
-__device__ __forceinline__ void dma_rows(const uint8_t* src, int count, v4u* lds) {
+__device__ __forceinline__ void dma_rows(const uint8_t* src, int count, lds_v4u* lds) {
   dma_rows_policy<D, STREAM ? kCacheStream : kCacheDefault>(src, count, lds);
 }
 
@@ -752,7 +762,7 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
   cursor_init<PAGED>(a, c);
   Tile cur;
   if (!next_tile<D, true, PAGED>(a, c, tensor, blob, cur, true)) return;
-  dma_rows<D, !PAGED>(cur.src, cur.count, lds);
+  dma_rows<D, !PAGED>(cur.src, cur.count, (lds_v4u*)lds);
   wait_vmem<0>();
   lds_order();
   HadamardA had;
@@ -764,7 +774,7 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
     lds_done();  // every lane's row is in registers: the buffer is free
     Tile nxt;
     const bool more = next_tile<D, true, PAGED>(a, c, tensor, blob, nxt, false);
-    if (more) dma_rows<D, !PAGED>(nxt.src, nxt.count, lds);
+    if (more) dma_rows<D, !PAGED>(nxt.src, nxt.count, (lds_v4u*)lds);
     KVC_PHASE();
     float y[D];
     hadamard_mfma<D, DT>(xc, had, y);
@@ -1058,7 +1068,7 @@ __device__ __forceinline__ void rotate_tiles(const LaunchArgs& a, float* out) {
   for (bool ok = next_tile<D, false, false>(a, c, tensor, nullptr, t, true); ok;
        ok = next_tile<D, false, false>(a, c, tensor, nullptr, t, false)) {
     lds_done();
-    dma_rows<D, false>(t.src, t.count, lds);
+    dma_rows<D, false>(t.src, t.count, (lds_v4u*)lds);
     wait_vmem<0>();
     lds_order();
     v4u xc[CH];

@@ -98,18 +98,23 @@ int blob_sizes(const kvc_desc* d, int64_t tokens, BlobSizes* out) {
   int st = check_desc(d);
   if (st != KVC_OK) return st;
   if (tokens < 0 || !out) return KVC_EINVAL;
-  uint64_t rows, lr, per_row, codes, meta, groups_total, a, b, total;
+  const uint64_t layers = static_cast<uint64_t>(d->layers);
+  const uint64_t row_k = static_cast<uint64_t>(d->head_dim) * d->bits_k / 8;
+  const uint64_t row_v = static_cast<uint64_t>(d->head_dim) * d->bits_v / 8;
+  const uint64_t meta_row = static_cast<uint64_t>(d->head_dim / d->group) * 4;
+  uint64_t rows, ck, cv, m, pair, codes, metas, total;
   if (!mul_ok(static_cast<uint64_t>(tokens), static_cast<uint64_t>(d->kv_heads), &rows)) return KVC_ESHAPE;
-  if (!mul_ok(rows, static_cast<uint64_t>(d->layers), &lr)) return KVC_ESHAPE;
-  per_row = static_cast<uint64_t>(d->head_dim) * (d->bits_k + d->bits_v) / 8;
-  if (!mul_ok(lr, per_row, &codes)) return KVC_ESHAPE;
-  if (!mul_ok(lr, 2ull * (d->head_dim / d->group), &groups_total)) return KVC_ESHAPE;
-  if (!mul_ok(groups_total, 4, &meta)) return KVC_ESHAPE;
-  if (!align_up(codes, &a) || !align_up(meta, &b) || !add_ok(a, b, &total)) return KVC_ESHAPE;
+  if (!mul_ok(rows, row_k, &ck) || !align_up(ck, &ck) || !mul_ok(rows, row_v, &cv) || !align_up(cv, &cv) ||
+      !mul_ok(rows, meta_row, &m) || !align_up(m, &m))
+    return KVC_ESHAPE;
+  if (!add_ok(ck, cv, &pair) || !mul_ok(pair, layers, &codes) || !mul_ok(2 * layers, m, &metas) ||
+      !add_ok(codes, metas, &total))
+    return KVC_ESHAPE;
   if (total > static_cast<uint64_t>(INT64_MAX)) return KVC_ESHAPE;
-  out->codes = codes;
-  out->meta_offset = a;
-  out->meta = meta;
+  out->code_slab_k = ck;
+  out->code_slab_v = cv;
+  out->meta_slab = m;
+  out->meta_offset = codes;
   out->total = total;
   return KVC_OK;
 }
@@ -186,6 +191,9 @@ int plan_contiguous(Op op, const kvc_desc* d, const void* src, void* dst,
   base.paged = 0;
   base.rows = static_cast<int64_t>(rows);
   base.tiles_per_slab = static_cast<int64_t>((rows + kTileVectors - 1) / kTileVectors);
+  base.code_slab_k = sz.code_slab_k;
+  base.code_slab_v = sz.code_slab_v;
+  base.meta_slab = sz.meta_slab;
   base.meta_offset = sz.meta_offset;
   base.blob_total = sz.total;
   split_slabs(op, d, plan, base);

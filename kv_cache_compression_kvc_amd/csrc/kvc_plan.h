@@ -38,8 +38,11 @@ struct LaunchArgs {
   // contiguous layout
   int64_t rows;           // T * H vectors per slab
   int64_t tiles_per_slab; // ceil(rows / 64)
+  uint64_t code_slab_k;   // bytes of one K code slab (rows * row_k rounded up to 256)
+  uint64_t code_slab_v;   // bytes of one V code slab
+  uint64_t meta_slab;     // bytes of one meta slab (rows * groups * 4 rounded up to 256)
   uint64_t meta_offset;   // byte offset of the meta section in the blob
-  uint64_t blob_total;    // bytes of the blob proper (codes, meta, padding)
+  uint64_t blob_total;    // bytes of the blob
 
   // paged layout
   int64_t num_blocks;
@@ -76,11 +79,15 @@ int plan_contiguous(Op op, const kvc_desc* d, const void* src, void* dst,
 int plan_paged(Op op, const kvc_desc* d, const void* src, void* dst,
                uint64_t blob_bytes, const kvc_paged* pg, Plan* plan);
 
-/* Sizes of a blob for T tokens (no validation beyond overflow). */
+/* Sizes of a blob for T tokens (no validation beyond overflow).  Each
+ * (layer, K/V) slab of codes and of meta is padded to a multiple of 256
+ * bytes; the codes section holds the code slabs (l, K), (l, V) for l = 0..L-1,
+ * the meta section the meta slabs in the same order. */
 struct BlobSizes {
-  uint64_t codes;       // bytes of the codes section before padding
-  uint64_t meta_offset; // start of the meta section
-  uint64_t meta;        // bytes of the meta section before padding
+  uint64_t code_slab_k; // bytes of one K code slab, padding included
+  uint64_t code_slab_v; // bytes of one V code slab, padding included
+  uint64_t meta_slab;   // bytes of one meta slab, padding included
+  uint64_t meta_offset; // start of the meta section (= bytes of the codes section)
   uint64_t total;
 };
 int blob_sizes(const kvc_desc* d, int64_t tokens, BlobSizes* out);

@@ -13,7 +13,7 @@
  *   E3 quantize  u, meta          -> q  u8 [rows, D]
  *   E4 pack      q                -> codes (the blob's codes section, in its
  *                                     tiled order of 16-byte pieces)
- *   E5 padding   zeroes the blob's two padding runs
+ *   E5 padding   zeroes the padding after each slab's codes and meta
  * Decode:
  *   D1 unpack    codes            -> q  u8 [rows, D]
  *   D2 dequant   q, meta          -> z  fp32 [rows, D]  (1/sqrt(D) folded in)
@@ -87,6 +87,17 @@ KVC_KERNEL void rotate_kernel(const LaunchArgs a, float* u) {
   dev::rotate_tiles<D, DT, true>(a, u);
 }
 
+/* Start of a slab's code rows and of its meta entries in the blob (each
+ * slab padded to a multiple of 256 bytes). */
+__device__ __forceinline__ uint8_t* codes_of(const LaunchArgs& a, uint8_t* blob, int64_t s) {
+  const int64_t l = s >> 1, kv = s & 1;
+  return blob + l * (a.code_slab_k + a.code_slab_v) + (kv ? a.code_slab_k : 0);
+}
+
+__device__ __forceinline__ uint8_t* meta_of(const LaunchArgs& a, uint8_t* blob, int64_t s) {
+  return blob + a.meta_offset + s * a.meta_slab;
+}
+
 /* E2: min / max per group across G/4 lanes, then the meta word. */
 template <int D, int B, int G>
 __global__ __launch_bounds__(kThreads) void minmax_kernel(const LaunchArgs a, const float* u) {
@@ -94,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(const LaunchArgs a, co
   const int lane = threadIdx.x & 63, m = lane % LPR, sub = lane / LPR;
   const int64_t s = slab_of(a);
   const float4* y = reinterpret_cast<const float4*>(u) + s * a.rows * LPR;
-  uint32_t* meta = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.dst) + a.meta_offset) + s * a.rows * NG;
+  uint32_t* meta = reinterpret_cast<uint32_t*>(meta_of(a, static_cast<uint8_t*>(a.dst), s));
   const int64_t wave = int64_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / 64;
   const int64_t stride = int64_t(gridDim.x) * kWavesPerBlock * STEP;
   for (int64_t r0 = wave * STEP; r0 < a.rows; r0 += stride) {
@@ -129,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const LaunchArgs a, 
   const float4* y = reinterpret_cast<const float4*>(u) + s * units;
   uint32_t* q = reinterpret_cast<uint32_t*>(q8) + s * units;
   const uint32_t* meta =
-      reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.dst) + a.meta_offset) + s * a.rows * NG;
+      reinterpret_cast<const uint32_t*>(meta_of(a, static_cast<uint8_t*>(a.dst), s));
   const int64_t stride = int64_t(gridDim.x) * kThreads;
   for (int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; i0 < units; i0 += stride * kUnroll) {
     float4 w[kUnroll];
@@ -157,11 +168,6 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const LaunchArgs a, 
   }
 }
 
-/* Bytes of the codes of one slab: start of its packed rows in the blob. */
-__device__ __forceinline__ uint8_t* codes_of(const LaunchArgs& a, uint8_t* blob, int64_t s) {
-  const int64_t l = s >> 1, kv = s & 1;
-  return blob + l * a.rows * (a.row_k + a.row_v) + kv * a.rows * a.row_k;
-}
 
 /* 32/B codes (bytes) of a unit -> one packed 32-bit word, code k at bits
  * [B*k, B*k + B). */
@@ -225,10 +231,13 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, cons
   }
 }
 
-/* E5: the blob's padding runs, one wave. */
-__global__ __launch_bounds__(64) void padding_kernel(uint8_t* blob, uint64_t codes_end, uint64_t meta_start,
-                                                     uint64_t meta_end, uint64_t blob_end) {
-  dev::write_padding(blob, codes_end, meta_start, meta_end, blob_end);
+/* E5: the padding after each slab's codes and meta, one wave per slab. */
+__global__ __launch_bounds__(64) void padding_kernel(const LaunchArgs a) {
+  const int64_t s = blockIdx.x, kv = s & 1;
+  const int64_t row = kv ? a.row_v : a.row_k;
+  uint8_t* blob = static_cast<uint8_t*>(a.dst);
+  dev::zero_tail(codes_of(a, blob, s) + a.rows * row, (kv ? a.code_slab_v : a.code_slab_k) - a.rows * row);
+  dev::zero_tail(meta_of(a, blob, s) + a.rows * a.groups * 4, a.meta_slab - a.rows * a.groups * 4);
 }
 
 /* ---- decode stages ---------------------------------------------------------- */
@@ -273,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const LaunchArgs a, c
   const uint32_t* q = reinterpret_cast<const uint32_t*>(q8) + s * units;
   float4* out = reinterpret_cast<float4*>(z) + s * units;
   const uint32_t* meta =
-      reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.src) + a.meta_offset) + s * a.rows * NG;
+      reinterpret_cast<const uint32_t*>(meta_of(a, static_cast<uint8_t*>(const_cast<void*>(a.src)), s));
   const int64_t stride = int64_t(gridDim.x) * kThreads;
   for (int64_t i0 = int64_t(blockIdx.x) * kThreads + threadIdx.x; i0 < units; i0 += stride * kUnroll) {
     uint32_t c[kUnroll], mw[kUnroll];
@@ -421,11 +430,13 @@ int run(const Plan& plan, hipStream_t st, uint8_t* q8, float* f) {
   }
   if (ENC && plan.n_launch > 0) {
     const LaunchArgs& a = plan.args[0];
-    const uint64_t codes_end = uint64_t(a.layers) * a.rows * (a.row_k + a.row_v);
-    const uint64_t meta_end = a.meta_offset + uint64_t(a.layers) * 2 * a.rows * a.groups * 4;
-    hipLaunchKernelGGL(padding_kernel, dim3(1), dim3(64), 0, st, static_cast<uint8_t*>(a.dst), codes_end,
-                       a.meta_offset, meta_end, a.blob_total);
-    if (hipGetLastError() != hipSuccess) return KVC_EHIP;
+    const bool padded = a.code_slab_k != uint64_t(a.rows) * a.row_k || a.code_slab_v != uint64_t(a.rows) * a.row_v ||
+                        a.meta_slab != uint64_t(a.rows) * a.groups * 4;
+    if (padded) {
+      if (a.layers > (1 << 30)) return KVC_ESHAPE;
+      hipLaunchKernelGGL(padding_kernel, dim3(static_cast<unsigned>(2 * a.layers)), dim3(64), 0, st, a);
+      if (hipGetLastError() != hipSuccess) return KVC_EHIP;
+    }
   }
   return KVC_OK;
 }

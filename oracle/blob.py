@@ -8,13 +8,19 @@ link and decoding it on the other side; they define no byte format.  The
 layout used here, for a KV tensor [L, 2, T, H, D] (2 = K then V) with b_K
 and b_V bits per code and group size G:
 
-  codes section  for l in 0..L-1, for kv in (K, V): the slab of T*H rows in
-                 (t, h) order, each row D*b_kv/8 bytes of packed codes,
-                 stored in tiles of 64 rows (see ``tile_codes``)
-  padding        zero bytes up to a multiple of 256
-  meta section   [L, 2, T, H, D/G] entries of 4 bytes: fp16 scale (bytes
-                 0-1) then fp16 zero (bytes 2-3), little endian
-  padding        zero bytes up to a multiple of 256
+  codes section  for l in 0..L-1, for kv in (K, V): the code slab of T*H
+                 rows in (t, h) order, each row D*b_kv/8 bytes of packed
+                 codes, stored in tiles of 64 rows (see ``tile_codes``),
+                 then zero bytes up to a multiple of 256
+  meta section   for l in 0..L-1, for kv in (K, V): the meta slab of T*H*D/G
+                 entries of 4 bytes in (t, h, group) order, fp16 scale
+                 (bytes 0-1) then fp16 zero (bytes 2-3), little endian, then
+                 zero bytes up to a multiple of 256
+
+Every slab therefore starts on a 256-byte boundary, and so does every full
+tile of 64 rows inside it (64 code rows are a multiple of 1 KiB, 64 rows of
+meta a multiple of 256 bytes).  When T*H*D*b/8 and T*H*D/G*4 are multiples
+of 256 there is no padding between slabs.
 
 Paged input: a pool [L, 2, num_blocks, block_size, H, D] and, per request
 r, a row of a block table naming the physical block of each logical block
@@ -49,7 +55,8 @@ PIECE = 16       # bytes of one piece of a code row
 # k * TILE_ROWS * RB of the slab.  Inside a tile each row's RB bytes are cut
 # into RB / PIECE pieces of PIECE bytes, and piece c of the tile's row i sits
 # at byte (c * n + i) * PIECE of the tile: all rows' piece 0, then all rows'
-# piece 1, and so on.  The slab keeps its size, rows * RB bytes.
+# piece 1, and so on.  The tiles take rows * RB bytes, the slab's padding
+# follows them.
 
 
 def tile_codes(rows: np.ndarray) -> np.ndarray:
@@ -104,32 +111,46 @@ class BlobLayout:
         return self.head_dim * (self.bits_k if kv == 0 else self.bits_v) // 8
 
     @property
-    def codes_bytes(self) -> int:
-        return self.layers * self.rows * (self.row_bytes(0) + self.row_bytes(1))
-
-    @property
-    def meta_offset(self) -> int:
-        return _align256(self.codes_bytes)
-
-    @property
     def groups(self) -> int:
         return self.head_dim // self.group
 
+    def code_slab_bytes(self, kv: int) -> int:
+        """Bytes of one (layer, K/V) code slab, padding included."""
+        return _align256(self.rows * self.row_bytes(kv))
+
     @property
-    def meta_bytes(self) -> int:
-        return self.layers * 2 * self.rows * self.groups * 4
+    def meta_slab_bytes(self) -> int:
+        """Bytes of one (layer, K/V) meta slab, padding included."""
+        return _align256(self.rows * self.groups * 4)
+
+    @property
+    def meta_offset(self) -> int:
+        return self.layers * (self.code_slab_bytes(0) + self.code_slab_bytes(1))
 
     @property
     def total(self) -> int:
-        return self.meta_offset + _align256(self.meta_bytes)
+        return self.meta_offset + 2 * self.layers * self.meta_slab_bytes
 
     def codes_slab(self, l: int, kv: int) -> int:
         """Byte offset of the (layer, K/V) code slab."""
-        return l * self.rows * (self.row_bytes(0) + self.row_bytes(1)) + kv * self.rows * self.row_bytes(0)
+        return l * (self.code_slab_bytes(0) + self.code_slab_bytes(1)) + kv * self.code_slab_bytes(0)
 
     def meta_slab(self, l: int, kv: int) -> int:
         """Byte offset of the (layer, K/V) meta slab."""
-        return self.meta_offset + (l * 2 + kv) * self.rows * self.groups * 4
+        return self.meta_offset + (l * 2 + kv) * self.meta_slab_bytes
+
+    def padding(self):
+        """The zero-filled byte ranges [start, end) of the blob, in order."""
+        out = []
+        for l in range(self.layers):
+            for kv in range(2):
+                c = self.codes_slab(l, kv)
+                out.append((c + self.rows * self.row_bytes(kv), c + self.code_slab_bytes(kv)))
+        for l in range(self.layers):
+            for kv in range(2):
+                m = self.meta_slab(l, kv)
+                out.append((m + self.rows * self.groups * 4, m + self.meta_slab_bytes))
+        return [(a, b) for a, b in out if b > a]
 
 
 def blob_layout(layers, tokens, kv_heads, head_dim, bits_k, bits_v, group) -> BlobLayout:

@@ -66,14 +66,19 @@ def check_sampled_encode(p, x_gpu, blob_gpu, idx):
     return rep
 
 
+def meta_scales(blob_gpu, lay):
+    """fp32 scales [L * 2 * rows, D / G] of a blob on the GPU, in (layer, K/V, row) order."""
+    n = lay.rows * lay.groups * 4
+    meta = torch.cat([blob_gpu[lay.meta_slab(l, kv):lay.meta_slab(l, kv) + n]
+                      for l in range(lay.layers) for kv in range(2)]).view(torch.int16)
+    return meta.view(-1, lay.groups, 2)[..., 0].contiguous().view(torch.float16).float()
+
+
 def decode_error_bound_ok(p, x_gpu, xhat_gpu, blob_gpu):
     """Every vector: ||x - xhat|| <= sqrt(D) * max group scale / 2 + the output rounding."""
     D = p.head_dim
     lay = oracle.blob_layout(p.layers, p.tokens, p.kv_heads, D, p.bits_k, p.bits_v, p.group)
-    ng = lay.groups
-    meta = blob_gpu[lay.meta_offset:lay.meta_offset + lay.meta_bytes].view(torch.int16)
-    scale = meta.view(-1, ng, 2)[..., 0].contiguous().view(torch.float16).float()
-    smax = scale.max(dim=1).values
+    smax = meta_scales(blob_gpu, lay).max(dim=1).values
     worst = 0.0
     nvec = x_gpu.numel() // D
     chunk = 1 << 22

@@ -134,6 +134,6 @@ def check_blob(x_bits, blob_gpu, dtype, bits_k, bits_v, group, seed):
             b = bits_k if kv == 0 else bits_v
             codes, meta = blob_rows(blob_gpu, lay, l, kv, np.arange(T * H))
             rep.merge(check_rows(x_bits[l, kv].reshape(-1, D), dtype, b, group, seed, codes, meta))
-    assert not blob_gpu[lay.codes_bytes:lay.meta_offset].any(), "codes padding not zero"
-    assert not blob_gpu[lay.meta_offset + lay.meta_bytes:lay.total].any(), "meta padding not zero"
+    for a, b in lay.padding():
+        assert not blob_gpu[a:b].any(), "padding [%d, %d) not zero" % (a, b)
     return rep

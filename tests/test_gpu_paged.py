@@ -185,8 +185,7 @@ def test_paged_full_size_sampled():
         slot = torch.from_numpy(toks % BS).to(DEV)
         a = pool[:, :, blk, slot].float().reshape(-1, D)         # [L*2*n*H, D] in (l, kv, t, h) order
         b = dst[:, :, blk, slot].float().reshape(-1, D)
-        meta = sub[lay.meta_offset:lay.meta_offset + lay.meta_bytes].view(torch.int16)
-        scale = meta.view(-1, lay.groups, 2)[..., 0].contiguous().view(torch.float16).float()
+        scale = gpu_util.meta_scales(sub, lay)
         bound = (D ** 0.5) * scale.max(dim=1).values / 2 * (1 + 1e-5) + 2.0 ** -8 * b.norm(dim=1)
         ratio = float(((a - b).norm(dim=1) / bound.clamp_min(1e-30)).max())
         assert ratio <= 1.0, (r, ratio)

@@ -42,7 +42,7 @@ def host_lib():
 def test_hip_library_exports_every_symbol(hip_lib):
     for name in declared():
         assert hasattr(hip_lib, name), name
-    assert hip_lib.kvc_abi_version() == 1
+    assert hip_lib.kvc_abi_version() == 2
 
 
 def test_host_library_exports_host_symbols(host_lib):
