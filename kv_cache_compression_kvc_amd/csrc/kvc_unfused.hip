@@ -231,13 +231,16 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const LaunchArgs a, cons
   }
 }
 
-/* E5: the padding after each slab's codes and meta, one wave per slab. */
+/* E5: the padding after each slab's codes and meta, one wave per slab
+ * (grid-stride over the 2 * L slabs). */
 __global__ __launch_bounds__(64) void padding_kernel(const LaunchArgs a) {
-  const int64_t s = blockIdx.x, kv = s & 1;
-  const int64_t row = kv ? a.row_v : a.row_k;
   uint8_t* blob = static_cast<uint8_t*>(a.dst);
-  dev::zero_tail(codes_of(a, blob, s) + a.rows * row, (kv ? a.code_slab_v : a.code_slab_k) - a.rows * row);
-  dev::zero_tail(meta_of(a, blob, s) + a.rows * a.groups * 4, a.meta_slab - a.rows * a.groups * 4);
+  for (int64_t s = blockIdx.x; s < 2 * a.layers; s += gridDim.x) {
+    const int64_t kv = s & 1;
+    const int64_t row = kv ? a.row_v : a.row_k;
+    dev::zero_tail(codes_of(a, blob, s) + a.rows * row, (kv ? a.code_slab_v : a.code_slab_k) - a.rows * row);
+    dev::zero_tail(meta_of(a, blob, s) + a.rows * a.groups * 4, a.meta_slab - a.rows * a.groups * 4);
+  }
 }
 
 /* ---- decode stages ---------------------------------------------------------- */
@@ -433,8 +436,8 @@ int run(const Plan& plan, hipStream_t st, uint8_t* q8, float* f) {
     const bool padded = a.code_slab_k != uint64_t(a.rows) * a.row_k || a.code_slab_v != uint64_t(a.rows) * a.row_v ||
                         a.meta_slab != uint64_t(a.rows) * a.groups * 4;
     if (padded) {
-      if (a.layers > (1 << 30)) return KVC_ESHAPE;
-      hipLaunchKernelGGL(padding_kernel, dim3(static_cast<unsigned>(2 * a.layers)), dim3(64), 0, st, a);
+      const unsigned grid = static_cast<unsigned>(std::min<int64_t>(2 * a.layers, 1024));
+      hipLaunchKernelGGL(padding_kernel, dim3(grid), dim3(64), 0, st, a);
       if (hipGetLastError() != hipSuccess) return KVC_EHIP;
     }
   }
