@@ -57,7 +57,8 @@ def parse():
 
 
 # the sources the fused encode / decode kernels are built from
-FUSED_SOURCES = ["kvc_device.h", "kvc_host.cpp", "kvc_inst.hip", "kvc_launch.hip", "kvc_pick.h", "kvc_plan.h"]
+FUSED_SOURCES = ["kvc_cursor.h", "kvc_device.h", "kvc_host.cpp", "kvc_inst.hip", "kvc_launch.hip", "kvc_pick.h",
+                 "kvc_plan.h"]
 
 
 def _code_only(text):

@@ -40,6 +40,9 @@
 
 #include "kvc_plan.h"
 
+#define KVC_CURSOR_FN __device__ __forceinline__
+#include "kvc_cursor.h"
+
 namespace kvc {
 namespace dev {
 
@@ -255,12 +258,14 @@ __device__ __forceinline__ T ld_const(const T* p) {
 
 /*
  * Wave-uniform position in a launch's item space, advanced by the grid size
- * without divisions.  Contiguous items are (slab i, tile) in radix
- * tiles_per_slab; paged items are (slab i, request r, block j, subtile sub)
- * in radices (num_reqs, max_blocks, subtiles).
+ * without divisions.  Contiguous items walk the launch's slabs tile by tile
+ * (kvc_cursor.h: slab offsets carried along, no products per step); paged
+ * items are (slab i, request r, block j, subtile sub) in radices (num_reqs,
+ * max_blocks, subtiles).  k.item is the item of either layout.
  */
 struct Cursor {
-  int64_t item, i, tile, di, dtile;
+  ContigCursor k;
+  int64_t i, di;
   int32_t r, j, sub, dr, dj, dsub;
 };
 
@@ -277,13 +282,10 @@ __device__ __forceinline__ void split_paged(const LaunchArgs& a, int64_t x, int6
 template <bool PAGED>
 __device__ __forceinline__ void cursor_init(const LaunchArgs& a, Cursor& c) {
   const int64_t start = blockIdx.x, step = gridDim.x;
-  c.item = start;
   if constexpr (!PAGED) {
-    c.i = start / a.tiles_per_slab;
-    c.tile = start - c.i * a.tiles_per_slab;
-    c.di = step / a.tiles_per_slab;
-    c.dtile = step - c.di * a.tiles_per_slab;
+    contig_init(a, start, step, c.k);
   } else {
+    c.k.item = start;
     split_paged(a, start, c.i, c.r, c.j, c.sub);
     split_paged(a, step, c.di, c.dr, c.dj, c.dsub);
   }
@@ -291,16 +293,11 @@ __device__ __forceinline__ void cursor_init(const LaunchArgs& a, Cursor& c) {
 
 template <bool PAGED>
 __device__ __forceinline__ void cursor_next(const LaunchArgs& a, Cursor& c) {
-  c.item += gridDim.x;
   if constexpr (!PAGED) {
-    c.tile += c.dtile;
-    c.i += c.di;
-    if (c.tile >= a.tiles_per_slab) {
-      c.tile -= a.tiles_per_slab;
-      ++c.i;
-    }
+    contig_next(a, int64_t(gridDim.x), c.k);
     return;
   }
+  c.k.item += gridDim.x;
   c.sub += c.dsub;
   int32_t carry = c.sub >= a.subtiles;
   if (carry) c.sub -= a.subtiles;
@@ -327,20 +324,16 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
                                             uint8_t* blob, Tile& t) {
   constexpr int64_t vec_bytes = int64_t(D) * 2;
   if constexpr (!PAGED) {
-    const int64_t v0 = c.tile * kTileVectors;
-    const int64_t s = c.i * a.slab_step + a.slab_first;
-    const int64_t l = s >> 1, kv = s & 1;
-    const int64_t row = kv ? a.row_v : a.row_k;
-    t.count = static_cast<int>(a.rows - v0 < kTileVectors ? a.rows - v0 : kTileVectors);
+    ContigTile ct;
+    contig_tile(a, c.k, vec_bytes, ct);
+    t.count = ct.count;
     t.geom = 0;
-    t.src = tensor + (s * a.rows + v0) * vec_bytes;
-    uint8_t* cs = blob + l * (a.code_slab_k + a.code_slab_v) + (kv ? a.code_slab_k : 0);
-    uint8_t* ms = blob + a.meta_offset + s * a.meta_slab;
-    t.codes = cs + v0 * row;
-    t.meta = ms + v0 * a.groups * 4;
-    if (PAD && v0 + t.count == a.rows) {  // the slab's last tile also zeroes its padding
-      zero_tail(cs + a.rows * row, (kv ? a.code_slab_v : a.code_slab_k) - a.rows * row);
-      zero_tail(ms + a.rows * a.groups * 4, a.meta_slab - a.rows * a.groups * 4);
+    t.src = tensor + ct.src;
+    t.codes = blob + ct.codes;
+    t.meta = blob + ct.meta;
+    if (PAD && ct.last) {  // the slab's last tile also zeroes its padding
+      zero_tail(blob + c.k.codes + a.rows * a.row, uint32_t(a.code_tail));
+      zero_tail(blob + c.k.meta + a.rows * a.groups * 4, uint32_t(a.meta_tail));
     }
     return true;
   }
@@ -392,7 +385,7 @@ template <int D, bool PAD, bool PAGED>
 __device__ __forceinline__ bool next_tile(const LaunchArgs& a, Cursor& c, const uint8_t* tensor, uint8_t* blob,
                                           Tile& t, bool first) {
   if (!first) cursor_next<PAGED>(a, c);
-  while (c.item < a.total_items) {
+  while (c.k.item < a.total_items) {
     if (cursor_tile<D, PAD, PAGED>(a, c, tensor, blob, t)) return true;
     cursor_next<PAGED>(a, c);
   }

@@ -197,12 +197,26 @@ int plan_contiguous(Op op, const kvc_desc* d, const void* src, void* dst,
   base.meta_offset = sz.meta_offset;
   base.blob_total = sz.total;
   split_slabs(op, d, plan, base);
+  // Every offset below is at most the tensor's or the blob's size, both of
+  // which were computed without overflow above.
+  const int64_t slab_bytes = static_cast<int64_t>(rows) * 2 * d->head_dim;
   for (int i = 0; i < plan->n_launch; ++i) {
+    LaunchArgs& a = plan->args[i];
     uint64_t items;
-    if (!mul_ok(static_cast<uint64_t>(plan->args[i].n_slabs),
-                static_cast<uint64_t>(plan->args[i].tiles_per_slab), &items))
+    if (!mul_ok(static_cast<uint64_t>(a.n_slabs), static_cast<uint64_t>(a.tiles_per_slab), &items))
       return KVC_ESHAPE;
-    plan->args[i].total_items = static_cast<int64_t>(items);
+    a.total_items = static_cast<int64_t>(items);
+    const bool v = a.slab_first == 1;  // a launch of V slabs only (K and V widths differ)
+    a.src_first = a.slab_first * slab_bytes;
+    a.src_stride = a.slab_step * slab_bytes;
+    a.codes_first = v ? static_cast<int64_t>(sz.code_slab_k) : 0;
+    a.codes_stride = a.slab_step == 1 ? static_cast<int64_t>(sz.code_slab_k)
+                                      : static_cast<int64_t>(sz.code_slab_k + sz.code_slab_v);
+    a.meta_first = static_cast<int64_t>(sz.meta_offset + a.slab_first * sz.meta_slab);
+    a.meta_stride = a.slab_step * static_cast<int64_t>(sz.meta_slab);
+    a.row = v ? a.row_v : a.row_k;
+    a.code_tail = static_cast<int32_t>((v ? sz.code_slab_v : sz.code_slab_k) - rows * a.row);
+    a.meta_tail = static_cast<int32_t>(sz.meta_slab - rows * a.groups * 4);
   }
   return KVC_OK;
 }

@@ -43,6 +43,16 @@ struct LaunchArgs {
   uint64_t meta_slab;     // bytes of one meta slab (rows * groups * 4 rounded up to 256)
   uint64_t meta_offset;   // byte offset of the meta section in the blob
   uint64_t blob_total;    // bytes of the blob
+  // slab i of this launch (s = i * slab_step + slab_first) starts at byte
+  // src_first + i * src_stride of the tensor, its codes at codes_first +
+  // i * codes_stride and its meta at meta_first + i * meta_stride of the blob
+  int64_t src_first, src_stride;
+  int64_t codes_first, codes_stride;
+  int64_t meta_first, meta_stride;
+  int32_t row;            // code bytes per vector in this launch (row_k or row_v)
+  int32_t code_tail;      // zero bytes after a code slab's rows * row bytes (< 256)
+  int32_t meta_tail;      // zero bytes after a meta slab's rows * groups * 4 bytes (< 256)
+  int32_t pad1;
 
   // paged layout
   int64_t num_blocks;

@@ -139,6 +139,23 @@ def test_host_half_under_sanitizers(tmp_path):
     assert p.stdout.strip() == "ok"
 
 
+def test_contiguous_cursor_against_layout(tmp_path):
+    """The kernels' contiguous cursor (kvc_cursor.h, built here for the host)
+    visits every tile once, at the offsets the blob layout defines, for many
+    shapes and grid sizes."""
+    cxx = shutil.which("g++")
+    if not cxx:
+        pytest.skip("g++ not available")
+    exe = tmp_path / "cursor_check"
+    src = os.path.join(ROOT, "tests", "host", "cursor_check.cpp")
+    host = os.path.join(ROOT, "kv_cache_compression_kvc_amd", "csrc", "kvc_host.cpp")
+    subprocess.run([cxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", src, host, "-o", str(exe)], check=True)
+    p = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert p.returncode == 0, p.stdout + p.stderr
+    assert p.stdout.startswith("ok")
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 def test_unfused_workspace_size(host_lib, shape):
     """One code byte per element (rounded up to 256), then four fp32 bytes per element."""
