@@ -14,7 +14,8 @@ Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
   encode/decode  per-kernel raw GB/s and algorithmic-HBM GB/s (bytes read
                  plus bytes written) as a fraction of the 8 TB/s peak
   roofline       the dominant kernel: algorithmic bytes per launch / mean
-                 launch time (HIP events on the launch stream), vs 8 TB/s
+                 launch time (HIP events on the launch stream, recorded
+                 without a system-scope fence), vs 8 TB/s
   break_even     encode + decode time vs the wire time the compression saves
                  at 100 and 400 Gbit/s
   pipeline       per-layer chunked encode overlapped with the copy of each
@@ -28,6 +29,7 @@ Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -40,6 +42,54 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+class TimingEvents:
+    """Timing-only HIP events, recorded without a system-scope fence.
+
+    torch's events use the default flags, and recording one performs a
+    system-scope release that writes back and invalidates the caches.
+    Between two kernels that adds several microseconds to each measured
+    kernel and slows the kernel after it.  These events are created with
+    hipEventDisableSystemFence (timing stays enabled) in the process's one
+    HIP runtime, the one torch and the library use.  The caller synchronizes
+    the device before reading them."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        from kv_cache_compression_kvc_amd import _lib
+        runtimes = _lib._hip_runtimes()
+        if len(runtimes) != 1:
+            raise RuntimeError("expected one HIP runtime in the process, found %s" % runtimes)
+        h = self._hip = ctypes.CDLL(runtimes[0])
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            self._check(h.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE), "create")
+            self._ev.append(e)
+
+    @staticmethod
+    def _check(status, what):
+        if status != 0:
+            raise RuntimeError("hipEvent %s failed with status %d" % (what, status))
+
+    def record(self, k, stream):
+        self._check(self._hip.hipEventRecord(self._ev[k], ctypes.c_void_p(stream.cuda_stream)), "record")
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        self._check(self._hip.hipEventElapsedTime(ctypes.byref(t), self._ev[a], self._ev[b]), "elapsed time")
+        return t.value
+
+    def close(self):
+        for e in self._ev:
+            self._hip.hipEventDestroy(e)
+        self._ev = []
 
 
 def parse():
@@ -152,16 +202,17 @@ def unfused_leg(kvc, p, xs, outs, dsts, a, stream, t_enc, t_dec, raw_bytes):
         enc(i % nsets)
         dec(i % nsets)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    ev = TimingEvents(3 * a.steps)
     for i in range(a.steps):
-        ev[i][0].record(stream)
+        ev.record(3 * i, stream)
         enc(i % nsets)
-        ev[i][1].record(stream)
+        ev.record(3 * i + 1, stream)
         dec(i % nsets)
-        ev[i][2].record(stream)
+        ev.record(3 * i + 2, stream)
     torch.cuda.synchronize()
-    te = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps / 1e3
-    td = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps / 1e3
+    te = sum(ev.ms(3 * i, 3 * i + 1) for i in range(a.steps)) / a.steps / 1e3
+    td = sum(ev.ms(3 * i + 1, 3 * i + 2) for i in range(a.steps)) / a.steps / 1e3
+    ev.close()
     del ws
     elems = raw_bytes // 2
     bk, bv, G = p.bits_k, p.bits_v, p.group
@@ -197,6 +248,8 @@ def pipeline_leg(kvc, p, x, xout, stream, raw_bytes, reps=3, chunk_layers=8):
         ts = []
         for i in range(reps + 1):
             torch.cuda.synchronize()
+            # torch's default events: the system-scope release at e1 makes the
+            # interval end when the copied data is visible to the host
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             copy.wait_stream(stream)
@@ -270,13 +323,14 @@ def copy_probe(kvc, dev, stream, reps=40):
     dst = torch.empty_like(src)
     for _ in range(reps // 2):
         kvc.probe_copy(src, dst)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
+    ev = TimingEvents(2)
+    ev.record(0, stream)
     for _ in range(reps - reps // 2):
         kvc.probe_copy(src, dst)
-    c1.record(stream)
+    ev.record(1, stream)
     torch.cuda.synchronize()
-    gbps = 2 * src.numel() * (reps - reps // 2) / (c0.elapsed_time(c1) / 1e3) / 1e9
+    gbps = 2 * src.numel() * (reps - reps // 2) / (ev.ms(0, 1) / 1e3) / 1e9
+    ev.close()
     del src, dst
     torch.cuda.empty_cache()
     return gbps
@@ -354,20 +408,20 @@ def main():
         dec(i % nsets)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    ev = TimingEvents(3 * a.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
-        e = ev[i]
-        e[0].record(stream)
+        ev.record(3 * i, stream)
         enc(i % nsets)
-        e[1].record(stream)
+        ev.record(3 * i + 1, stream)
         dec(i % nsets)
-        e[2].record(stream)
+        ev.record(3 * i + 2, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    enc_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    enc_ms = sorted(ev.ms(3 * i, 3 * i + 1) for i in range(a.steps))
+    dec_ms = sorted(ev.ms(3 * i + 1, 3 * i + 2) for i in range(a.steps))
+    ev.close()
     t_enc = sum(enc_ms) / a.steps / 1e3   # s per encode (mean)
     t_dec = sum(dec_ms) / a.steps / 1e3
     ms_per_step = wall / a.steps * 1e3
