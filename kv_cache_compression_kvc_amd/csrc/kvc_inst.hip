@@ -22,7 +22,10 @@ template <int D, int DT, int B, int G, bool PAGED>
 Kernel pick_op(Op op, int mode) {
   if (op == Op::Encode) return dev::encode_kernel<D, DT, B, G, PAGED>;
   if constexpr (!PAGED) {
-    if (mode == dev::kDecodeLarge) return dev::decode_kernel<D, DT, B, G, false, dev::kDecodeLarge>;
+    // the butterfly decode is picked at head_dim 64, and for 4-bit codes in
+    // one group per vector at head_dim 128 (the launch rule in kvc_launch.hip)
+    if constexpr (D == 64 || (B == 4 && G == D))
+      if (mode == dev::kDecodeLarge) return dev::decode_kernel<D, DT, B, G, false, dev::kDecodeLarge>;
     if (mode == dev::kDecodeWaitStores) return dev::decode_kernel<D, DT, B, G, false, dev::kDecodeWaitStores>;
   } else {
     constexpr int M = D == 64 ? dev::kDecodeWaitTop : dev::kDecodeWaitStores;

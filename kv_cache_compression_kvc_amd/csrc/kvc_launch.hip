@@ -91,9 +91,11 @@ int resident_groups(Kernel k, int threads, int64_t* out, int* cus_out = nullptr)
 
 constexpr int kSimdsPerCu = 4;
 
-/* Blob size above which the contiguous decode runs in kDecodeLarge mode:
- * 3/4 of the 256 MB memory-side cache. */
-constexpr uint64_t kDecodeLargeBlob = uint64_t(192) << 20;
+/* Blob sizes above which a contiguous decode launch runs in kDecodeLarge
+ * mode: at head_dim 64, 3/4 of the 256 MB memory-side cache; at head_dim
+ * 128, only for 4-bit codes in one group per vector, past 512 MiB. */
+constexpr uint64_t kDecodeLargeBlobD64 = uint64_t(192) << 20;
+constexpr uint64_t kDecodeLargeBlobD128 = uint64_t(512) << 20;
 
 /*
  * How a launch fills the chip: waves per SIMD (0: every resident wave) and,
@@ -106,10 +108,15 @@ constexpr uint64_t kDecodeLargeBlob = uint64_t(192) << 20;
  *     5-6% at 32k, about 4% at head_dim 64, 3% on the paged pool), except on
  *     a paged pool at head_dim 64, 5% slower there: 8 KiB tiles, each behind
  *     a dependent table load, keep too few bytes in flight;
- *   - contiguous decode of a blob larger than kDecodeLargeBlob (the blob an
- *     encode just wrote then no longer sits in the memory-side cache):
- *     kDecodeLarge at one wave per SIMD, 3-10% faster from 6k tokens up than
- *     two waves that wait, and up to 2.5% faster than kDecodeWaitStores;
+ *   - contiguous decode, head_dim 64, blob above kDecodeLargeBlobD64 (the
+ *     blob an encode just wrote then no longer sits in the memory-side
+ *     cache): kDecodeLarge at one wave per SIMD, 1-3% faster than
+ *     kDecodeWaitStores (2- and 4-bit, groups of 32 and 64, 1 GB blobs);
+ *   - contiguous decode, head_dim 128: kDecodeWaitStores at every size,
+ *     2-11% faster than kDecodeLarge on 0.3-2 GB blobs of 2-bit, 8-bit or
+ *     grouped codes and on 4-bit G128 blobs up to 408 MiB; only 4-bit codes
+ *     with G = 128 past kDecodeLargeBlobD128 keep kDecodeLarge (1.4-3.8%
+ *     faster from 544 MiB up);
  *   - a smaller blob: kDecodeWaitStores at one wave per SIMD, 5.6-6.6%
  *     faster than kDecodeWaitTop at two waves (8B-4k, and head_dim 64 at 8k
  *     tokens);
@@ -125,16 +132,22 @@ struct LaunchShape {
   int mode;
 };
 
-LaunchShape launch_shape(Op op, const LaunchArgs& a, int head_dim) {
+/* Whether a contiguous decode launch of `bits`-bit codes takes kDecodeLarge. */
+bool decode_large(const LaunchArgs& a, int head_dim, int bits) {
+  if (head_dim == 64) return a.blob_total > kDecodeLargeBlobD64;
+  return bits == 4 && a.groups == 1 && a.blob_total > kDecodeLargeBlobD128;
+}
+
+LaunchShape launch_shape(Op op, const LaunchArgs& a, int head_dim, int bits) {
   if (op == Op::Encode) return {(a.paged && head_dim == 64) ? 0 : 1, 0};
   if (op != Op::Decode) return {0, 0};
   if (a.paged) return head_dim == 64 ? LaunchShape{2, dev::kDecodeWaitTop} : LaunchShape{1, dev::kDecodeWaitStores};
-  return a.blob_total > kDecodeLargeBlob ? LaunchShape{1, dev::kDecodeLarge} : LaunchShape{1, dev::kDecodeWaitStores};
+  return decode_large(a, head_dim, bits) ? LaunchShape{1, dev::kDecodeLarge} : LaunchShape{1, dev::kDecodeWaitStores};
 }
 
 int run_plan(Op op, const Plan& plan, void* stream) {
   for (int i = 0; i < plan.n_launch; ++i) {
-    const LaunchShape shape = launch_shape(op, plan.args[i], plan.head_dim);
+    const LaunchShape shape = launch_shape(op, plan.args[i], plan.head_dim, plan.bits[i]);
     Kernel k = pick(op, plan.head_dim, plan.dtype, plan.bits[i], plan.group, plan.args[i].paged != 0, shape.mode);
     if (!k) return KVC_ESHAPE;
     int64_t resident = 0;

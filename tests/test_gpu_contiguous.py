@@ -237,26 +237,30 @@ def _tokens_for(D, bk, bv, G, H, target):
     return (target // per_token) // 64 * 64 + 3
 
 
-# every (head_dim, bits_k, bits_v, group), plus K and V at different widths
-LARGE_GRID = [(D, b, b, G) for D in (64, 128) for b in (2, 4, 8) for G in (32, 64, 128) if G <= D]
-LARGE_GRID.append((128, 2, 4, 64))
+# Where the contiguous decode takes the butterfly variant (kDecodeLarge): at
+# head_dim 64 past 192 MiB of blob, at head_dim 128 for 4-bit codes with
+# G = 128 past 512 MiB.  Every such (head_dim, bits, group), plus K 2-bit /
+# V 4-bit at G = 128, where only the V launch takes the butterfly.
+# (head_dim, bits_k, bits_v, group, MiB of one layer's blob, line in MiB)
+LARGE_GRID = [(64, b, b, G, 120, 192) for b in (2, 4, 8) for G in (32, 64)]
+LARGE_GRID += [(128, 4, 4, 128, 300, 512), (128, 2, 4, 128, 300, 512)]
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("D,bk,bv,G", LARGE_GRID)
-def test_large_blob_decode_matches_per_layer(D, bk, bv, G):
-    """Two layers whose blob is above 192 MiB decode with the butterfly variant
-    (one wave per SIMD); each layer alone (about 120 MiB) decodes on the
-    matrix cores.  Both must give the same bits; the slabs end in a partial
-    tile (8 heads, tokens 3 past a multiple of 64)."""
+@pytest.mark.parametrize("D,bk,bv,G,layer_mib,line_mib", LARGE_GRID)
+def test_large_blob_decode_matches_per_layer(D, bk, bv, G, layer_mib, line_mib):
+    """Two layers whose blob is past the line decode with the butterfly
+    variant (one wave per SIMD); each layer alone, below the line, decodes on
+    the matrix cores.  Both must give the same bits; the slabs end in a
+    partial tile (8 heads, tokens 3 past a multiple of 64)."""
     dtype = "bf16" if G != 64 else "fp16"
-    T = _tokens_for(D, bk, bv, G, 8, 120 << 20)
+    T = _tokens_for(D, bk, bv, G, 8, layer_mib << 20)
     p = _small(D, dtype, bk, bv, G, L=2, T=T, H=8)
     _say("large blob", D, bk, bv, G, dtype, T)
     x = inputs.make_kv(p, device=DEV)
     total, _ = kvc.encoded_size(2, T, 8, D, bk, bv, G, dtype)
     one, _ = kvc.encoded_size(1, T, 8, D, bk, bv, G, dtype)
-    assert total > 192 << 20 and one < 192 << 20
+    assert total > line_mib << 20 and one < line_mib << 20
     xd = kvc.decode(kvc.encode(x, bk, bv, G, seed=p.seed), x.shape, dtype, bk, bv, G, seed=p.seed)
     for l in range(2):
         xl = x[l:l + 1].contiguous()

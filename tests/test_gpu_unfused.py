@@ -122,25 +122,27 @@ def test_unfused_full_size_equals_fused(name):
     torch.cuda.empty_cache()
 
 
-# (head_dim, dtype, bits, group, tokens, heads): blobs above 192 MiB whose
-# slabs end in a partial tile (rows per slab 500015 = 47 mod 64, 1000015 = 15)
-LARGE_RAGGED = [(128, "bf16", 8, 64, 100003, 5), (64, "fp16", 8, 32, 200003, 5)]
+# (head_dim, dtype, bits, group, tokens, heads, line in MiB): blobs past the
+# size where the decode takes the butterfly variant (head_dim 64: 192 MiB;
+# head_dim 128, 4-bit, G = 128: 512 MiB), whose slabs end in a partial tile
+# (rows per slab 2000015 = 15 mod 64, 1000015 = 15)
+LARGE_RAGGED = [(128, "bf16", 4, 128, 400003, 5, 512), (64, "fp16", 8, 32, 200003, 5, 192)]
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("D,dtype,b,G,T,H", LARGE_RAGGED)
-def test_large_ragged_blob_both_decodes(D, dtype, b, G, T, H):
-    """A blob above 192 MiB (decoded by the butterfly variant, one wave per
+@pytest.mark.parametrize("D,dtype,b,G,T,H,line_mib", LARGE_RAGGED)
+def test_large_ragged_blob_both_decodes(D, dtype, b, G, T, H, line_mib):
+    """A blob past the line (decoded by the butterfly variant, one wave per
     SIMD, stores overlapped) whose slabs end in a partial tile.  Each layer
-    encoded on its own gives a blob below 192 MiB, decoded by the matrix-core
-    variant; the two decodes must agree to the bit, the encode must match the
-    separate-kernel comparator's blob, and nothing may be written outside the
-    decode output."""
+    encoded on its own gives a blob below the line, decoded by the
+    matrix-core variant; the two decodes must agree to the bit, the encode
+    must match the separate-kernel comparator's blob, and nothing may be
+    written outside the decode output."""
     p = _small(D, dtype, b, b, G, L=2, T=T, H=H)
     _say("large ragged: generate", D, dtype)
     x = inputs.make_kv(p, device=DEV)
     total, _ = kvc.encoded_size(p.layers, p.tokens, p.kv_heads, D, b, b, G, dtype)
-    assert total > 192 << 20
+    assert total > line_mib << 20
     out_f, out_u, dec_f, dec_u = _both(p, x)
     assert torch.equal(out_f, out_u)
     _decodes_agree(dec_u, dec_f)
@@ -153,7 +155,7 @@ def test_large_ragged_blob_both_decodes(D, dtype, b, G, T, H):
     for l in range(p.layers):
         xl = x[l:l + 1].contiguous()
         tl, _ = kvc.encoded_size(1, p.tokens, p.kv_heads, D, b, b, G, dtype)
-        assert tl < 192 << 20
+        assert tl < line_mib << 20
         bl = kvc.encode(xl, b, b, G, seed=p.seed)
         dl = kvc.decode(bl, xl.shape, dtype, b, b, G, seed=p.seed)
         torch.cuda.synchronize()
