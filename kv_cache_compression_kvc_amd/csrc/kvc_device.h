@@ -401,13 +401,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4u lds_v4u;
 
 /* Cache policy of the streaming accesses (the NT bit of the DMA loads and
- * the decode's output stores).  A contiguous tensor is read or written once,
- * front to back, and the NT hint keeps it from displacing other lines in L2
- * and the memory-side cache: measured on a 0.54 GB encode + decode pair, the
- * two kernels run 15% faster back to back and the decode no longer leaves
- * dirty lines for the next kernel to write back.  On the paged pool (16 KiB
- * blocks scattered over the pool) the same hint made both kernels about 5%
- * slower, so paged launches keep the default policy. */
+ * the decode's output stores).  A tensor is read or written once, front to
+ * back, and the NT hint keeps it from displacing other lines in L2 and the
+ * memory-side cache: measured on a 0.54 GB encode + decode pair, the two
+ * kernels run 15% faster back to back and the decode no longer leaves dirty
+ * lines for the next kernel to write back.  The decode's stores into a
+ * paged pool take the hint too (the encode after it ran 1.2% faster); the
+ * encode's loads from a pool keep the default policy, which measured the
+ * same there. */
 constexpr int kCacheDefault = 0;
 constexpr int kCacheStream = 2;
 
@@ -1023,7 +1024,7 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
         const int v = slot / HALF;
         const int q = (slot % HALF) ^ (v % HALF);
         __builtin_amdgcn_raw_buffer_store_b128(lds_out[slot], out, uint32_t((v * CH + h * HALF + q) * 16), 0,
-                                               PAGED ? kCacheDefault : kCacheStream);
+                                               kCacheStream);
       }
     }
     if (!more) break;
