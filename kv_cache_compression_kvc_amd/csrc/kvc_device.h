@@ -919,10 +919,10 @@ __device__ __forceinline__ void butterfly_stages(float (&y)[D]) {
  *     issued.  At most one tile of stores per wave is then in flight: with
  *     two (the compiler's own waits allow that) the wider window of writes
  *     ran 12-13% slower.
- *   kDecodeLarge (one wave, blobs larger than the memory-side cache): the
- *     butterfly, stores overlapped with no extra wait; its arithmetic spaces
- *     the stores by itself, and it measured up to 2.5% faster there than the
- *     matrix cores.
+ *   kDecodeLarge (one wave; large blobs at head_dim 64, and 4-bit codes in
+ *     one group per vector past 512 MiB at head_dim 128): the butterfly,
+ *     stores overlapped with no extra wait; its arithmetic spaces the stores
+ *     by itself, and it measured 1-4% faster there than the matrix cores.
  */
 constexpr int kDecodeWaitTop = 0, kDecodeWaitStores = 1, kDecodeLarge = 2;
 
