@@ -1,8 +1,9 @@
-"""The fused encode and decode under HIP graph capture: the calls allocate
-nothing and enqueue only kernel launches, so a serving loop can capture them
-once and replay.  Every replay is checked against the eager result, with
-eager work and synchronizations between replays, and the input changes
-between replays (the graph reads it afresh each time)."""
+"""The fused encode and decode under HIP graph capture, and on two streams
+at once.  The calls allocate nothing and enqueue only kernel launches, so a
+serving loop can capture them once and replay.  Every replay is checked
+against the eager result, with eager work and synchronizations between
+replays, and the input changes between replays (the graph reads it afresh
+each time)."""
 import sys
 
 import pytest
@@ -100,3 +101,36 @@ def test_paged_graph_replays():
         assert torch.equal(blob, refs[k][0]), "replay %d: blob" % r
         assert torch.equal(out.view(torch.int16), refs[k][1].view(torch.int16)), "replay %d: decode" % r
     del g
+
+
+def test_two_streams_at_once_equal_serial():
+    """Encodes and decodes enqueued on two streams at the same time, on
+    independent buffers, give the same bits as the same calls run one after
+    the other: the kernels share no state, and the launch-shape cache is
+    filled on the host under a lock."""
+    shapes = [(4, 4, 128, 301), (2, 8, 64, 77), (8, 2, 32, 190)]
+    cases = []
+    for n, (bk, bv, G, T) in enumerate(shapes):
+        p = presets.preset("llama3_8b_4k").with_(name="streams-%d" % n, layers=2, tokens=T, kv_heads=8,
+                                                 bits_k=bk, bits_v=bv, group=G, seed=n)
+        x = inputs.make_kv(p, device=DEV)
+        b = kvc.encode(x, bk, bv, G, seed=n)
+        cases.append((p, x, b, kvc.decode(b, x.shape, p.dtype, bk, bv, G, seed=n)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):
+        for k, (p, x, b, y) in enumerate(cases):
+            s = streams[(k + rep) % 2]
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                ob = torch.empty_like(b)
+                oy = torch.empty_like(y)
+                kvc.encode(x, p.bits_k, p.bits_v, p.group, seed=p.seed, out=ob, stream=s)
+                kvc.decode(ob, x.shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed, out=oy, stream=s)
+            outs.append((k, ob, oy))
+    torch.cuda.synchronize()
+    _say("two streams:", len(outs), "calls")
+    for k, ob, oy in outs:
+        assert torch.equal(ob, cases[k][2])
+        assert torch.equal(oy.view(torch.int16), cases[k][3].view(torch.int16))
