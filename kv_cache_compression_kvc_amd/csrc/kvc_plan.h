@@ -1,7 +1,8 @@
 /*
  * kvc_plan.h -- launch plans shared by the host half (kvc_host.cpp, plain
- * C++) and the device half (kvc_kernels.hip).  No HIP types: the host half
- * builds with g++ and is unit-tested without a GPU.
+ * C++) and the device half (kvc_device.h, kvc_cursor.h and the .hip files).
+ * No HIP types: the host half builds with g++ and is unit-tested without a
+ * GPU.
  *
  * A plan describes one kernel launch over "items".  Each item is a tile of
  * at most 64 consecutive head_dim vectors of one (layer, K/V) slab; every
