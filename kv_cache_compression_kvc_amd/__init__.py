@@ -53,6 +53,35 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
+def _dtype_name(t):
+    if t.dtype not in _TORCH_TO_NAME:
+        raise ValueError("KV tensors must be bfloat16 or float16, not %s" % t.dtype)
+    return _TORCH_TO_NAME[t.dtype]
+
+
+def _torch_dtype(name):
+    if name not in _NAME_TO_TORCH:
+        raise ValueError("dtype must be 'bf16' or 'fp16', not %r" % (name,))
+    return _NAME_TO_TORCH[name]
+
+
+def _kv_shape(shape, what):
+    """(L, T, H, D) of a [L, 2, T, H, D] shape; axis 1 holds K and V."""
+    shape = tuple(int(n) for n in shape)
+    if len(shape) != 5 or shape[1] != 2:
+        raise ValueError("%s must have shape [L, 2, T, H, D], got %s" % (what, list(shape)))
+    return shape[0], shape[2], shape[3], shape[4]
+
+
+def _check_out(out, shape, dtype):
+    """A caller's output tensor must be exactly what the kernels write: the C
+    calls take no output size, so a smaller tensor would be written past its
+    end."""
+    if out is not None and (tuple(out.shape) != tuple(shape) or out.dtype != dtype):
+        raise ValueError("out must be a %s tensor of shape %s, got %s of shape %s"
+                         % (dtype, list(shape), out.dtype, list(out.shape)))
+
+
 def _check_cuda(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
@@ -84,11 +113,9 @@ def sign_mask(seed, head_dim):
 
 def encode(kv, bits_k, bits_v, group, seed=0, out=None, stream=None):
     """Encode a contiguous [L, 2, T, H, D] GPU tensor; returns the uint8 blob."""
+    L, T, H, D = _kv_shape(kv.shape, "kv")
+    dt = _dtype_name(kv)
     _check_cuda(kv, out)
-    L, two, T, H, D = kv.shape
-    if two != 2:
-        raise ValueError("axis 1 must hold K and V")
-    dt = _TORCH_TO_NAME[kv.dtype]
     total, _ = encoded_size(L, T, H, D, bits_k, bits_v, group, dt)
     if out is None:
         out = torch.empty(total, dtype=torch.uint8, device=kv.device)
@@ -99,10 +126,11 @@ def encode(kv, bits_k, bits_v, group, seed=0, out=None, stream=None):
 
 def decode(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, stream=None):
     """Decode a blob into a [L, 2, T, H, D] GPU tensor of ``dtype``."""
+    L, T, H, D = _kv_shape(shape, "shape")
+    _check_out(out, shape, _torch_dtype(dtype))
     _check_cuda(blob, out)
-    L, two, T, H, D = shape
     if out is None:
-        out = torch.empty(tuple(shape), dtype=_NAME_TO_TORCH[dtype], device=blob.device)
+        out = torch.empty(tuple(shape), dtype=_torch_dtype(dtype), device=blob.device)
     d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
     _lib.check(_lib.lib().kvc_decode(ctypes.byref(d), _ptr(blob), _nbytes(blob), _ptr(out), _stream(stream)))
     return out
@@ -125,11 +153,9 @@ def _workspace(ws, nbytes, device):
 
 def encode_unfused(kv, bits_k, bits_v, group, seed=0, out=None, workspace=None, stream=None):
     """Comparator: :func:`encode` computed by separate kernels through ``workspace``."""
+    L, T, H, D = _kv_shape(kv.shape, "kv")
+    dt = _dtype_name(kv)
     _check_cuda(kv, out)
-    L, two, T, H, D = kv.shape
-    if two != 2:
-        raise ValueError("axis 1 must hold K and V")
-    dt = _TORCH_TO_NAME[kv.dtype]
     total, _ = encoded_size(L, T, H, D, bits_k, bits_v, group, dt)
     if out is None:
         out = torch.empty(total, dtype=torch.uint8, device=kv.device)
@@ -142,10 +168,11 @@ def encode_unfused(kv, bits_k, bits_v, group, seed=0, out=None, workspace=None, 
 
 def decode_unfused(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, workspace=None, stream=None):
     """Comparator: :func:`decode` computed by separate kernels through ``workspace``."""
+    L, T, H, D = _kv_shape(shape, "shape")
+    _check_out(out, shape, _torch_dtype(dtype))
     _check_cuda(blob, out)
-    L, two, T, H, D = shape
     if out is None:
-        out = torch.empty(tuple(shape), dtype=_NAME_TO_TORCH[dtype], device=blob.device)
+        out = torch.empty(tuple(shape), dtype=_torch_dtype(dtype), device=blob.device)
     ws = _workspace(workspace, unfused_workspace_size(L, T, H, D, bits_k, bits_v, group, dtype), blob.device)
     d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
     _lib.check(_lib.lib().kvc_decode_unfused(ctypes.byref(d), _ptr(blob), _nbytes(blob), _ptr(out), _ptr(ws),
@@ -166,11 +193,11 @@ def encode_send(kv, bits_k, bits_v, group, chunk_layers, dst, seed=0, out=None, 
                 copy_stream=None):
     """Encode layer chunks on ``compute_stream`` and copy each finished chunk
     into ``dst`` (a pinned host or device tensor) on ``copy_stream``."""
+    L, T, H, D = _kv_shape(kv.shape, "kv")
+    dt = _dtype_name(kv)
     _check_cuda(kv, out)
     if not dst.is_contiguous():
         raise ValueError("dst must be contiguous")
-    L, two, T, H, D = kv.shape
-    dt = _TORCH_TO_NAME[kv.dtype]
     total, _ = chunked_size(L, T, H, D, bits_k, bits_v, group, chunk_layers, dt)
     if out is None:
         out = torch.empty(total, dtype=torch.uint8, device=kv.device)
@@ -186,16 +213,17 @@ def receive_decode(src, shape, dtype, bits_k, bits_v, group, chunk_layers, seed=
     """Copy layer chunks of ``src`` (a pinned host or device tensor) into
     ``staging`` on ``copy_stream`` and decode each on ``compute_stream``
     into ``out``."""
+    L, T, H, D = _kv_shape(shape, "shape")
+    _check_out(out, shape, _torch_dtype(dtype))
     _check_cuda(staging, out)
     if not src.is_contiguous():
         raise ValueError("src must be contiguous")
-    L, two, T, H, D = shape
     total, _ = chunked_size(L, T, H, D, bits_k, bits_v, group, chunk_layers, dtype)
     if staging is None:
         device = src.device if src.is_cuda else torch.device("cuda", torch.cuda.current_device())
         staging = torch.empty(max(total, 1), dtype=torch.uint8, device=device)
     if out is None:
-        out = torch.empty(tuple(shape), dtype=_NAME_TO_TORCH[dtype], device=staging.device)
+        out = torch.empty(tuple(shape), dtype=_torch_dtype(dtype), device=staging.device)
     d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
     _lib.check(_lib.lib().kvc_receive_decode(ctypes.byref(d), _ptr(src), _nbytes(src), _ptr(staging),
                                              _nbytes(staging), int(chunk_layers), _ptr(out),
@@ -215,11 +243,28 @@ def paged_layout(seq_lens, layers, kv_heads, head_dim, bits_k, bits_v, group, dt
     return offs, total.value
 
 
+def _pool_shape(pool):
+    """(L, NB, BS, H, D) of a [L, 2, NB, BS, H, D] pool."""
+    if pool.dim() != 6 or pool.shape[1] != 2:
+        raise ValueError("pool must have shape [L, 2, NB, BS, H, D], got %s" % list(pool.shape))
+    L, _, NB, BS, H, D = pool.shape
+    return L, NB, BS, H, D
+
+
 def _paged(pool, block_table, seq_lens, out_offsets, err_flag):
-    _check_cuda(block_table, seq_lens, out_offsets, err_flag)
+    """The kernels read seq_lens[r], out_offsets[r] and the first max_blocks
+    entries of row r of block_table for every r < R, and write err_flag[0]:
+    the arrays must hold that much."""
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or out_offsets.dtype != torch.int64:
         raise ValueError("block_table / seq_lens must be int32 and out_offsets int64")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_reqs, max_blocks]")
     R, MB = block_table.shape
+    if tuple(seq_lens.shape) != (R,) or tuple(out_offsets.shape) != (R,):
+        raise ValueError("seq_lens and out_offsets must hold one entry per block_table row (%d)" % R)
+    if err_flag is not None and (err_flag.dtype != torch.int32 or err_flag.numel() < 1):
+        raise ValueError("err_flag must be an int32 tensor of at least one element")
+    _check_cuda(block_table, seq_lens, out_offsets, err_flag)
     return KvcPaged(pool.shape[2], pool.shape[3], R, MB, 0, _ptr(block_table).value,
                     _ptr(seq_lens).value, _ptr(out_offsets).value,
                     _ptr(err_flag).value if err_flag is not None else None)
@@ -228,12 +273,12 @@ def _paged(pool, block_table, seq_lens, out_offsets, err_flag):
 def encode_paged(pool, block_table, seq_lens, out_offsets, total, bits_k, bits_v, group, seed=0,
                  out=None, err_flag=None, stream=None):
     """Encode every request of a [L, 2, NB, BS, H, D] pool into one blob buffer."""
+    L, NB, BS, H, D = _pool_shape(pool)
+    dt = _dtype_name(pool)
+    pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag)
     _check_cuda(pool, out)
-    L, two, NB, BS, H, D = pool.shape
-    dt = _TORCH_TO_NAME[pool.dtype]
     if out is None:
         out = torch.empty(int(total), dtype=torch.uint8, device=pool.device)
-    pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag)
     d = _desc(L, 0, H, D, dt, bits_k, bits_v, group, seed)
     _lib.check(_lib.lib().kvc_encode_paged(ctypes.byref(d), _ptr(pool), ctypes.byref(pg), _ptr(out),
                                            _nbytes(out), _stream(stream)))
@@ -243,10 +288,10 @@ def encode_paged(pool, block_table, seq_lens, out_offsets, total, bits_k, bits_v
 def decode_paged(blob, pool, block_table, seq_lens, out_offsets, bits_k, bits_v, group, seed=0,
                  err_flag=None, stream=None):
     """Decode every request's blob back into the pool slots of its block table."""
-    _check_cuda(blob, pool)
-    L, two, NB, BS, H, D = pool.shape
-    dt = _TORCH_TO_NAME[pool.dtype]
+    L, NB, BS, H, D = _pool_shape(pool)
+    dt = _dtype_name(pool)
     pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag)
+    _check_cuda(blob, pool)
     d = _desc(L, 0, H, D, dt, bits_k, bits_v, group, seed)
     _lib.check(_lib.lib().kvc_decode_paged(ctypes.byref(d), _ptr(blob), _nbytes(blob), ctypes.byref(pg),
                                            _ptr(pool), _stream(stream)))
@@ -255,11 +300,13 @@ def decode_paged(blob, pool, block_table, seq_lens, out_offsets, bits_k, bits_v,
 
 def debug_rotate(kv, seed=0, out=None, stream=None):
     """Rotated values y = H (s * x) / sqrt(D) of the encode path, fp32."""
+    L, T, H, D = _kv_shape(kv.shape, "kv")
+    dt = _dtype_name(kv)
+    _check_out(out, kv.shape, torch.float32)
     _check_cuda(kv, out)
-    L, two, T, H, D = kv.shape
     if out is None:
         out = torch.empty(tuple(kv.shape), dtype=torch.float32, device=kv.device)
-    d = _desc(L, T, H, D, _TORCH_TO_NAME[kv.dtype], 4, 4, 32, seed)
+    d = _desc(L, T, H, D, dt, 4, 4, 32, seed)
     _lib.check(_lib.lib().kvc_debug_rotate(ctypes.byref(d), _ptr(kv), _ptr(out), _stream(stream)))
     return out
 
