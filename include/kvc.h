@@ -166,7 +166,9 @@ kvc_status kvc_encode(const kvc_desc* desc, const void* kv, void* out,
 
 /*
  * Decode a blob written by kvc_encode (same desc) into a contiguous
- * device tensor kv_out [L, 2, T, H, D] of desc->dtype.
+ * device tensor kv_out [L, 2, T, H, D] of desc->dtype.  Its size is not
+ * passed: the caller guarantees L*2*T*H*D elements of desc->dtype, all of
+ * which are written.
  */
 kvc_status kvc_decode(const kvc_desc* desc, const void* in, uint64_t in_bytes,
                       void* kv_out, void* stream);
