@@ -108,7 +108,8 @@ def storage_to_f64(bits, dtype: str) -> np.ndarray:
     if dtype == "fp16":
         return b.view(np.float16).astype(np.float64)
     if dtype == "bf16":
-        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):  # NaN patterns stay NaN; numpy flags their cast
+            return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     raise ValueError(dtype)
 
 
