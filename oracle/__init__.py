@@ -35,7 +35,7 @@ from .signs import splitmix64_outputs, sign_vector, sign_bits_mask
 from .rounding import round_binary, to_fp16, rd16, ru16, rne_bf16, rne_fp16, \
     storage_to_f64, f64_to_storage
 from .rht import hadamard, rotate_raw, rotate, unrotate
-from .quant import fl, div_f32, group_meta, code_values, quantize, pack_codes, unpack_codes, \
+from .quant import group_meta, code_values, nearest_codes, quantize, pack_codes, unpack_codes, \
     dequantize
 from .blob import BlobLayout, blob_layout, encode, decode, EncodeTrace, \
     paged_layout, gather_request, encode_paged, decode_paged, tile_codes, untile_codes, code_offsets
@@ -45,7 +45,7 @@ __all__ = [
     "round_binary", "to_fp16", "rd16", "ru16", "rne_bf16", "rne_fp16",
     "storage_to_f64", "f64_to_storage",
     "hadamard", "rotate_raw", "rotate", "unrotate",
-    "fl", "div_f32", "group_meta", "code_values", "quantize", "pack_codes", "unpack_codes",
+    "group_meta", "code_values", "nearest_codes", "quantize", "pack_codes", "unpack_codes",
     "dequantize",
     "BlobLayout", "blob_layout", "encode", "decode", "EncodeTrace",
     "paged_layout", "gather_request", "encode_paged", "decode_paged",

@@ -38,7 +38,7 @@ import numpy as np
 
 from .rounding import storage_to_f64, f64_to_storage
 from .signs import sign_vector
-from .rht import rotate_raw, unrotate
+from .rht import rotate, unrotate
 from .quant import group_meta, quantize, pack_codes, unpack_codes, dequantize
 
 
@@ -167,9 +167,8 @@ def blob_layout(layers, tokens, kv_heads, head_dim, bits_k, bits_v, group) -> Bl
 @dataclass
 class EncodeTrace:
     """Intermediate values of one oracle encode (indexed [L, 2, T, H, ...])."""
-    y: np.ndarray       # rotated values y = u / sqrt(D), float64 [L,2,T,H,D]
-    u: np.ndarray       # unnormalized rotated values u = H (s * x), float64
-    t: np.ndarray       # pre-rounding code values, float64 [L,2,T,H,D]
+    y: np.ndarray       # rotated values y = H (s * x) / sqrt(D), float64 [L,2,T,H,D]
+    t: np.ndarray       # pre-rounding code values (y - zero) / scale, float64 [L,2,T,H,D]
     q: np.ndarray       # codes, uint8 [L,2,T,H,D]
     scale: np.ndarray   # float16 [L,2,T,H,D/G]
     zero: np.ndarray    # float16 [L,2,T,H,D/G]
@@ -187,8 +186,7 @@ def encode(x_bits: np.ndarray, dtype: str, bits_k: int, bits_v: int, group: int,
     lay = blob_layout(L, T, H, D, bits_k, bits_v, group)
     s = sign_vector(seed, D)
     x = storage_to_f64(x_bits, dtype)
-    u = rotate_raw(x, s)
-    y = u / np.sqrt(D)
+    y = rotate(x, s)
     blob = np.zeros(lay.total, dtype=np.uint8)
     G = group
     t_all = np.zeros_like(y)
@@ -198,9 +196,9 @@ def encode(x_bits: np.ndarray, dtype: str, bits_k: int, bits_v: int, group: int,
     for l in range(L):
         for kv in range(2):
             b = bits_k if kv == 0 else bits_v
-            ul = u[l, kv].reshape(T * H, D)
-            scale, zero = group_meta(ul, G, b)
-            q, t = quantize(ul, scale, zero, G, b)
+            yl = y[l, kv].reshape(T * H, D)
+            scale, zero = group_meta(yl, G, b)
+            q, t = quantize(yl, scale, zero, G, b)
             packed = tile_codes(pack_codes(q, b))
             off = lay.codes_slab(l, kv)
             blob[off:off + packed.size] = packed
@@ -212,7 +210,7 @@ def encode(x_bits: np.ndarray, dtype: str, bits_k: int, bits_v: int, group: int,
             q_all[l, kv] = q.reshape(T, H, D)
             sc_all[l, kv] = scale.reshape(T, H, D // G)
             ze_all[l, kv] = zero.reshape(T, H, D // G)
-    return blob, EncodeTrace(y=y, u=u, t=t_all, q=q_all, scale=sc_all, zero=ze_all)
+    return blob, EncodeTrace(y=y, t=t_all, q=q_all, scale=sc_all, zero=ze_all)
 
 
 def decode(blob: np.ndarray, shape, dtype: str, bits_k: int, bits_v: int, group: int, seed: int):

@@ -1,49 +1,37 @@
 """Per-group asymmetric min/max low-bit quantization and sub-byte packing.
 
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
 The episode notes of *FastKVComp: checking whether high-throughput KV
 compression pays off* (radioguide.fm) name "low-bit quantization" as the
-second stage and say it is the only lossy step; they give no formula.  The
-reading implemented here:
+second stage and say it is the only step that loses information; they give
+no formula.  The reading implemented here, on the rotated values y of one
+head_dim vector (the orthonormal transform's output, float64):
 
   * a group is G consecutive rotated coordinates of one head_dim vector
     (G divides D; groups never span tokens, heads or K/V);
-  * per group, from the unnormalized rotated values u = H (s * x) (so that
-    the rotated value is y = u / sqrt(D)):
-        zero  = RD16(mn)   with mn = min y     (fp16, rounded toward -inf)
-        scale = RU16((mx - zero) / (2**b - 1)), mx = max y  (toward +inf)
-    so every t = (y - zero) / scale lies in [0, 2**b - 1] up to the rounding
-    of the decision arithmetic below, and |y - yhat| <= scale / 2 holds
-    against the stored scale;
+  * per group, with mn = min y and mx = max y over the group:
+        zero  = RD16(mn)                        fp16, rounded toward -inf
+        scale = RU16((mx - zero) / (2**b - 1))  fp16, rounded toward +inf
+    so that every t = (y - zero) / scale lies in [0, 2**b - 1] and
+    |y - yhat| <= scale / 2 holds against the stored scale;
+  * codes: q = the code k in [0, 2**b - 1] whose level zero + k * scale is
+    nearest to y, ties to the even k -- that is, round-half-even of
+    t = (y - zero) / scale, clipped to the code range;
   * a constant group (mx == zero) has scale 0: every code is 0 and the
     group decodes to zero exactly;
-  * codes: q = round-half-even(t);
   * packing: code j of a row sits at bits [b*j, b*j + b) of the row's
     D*b/8 bytes, least significant bits first;
   * dequantization: yhat = zero + q * scale (exact in float64: the operands
     carry 11 + 8 significant bits).
 
-Decision precision.  The meta and the codes are discrete results decided by
-floating-point arithmetic; this oracle takes those decisions in IEEE
-binary32, in the same arithmetic the kernel performs (fl() = round to
-nearest binary32, rs = fl(1 / sqrt(D))):
-
-    mn, mx = fl(min u), fl(max u)
-    zero   = RD16(fl(mn * rs))
-    scale  = RU16(fl(fl(fl(mx * rs) - zero) / (2**b - 1)))
-    inv    = fl(1 / scale)          (0 when scale == 0)
-    a      = fl(inv * rs),  c = fl(-zero * inv)
-    t      = fl(fl(u) * a + c)      (fused multiply-add: one rounding)
-    q      = round-half-even(min(max(t, 0), 2**b - 1))
-
-The clamp never acts on ordinary data (t stays within a few 1e-6 of
-[0, 2**b - 1]); it bounds the code of a degenerate group -- a huge offset
-with a tiny range, where the binary32 rounding of u alone moves t by more
-than one half -- so that a code never spills into its neighbour's bits.
-
-Every binary32 operation is evaluated exactly in float64 (products of two
-binary32 values are exact there) and rounded once; the two divisions are
-rounded correctly by comparing the exact residuals of the three nearest
-binary32 candidates.  The transform itself stays float64.
+Arithmetic: the definition above, evaluated in float64 step by step -- one
+subtraction and one division for the scale, one subtraction and one division
+for t, no reciprocal, no fused multiply-add, no folding of constants.  The
+float64 result equals the exact one except where an exact intermediate lies
+within a few float64 ulps (about 1e-16 relative) of an fp16 grid point or of
+a code boundary k + 1/2; the brute-force twin in ``oracle/scalar.py``
+decides every such comparison exactly and is checked against this module.
 
 A rotated value outside the fp16 range has no representable meta; the
 oracle raises instead of producing infinities.
@@ -61,83 +49,53 @@ def _check(bits: int, D: int, G: int):
         raise ValueError("group must divide head_dim")
 
 
-def fl(x) -> np.ndarray:
-    """Round float64 values to the nearest binary32 value (returned as float64)."""
-    with np.errstate(over="ignore"):
-        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+def _groups(a: np.ndarray, G: int) -> np.ndarray:
+    D = a.shape[-1]
+    return a.reshape(a.shape[:-1] + (D // G, G))
 
 
-def div_f32(num, den) -> np.ndarray:
-    """Correctly rounded binary32 quotient of binary32 operands (den != 0).
-
-    The float64 quotient rounded to binary32 gives a candidate; it and its two
-    binary32 neighbours are compared by the exact residual |num - c * den|
-    (exact in float64: c * den carries at most 48 significant bits), ties to
-    the candidate with an even significand.
-    """
-    num = np.asarray(num, dtype=np.float64)
-    den = np.asarray(den, dtype=np.float64)
-    c0 = (num / den).astype(np.float32)
-    cands = np.stack([np.nextafter(c0, np.float32(-np.inf)), c0, np.nextafter(c0, np.float32(np.inf))])
-    res = np.abs(num - cands.astype(np.float64) * den)
-    best = np.argmin(res, axis=0)
-    # an exact tie between two candidates goes to the even significand
-    r_sorted = np.sort(res, axis=0)
-    tie = r_sorted[0] == r_sorted[1]
-    if np.any(tie):
-        odd = (cands.view(np.uint32) & 1).astype(np.float64)
-        even_pick = np.argmin(np.where(res == r_sorted[0], odd, 2.0), axis=0)
-        best = np.where(tie, even_pick, best)
-    return np.take_along_axis(cands, best[None], axis=0)[0].astype(np.float64)
-
-
-def _rs(D: int) -> float:
-    return float(fl(1.0 / np.sqrt(D)))
-
-
-def group_meta(u: np.ndarray, G: int, bits: int):
+def group_meta(y: np.ndarray, G: int, bits: int):
     """(scale, zero) as float16 arrays of shape (..., D // G).
 
-    u: unnormalized rotated values H (s * x), float64 (..., D).
+    y: rotated values, float64 (..., D).
     """
-    u = np.asarray(u, dtype=np.float64)
-    D = u.shape[-1]
-    _check(bits, D, G)
-    rs = _rs(D)
-    ug = u.reshape(u.shape[:-1] + (D // G, G))
-    mn = fl(ug.min(axis=-1))
-    mx = fl(ug.max(axis=-1))
-    zero = rd16(fl(mn * rs))
-    zf = zero.astype(np.float64)
-    scale = ru16(div_f32(fl(fl(mx * rs) - zf), float(2 ** bits - 1)))
+    y = np.asarray(y, dtype=np.float64)
+    _check(bits, y.shape[-1], G)
+    if y.size and not np.abs(y).max() <= 65504.0:
+        raise OverflowError("rotated values exceed the fp16 range of the meta")
+    yg = _groups(y, G)
+    mn = yg.min(axis=-1) + 0.0       # an exact zero minimum is stored as +0
+    mx = yg.max(axis=-1)
+    zero = rd16(mn)
+    scale = ru16((mx - zero.astype(np.float64)) / float(2 ** bits - 1))
     if not (np.all(np.isfinite(zero)) and np.all(np.isfinite(scale))):
         raise OverflowError("rotated values exceed the fp16 range of the meta")
     return scale, zero
 
 
-def code_values(u: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int) -> np.ndarray:
-    """Pre-rounding code values t (binary32 decision arithmetic), float64 (..., D)."""
-    u = np.asarray(u, dtype=np.float64)
-    D = u.shape[-1]
-    rs = _rs(D)
-    ug = u.reshape(u.shape[:-1] + (D // G, G))
-    s = scale.astype(np.float64)
-    z = zero.astype(np.float64)
-    inv = np.where(s > 0, div_f32(np.ones_like(s), np.where(s > 0, s, 1.0)), 0.0)
-    a = fl(inv * rs)
-    c = fl(-z * inv)
-    t = fl(fl(ug) * a[..., None] + c[..., None])
-    return t.reshape(u.shape)
+def code_values(y: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int) -> np.ndarray:
+    """Pre-rounding code values t = (y - zero) / scale, float64 (..., D).
+
+    Elements of a group with scale 0 get t = 0.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    s = np.asarray(scale).astype(np.float64)[..., None]
+    z = np.asarray(zero).astype(np.float64)[..., None]
+    t = np.where(s > 0, (_groups(y, G) - z) / np.where(s > 0, s, 1.0), 0.0)
+    return t.reshape(y.shape)
 
 
-def quantize(u: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int, bits: int):
-    """Codes q (uint8, same shape as u) and the pre-rounding values t (float64)."""
-    u = np.asarray(u, dtype=np.float64)
-    _check(bits, u.shape[-1], G)
-    t = code_values(u, scale, zero, G)
-    qmax = 2 ** bits - 1
-    q = np.rint(np.clip(t, 0.0, float(qmax)))
-    return q.astype(np.uint8), t
+def nearest_codes(t: np.ndarray, bits: int) -> np.ndarray:
+    """The code nearest to t among 0 .. 2**b - 1, ties to even (uint8)."""
+    return np.clip(np.rint(t), 0.0, float(2 ** bits - 1)).astype(np.uint8)
+
+
+def quantize(y: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int, bits: int):
+    """Codes q (uint8, same shape as y) and the pre-rounding values t (float64)."""
+    y = np.asarray(y, dtype=np.float64)
+    _check(bits, y.shape[-1], G)
+    t = code_values(y, scale, zero, G)
+    return nearest_codes(t, bits), t
 
 
 def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
@@ -170,7 +128,6 @@ def unpack_codes(packed: np.ndarray, bits: int, D: int) -> np.ndarray:
 def dequantize(q: np.ndarray, scale: np.ndarray, zero: np.ndarray, G: int) -> np.ndarray:
     """yhat = zero + q * scale per group, float64 (normalized domain)."""
     q = np.asarray(q)
-    D = q.shape[-1]
-    qg = q.reshape(q.shape[:-1] + (D // G, G)).astype(np.float64)
-    yhat = zero.astype(np.float64)[..., None] + qg * scale.astype(np.float64)[..., None]
+    qg = _groups(q, G).astype(np.float64)
+    yhat = np.asarray(zero).astype(np.float64)[..., None] + qg * np.asarray(scale).astype(np.float64)[..., None]
     return yhat.reshape(q.shape)

@@ -37,12 +37,18 @@ def sample_vectors(p, rng, n_random=1500):
 
 
 def check_sampled_encode(p, x_gpu, blob_gpu, idx):
-    """Criteria (2) and (3) on sampled vectors of a full-size contiguous encode."""
+    """Criteria (2) and (3) on sampled vectors of a full-size contiguous encode.
+
+    Returns (CodeReport, reference): reference[i] is the oracle's decode (storage
+    bits [D]) of vector idx[i] from its own encode with the differences that
+    criteria (2) and (3) allow taken from the GPU -- what criterion (4)
+    compares the GPU's decode of that vector with."""
     D = p.head_dim
     rows = p.tokens * p.kv_heads
     lay = oracle.blob_layout(p.layers, p.tokens, p.kv_heads, D, p.bits_k, p.bits_v, p.group)
     xs = inputs.as_u16(x_gpu.view(-1, D)[torch.from_numpy(idx).to(x_gpu.device)])
     rep = parity.CodeReport()
+    reference = np.zeros((len(idx), D), dtype=np.uint16)
     for kv in (0, 1):
         sel = np.nonzero((idx // rows) % 2 == kv)[0]
         if not len(sel):
@@ -62,8 +68,10 @@ def check_sampled_encode(p, x_gpu, blob_gpu, idx):
         mi = (meta_off[:, None] + torch.arange(ng * 4)[None, :]).to(dev)
         codes = blob_gpu[ci].cpu().numpy()
         meta = blob_gpu[mi].cpu().numpy().view("<u2").reshape(len(v), ng, 2)
-        rep.merge(parity.check_rows(xs[sel], p.dtype, b, p.group, p.seed, codes, meta))
-    return rep
+        res = parity.check_rows(xs[sel], p.dtype, b, p.group, p.seed, codes, meta)
+        rep.merge(res.report)
+        reference[sel] = parity.decode_rows_ref(res, p.dtype, p.group, p.seed)
+    return rep, reference
 
 
 def meta_scales(blob_gpu, lay):

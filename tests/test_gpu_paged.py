@@ -69,11 +69,15 @@ def test_paged_matches_oracle(D, dtype, bk, bv, G, H, lens):
     assert gpu_util.canaries_intact(whole)
     blob = out.cpu().numpy()
     pool_b = inputs.as_u16(pool)
-    oblob, _, _ = oracle.encode_paged(pool_b, table, lens, dtype, bk, bv, G, p.seed)
+    # the oracle's paged blob with the differences criteria (2) and (3) allow
+    # taken from the GPU: what criterion (4) decodes as the reference
+    oblob = np.zeros(total, dtype=np.uint8)
     for r, n in enumerate(lens):
         x = oracle.gather_request(pool_b, table[r], int(n))
-        sub = blob[offs[r]:offs[r] + oracle.blob_layout(p.layers, int(n), H, D, bk, bv, G).total]
-        parity.check_blob(x, sub, dtype, bk, bv, G, p.seed)
+        size = oracle.blob_layout(p.layers, int(n), H, D, bk, bv, G).total
+        sub = blob[offs[r]:offs[r] + size]
+        res = parity.check_blob(x, sub, dtype, bk, bv, G, p.seed)
+        oblob[offs[r]:offs[r] + size] = res.blob
     # decode into a pool filled with a sentinel: used slots decoded, the rest untouched
     _say("paged decode", p.name)
     sentinel = torch.full(pool.shape, 7.0, dtype=pool.dtype, device=DEV)
@@ -153,6 +157,7 @@ def test_paged_full_size_sampled():
     rng = np.random.default_rng(3)
     rep = parity.CodeReport()
     D, H, BS = p.head_dim, p.kv_heads, p.block_size
+    sampled = []   # (request, layer, K/V, rows, reference decode of those rows)
     for r in rng.choice(len(lens), 6, replace=False).tolist() + [int(np.argmin(lens)), int(np.argmax(lens))]:
         n = int(lens[r])
         lay = oracle.blob_layout(p.layers, n, H, D, p.bits_k, p.bits_v, p.group)
@@ -166,13 +171,24 @@ def test_paged_full_size_sampled():
                 rows = (toks[:, None] * H + np.arange(H)[None, :]).reshape(-1)
                 codes, meta = parity.blob_rows(sub, lay, int(l), kv, rows)
                 b = p.bits_k if kv == 0 else p.bits_v
-                rep.merge(parity.check_rows(xb, p.dtype, b, p.group, p.seed, codes, meta))
+                res = parity.check_rows(xb, p.dtype, b, p.group, p.seed, codes, meta)
+                rep.merge(res.report)
+                sampled.append((r, int(l), kv, toks, parity.decode_rows_ref(res, p.dtype, p.group, p.seed)))
     _say("  sampled paged codes vs oracle:", rep)
     _say("paged full size: decode")
     dst = torch.zeros_like(pool)
     kvc.decode_paged(out, dst, bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed, err_flag=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
+    # criterion (4) on the sampled vectors: the GPU decode against the oracle's
+    # decode of its own encode (allowed differences substituted)
+    got_s, ref_s = [], []
+    for r, l, kv, toks, ref in sampled:
+        blk = torch.from_numpy(table[r][toks // BS].astype(np.int64)).to(DEV)
+        got_s.append(inputs.as_u16(dst[l, kv][blk, torch.from_numpy(toks % BS).to(DEV)]).reshape(-1, D))
+        ref_s.append(ref)
+    rr = parity.check_decode(np.concatenate(got_s), np.concatenate(ref_s), p.dtype, axis_slices=(1,))
+    _say("  sampled paged decode vs the oracle's decode: rrms %.3g" % rr)
     # every vector of a few requests: ||x - xhat|| <= sqrt(D) * max group scale / 2
     # (+ the bf16 rounding of xhat); sampled vectors: GPU decode == oracle decode
     # of the GPU's codes

@@ -1,5 +1,6 @@
-"""Pins of quantization and packing: error bound, exact grids, constant groups,
-brute force on tiny tensors, hand-worked packing."""
+"""Pins of quantization and packing: the exact definition of the meta and the
+codes (brute force in exact arithmetic), error bound, exact grids, ties,
+constant groups, degenerate groups, hand-worked packing."""
 import itertools
 from fractions import Fraction
 
@@ -11,63 +12,117 @@ from oracle import scalar
 from conftest import golden_rows
 
 
-def _rotated_raw(rng, n, D, spread=1.0, offset=0.0):
+def _rotated(rng, n, D, spread=1.0, offset=0.0):
     x = rng.normal(size=(n, D)) * spread + offset
-    return oracle.rotate_raw(x, oracle.sign_vector(5, D))
+    return oracle.rotate(x, oracle.sign_vector(5, D))
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 def test_error_bound_and_code_range(bits, G):
+    """Spec invariant, exact in float64: 0 <= t <= 2^b - 1 and
+    |y - yhat| <= scale / 2 for every element, zero <= min y and
+    zero + (2^b - 1) scale >= max y for every group."""
     rng = np.random.default_rng(bits * 1000 + G)
     D = 128
     qmax = 2 ** bits - 1
-    u = np.concatenate([_rotated_raw(rng, 2000, D), _rotated_raw(rng, 200, D, spread=30.0)])
-    y = u / np.sqrt(D)
-    scale, zero = oracle.group_meta(u, G, bits)
-    q, t = oracle.quantize(u, scale, zero, G, bits)
-    slack = 1e-6 * (qmax + 1)   # binary32 rounding of t: a few ulps of max(|t|, |zero/scale|)
-    assert t.min() >= -slack and t.max() <= qmax + slack
+    y = np.concatenate([_rotated(rng, 2000, D), _rotated(rng, 200, D, spread=30.0),
+                        _rotated(rng, 200, D, spread=0.01, offset=3.0)])
+    scale, zero = oracle.group_meta(y, G, bits)
+    q, t = oracle.quantize(y, scale, zero, G, bits)
+    eps = 1e-12
+    assert t.min() >= -eps and t.max() <= qmax * (1 + eps)
     yhat = oracle.dequantize(q, scale, zero, G)
     sc = np.repeat(scale.astype(np.float64), G, axis=-1)
-    assert np.all(np.abs(y - yhat) <= sc * (0.5 + slack))
-    # the stored zero is a lower bound of its group (up to one binary32 rounding
-    # of the normalized minimum), zero + (2^b-1)*scale an upper one
+    assert np.all(np.abs(y - yhat) <= sc * (0.5 + eps))
     yg = y.reshape(len(y), -1, G)
-    lo = yg.min(-1)
-    hi = yg.max(-1)
-    assert np.all(zero.astype(np.float64) <= lo + 2.0 ** -22 * np.abs(lo))
-    assert np.all(zero.astype(np.float64) + qmax * scale.astype(np.float64) >= hi - 2.0 ** -22 * np.abs(hi))
+    assert np.all(zero.astype(np.float64) <= yg.min(-1))
+    assert np.all(zero.astype(np.float64) + qmax * scale.astype(np.float64) >= yg.max(-1))
+    # and the meta is the tightest fp16 pair: one fp16 step up for zero, or
+    # down for scale, breaks the bounds above
+    z_up = np.nextafter(zero, np.float16(np.inf)).astype(np.float64)
+    assert np.all(z_up > yg.min(-1))
+    s_dn = np.nextafter(scale, np.float16(-np.inf)).astype(np.float64)
+    pos = scale > 0
+    assert np.all((zero.astype(np.float64) + qmax * s_dn < yg.max(-1))[pos])
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_codes_are_the_nearest_level(bits):
+    """Against an argmin over every code level (float64 brute force): the code
+    is the level nearest to y; equal distances only at exact midpoints."""
+    rng = np.random.default_rng(40 + bits)
+    G, D = 32, 64
+    y = _rotated(rng, 300, D) * rng.uniform(0.1, 10, size=(300, 1))
+    scale, zero = oracle.group_meta(y, G, bits)
+    q, _ = oracle.quantize(y, scale, zero, G, bits)
+    levels = zero.astype(np.float64)[..., None] + np.arange(2 ** bits) * scale.astype(np.float64)[..., None]
+    dist = np.abs(y.reshape(300, -1, G)[..., None] - levels[..., None, :])      # [n, groups, G, codes]
+    best = dist.argmin(-1).reshape(y.shape)
+    assert np.array_equal(q, best.astype(np.uint8))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_codes_match_exact_brute_force(bits):
+    """Random y, meta and codes against the exact twin (y taken as exact
+    rationals, D = 1): RD16 / RU16 by search over every fp16 value and the
+    code by exact argmin over all 2^b levels."""
+    rng = np.random.default_rng(70 + bits)
+    G = 16
+    y = rng.normal(size=(12, G)) * np.exp(rng.uniform(-6, 6, size=(12, 1))) + rng.normal(size=(12, 1))
+    scale, zero = oracle.group_meta(y, G, bits)
+    q, _ = oracle.quantize(y, scale, zero, G, bits)
+    qmax = 2 ** bits - 1
+    for r in range(len(y)):
+        u = [Fraction(float(v)) for v in y[r]]
+        z = scalar.rd16_exact(min(u), 1)
+        s = scalar.ru16_scale(max(u), 1, z, qmax)
+        assert z == Fraction(float(zero[r, 0])) and s == Fraction(float(scale[r, 0]))
+        assert [scalar.nearest_code(v, 1, z, s, qmax) for v in u] == q[r].tolist()
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_exact_ties_go_to_the_even_code(bits):
+    """y exactly halfway between two levels: both the numpy oracle and the twin
+    pick the even code (round half to even)."""
+    qmax = 2 ** bits - 1
+    z, s = Fraction(-3, 4), Fraction(3, 64)          # both exact in fp16
+    for k in range(qmax):
+        mid = z + (k + Fraction(1, 2)) * s            # exact in float64 too
+        want = k if k % 2 == 0 else k + 1
+        assert scalar.nearest_code(mid, 1, z, s, qmax) == want
+        t = oracle.code_values(np.array([[float(mid)]]), np.array([[np.float16(float(s))]]),
+                               np.array([[np.float16(float(z))]]), 1)
+        assert t[0, 0] == k + 0.5
+        assert oracle.nearest_codes(t, bits)[0, 0] == want
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_degenerate_groups_stay_in_range(bits):
-    """Huge offset, tiny range: binary32 error in t is ~|y / scale| * 2^-23, the
-    clamp keeps codes in [0, 2^b - 1], and the error bound holds up to it."""
+    """Huge offset, tiny range: the exact definition keeps every code in
+    [0, 2^b - 1] and the error bound |y - yhat| <= scale / 2 holds."""
     rng = np.random.default_rng(bits)
     D, G = 128, 32
     qmax = 2 ** bits - 1
     y = np.concatenate([1000.0 + 0.01 * rng.random((200, D)), -700.0 + 0.003 * rng.random((200, D)),
                         np.full((4, D), 3.0) + np.linspace(0, 1e-5, D)])
-    u = y * np.sqrt(D)
-    scale, zero = oracle.group_meta(u, G, bits)
-    q, t = oracle.quantize(u, scale, zero, G, bits)
-    assert q.max() <= qmax
+    scale, zero = oracle.group_meta(y, G, bits)
+    q, t = oracle.quantize(y, scale, zero, G, bits)
+    assert q.max() <= qmax and t.min() >= -1e-9 and t.max() <= qmax + 1e-9
     yhat = oracle.dequantize(q, scale, zero, G)
     sc = np.repeat(scale.astype(np.float64), G, axis=-1)
-    slack = np.abs(y) * 2.0 ** -21
-    assert np.all(np.abs(y - yhat) <= sc / 2 + slack)
+    assert np.all(np.abs(y - yhat) <= sc / 2 + np.abs(y) * 2.0 ** -50)
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_exact_grid_groups_round_trip(bits):
-    """D = 64 (1/sqrt(D) = 1/8 exactly): y = zero + k * scale on fp16 grids."""
+    """y = zero + k * scale on fp16 grids, with the extreme codes present:
+    the meta is (scale, zero) again, the codes are k and yhat == y."""
     rng = np.random.default_rng(bits)
     G, D = 32, 64
-    rows = []
-    codes = []
+    rows, codes, metas = [], [], []
     for _ in range(50):
-        row, crow = [], []
+        row, crow, mrow = [], [], []
         for g in range(D // G):
             z = float(np.float16(rng.uniform(-8, 8)))
             s = float(np.float16(rng.uniform(0.01, 0.5)))
@@ -76,54 +131,43 @@ def test_exact_grid_groups_round_trip(bits):
             rng.shuffle(k)
             row.extend(z + k * s)
             crow.extend(k)
+            mrow.append((s, z))
         rows.append(row)
         codes.append(crow)
+        metas.append(mrow)
     y = np.array(rows)
-    u = y * 8.0
-    scale, zero = oracle.group_meta(u, G, bits)
-    q, _ = oracle.quantize(u, scale, zero, G, bits)
+    scale, zero = oracle.group_meta(y, G, bits)
+    assert np.array_equal(scale.astype(np.float64), np.array([[m[0] for m in r] for r in metas]))
+    assert np.array_equal(zero.astype(np.float64), np.array([[m[1] for m in r] for r in metas]))
+    q, _ = oracle.quantize(y, scale, zero, G, bits)
     assert np.array_equal(q, np.array(codes, dtype=np.uint8))
     assert np.array_equal(oracle.dequantize(q, scale, zero, G), y)
 
 
 def test_constant_groups():
-    G, D = 64, 128
-    u = np.zeros((3, D))
-    u[1] = 0.375 * 8.0           # D=64 below: 1/sqrt(D) = 1/8
-    u[2, :64] = -3.25 * 8.0
-    u[2, 64:] = np.linspace(0, 8, 64)
-    u = u[:, :64].copy(), u[:, 64:].copy()
-    u = np.concatenate([u[0], u[1]], axis=1)[:, :64]
-    uu = np.zeros((3, 64))
-    uu[1] = 0.375 * 8.0
-    uu[2, :32] = -3.25 * 8.0
-    uu[2, 32:] = np.linspace(0, 8, 32)
-    scale, zero = oracle.group_meta(uu, 32, 4)
-    q, t = oracle.quantize(uu, scale, zero, 32, 4)
-    assert scale[0, 0] == 0 and scale[1, 0] == 0 and scale[2, 0] == 0
+    """Constant groups (all-zero vectors among them) get scale 0 and codes 0,
+    and decode to the stored zero exactly; a zero minimum is stored as +0."""
+    y = np.zeros((3, 64))
+    y[1] = 0.375
+    y[2, :32] = -3.25
+    y[2, 32:] = np.linspace(0, 1, 32)
+    scale, zero = oracle.group_meta(y, 32, 4)
+    q, t = oracle.quantize(y, scale, zero, 32, 4)
+    assert np.all(scale[:2] == 0) and scale[2, 0] == 0 and scale[2, 1] > 0
     assert np.all(q[:2] == 0) and np.all(q[2, :32] == 0)
-    assert np.array_equal(oracle.dequantize(q, scale, zero, 32)[:2], uu[:2] / 8.0)
+    assert np.array_equal(oracle.dequantize(q, scale, zero, 32)[:2], y[:2])
     assert np.all(oracle.dequantize(q, scale, zero, 32)[2, :32] == -3.25)
-    assert scale[2, 1] > 0
+    assert zero[0, 0].view(np.uint16) == 0 and zero[2, 1].view(np.uint16) == 0
+    neg = oracle.group_meta(-np.zeros((1, 64)), 32, 4)[1]
+    assert np.all(neg.view(np.uint16) == 0)
 
 
-def test_binary32_helpers_are_exact():
-    """fl / div_f32 / the fused multiply-add against exact rational rounding."""
-    rng = np.random.default_rng(5)
-    a = rng.normal(size=3000) * np.exp(rng.uniform(-20, 20, 3000))
-    assert np.array_equal(oracle.fl(a), np.array([scalar.f32_round(float(v)) for v in a]))
-    num = oracle.fl(rng.normal(size=3000) * 100)
-    den = oracle.fl(np.abs(rng.normal(size=3000)) * 10 + 1e-3)
-    den[:500] = np.float16(np.abs(rng.normal(size=500))).astype(np.float64) + 2.0 ** -10
-    num[:500] = 1.0
-    got = oracle.div_f32(num, den)
-    want = [scalar.f32_round(Fraction(float(n)) / Fraction(float(d))) for n, d in zip(num, den)]
-    assert np.array_equal(got, np.array(want))
-    x, y, z = oracle.fl(rng.normal(size=(3, 3000)) * 50)
-    fused = oracle.fl(x * y + z)
-    want = [scalar.f32_round(Fraction(float(p)) * Fraction(float(q)) + Fraction(float(r)))
-            for p, q, r in zip(x, y, z)]
-    assert np.array_equal(fused, np.array(want))
+def test_overflowing_meta_raises():
+    with pytest.raises(OverflowError):
+        oracle.group_meta(np.full((1, 32), 70000.0), 32, 4)
+    # inside the range the widest group still has a finite scale (131008 / 3)
+    sc, ze = oracle.group_meta(np.concatenate([np.full((1, 16), -65504.0), np.full((1, 16), 65504.0)], 1), 32, 2)
+    assert float(ze[0, 0]) == -65504.0 and float(sc[0, 0]) == float(np.float16(131008 / 3 + 16))
 
 
 def test_packing_worked_examples():
@@ -147,15 +191,16 @@ def test_every_byte_pattern_round_trips(bits):
 
 @pytest.mark.parametrize("bits,G,seed", list(itertools.product([2, 4, 8], [4, 8], [0, 1, 99])))
 def test_brute_force_4x8(bits, G, seed):
-    """4 rows x D=8: the numpy oracle equals the brute-force scalar twin."""
+    """4 rows x D=8: the float64 oracle equals the exact brute-force twin --
+    meta, codes, packed bytes and the decoded bit patterns."""
     rng = np.random.default_rng(bits * 100 + G * 10 + seed)
     for dt in ("bf16", "fp16"):
         xb = oracle.f64_to_storage(rng.normal(size=(4, 8)) * 3, dt)
         x = oracle.storage_to_f64(xb, dt)
         s = oracle.sign_vector(seed, 8)
-        u = oracle.rotate_raw(x, s)
-        scale, zero = oracle.group_meta(u, G, bits)
-        q, _ = oracle.quantize(u, scale, zero, G, bits)
+        y = oracle.rotate(x, s)
+        scale, zero = oracle.group_meta(y, G, bits)
+        q, _ = oracle.quantize(y, scale, zero, G, bits)
         packed = oracle.pack_codes(q, bits)
         sp, sm, sc = scalar.encode_rows(x.tolist(), 8, G, bits, seed)
         assert np.array_equal(packed, np.array(sp, dtype=np.uint8))
@@ -174,10 +219,9 @@ def test_reconstruction_error_equals_rotated_error():
     D, G, bits = 128, 64, 4
     x = rng.normal(size=(300, D))
     s = oracle.sign_vector(2, D)
-    u = oracle.rotate_raw(x, s)
-    y = u / np.sqrt(D)
-    scale, zero = oracle.group_meta(u, G, bits)
-    q, _ = oracle.quantize(u, scale, zero, G, bits)
+    y = oracle.rotate(x, s)
+    scale, zero = oracle.group_meta(y, G, bits)
+    q, _ = oracle.quantize(y, scale, zero, G, bits)
     yhat = oracle.dequantize(q, scale, zero, G)
     xhat = oracle.unrotate(yhat, s)
     ex = np.linalg.norm(x - xhat, axis=1)
