@@ -9,15 +9,26 @@ tensor.  Inputs are resident in HBM before the timed region starts; two
 buffer sets alternate between steps so that consecutive steps do not reuse
 cache-resident data.  Prints ONE JSON line.
 
+Warm-up: after an idle period the GPU needs some hundreds of milliseconds
+of load to reach its steady clocks, so before the W warm-up steps the
+headline workload runs encode + decode back to back for --prewarm-s seconds
+of wall time (reported as "prewarm"), whatever W is; the copy probe runs
+after that.
+
 Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
-  value          raw bytes / (encode + decode time), GB/s (1e9)
-  encode/decode  per-kernel raw GB/s and algorithmic-HBM GB/s (bytes read
+  value          raw bytes per step / ms_per_step, GB/s (1e9); ms_per_step is
+                 the wall time of the K timed steps / K (device synchronized
+                 on both sides)
+  encode/decode  per-kernel time (HIP events on the launch stream, mean,
+                 median, min), raw GB/s and algorithmic-HBM GB/s (bytes read
                  plus bytes written) as a fraction of the 8 TB/s peak
   roofline       the dominant kernel: algorithmic bytes per launch / mean
-                 launch time (HIP events on the launch stream, recorded
-                 without a system-scope fence), vs 8 TB/s
+                 launch time, vs 8 TB/s
   break_even     encode + decode time vs the wire time the compression saves
                  at 100 and 400 Gbit/s
+  workloads      every other named workload (tiny as latency; the 8B-32k,
+                 70B-16k and paged ones as encode / decode fractions of the
+                 peak and break-even), same event protocol, fewer steps
   pipeline       per-layer chunked encode overlapped with the copy of each
                  chunk to pinned host memory (PCIe standing in for the link),
                  and copy-in overlapped with decode, against the raw copy and
@@ -25,7 +36,9 @@ Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
   unfused        the same encode / decode run as separate kernels that pass
                  fp32 / byte intermediates through HBM (contiguous workloads):
                  times, stage bytes, and the fused kernels' speedup over them
-  cpu_baseline   the CPU oracle on a bounded sample of the same workload
+  cpu_baseline   the CPU oracle on a bounded sample of the same workload,
+                 and the parity of the GPU's encode / decode of one sample
+                 chunk against it (boundary flips counted)
 """
 
 import argparse
@@ -92,18 +105,22 @@ class TimingEvents:
         self._ev = []
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prewarm-s", type=float, default=1.0,
+                    help="seconds of back-to-back encode + decode before the warm-up steps")
     ap.add_argument("--workload", default="llama3_8b_4k")
+    ap.add_argument("--other-steps", type=int, default=10,
+                    help="timed steps of each other workload (0: skip them)")
     ap.add_argument("--cpu-sample-chunks", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true", help="skip the separate-kernel comparator")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the transfer legs (they launch the fused kernels on layer chunks)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 # the sources the fused encode / decode kernels are built from
@@ -165,7 +182,7 @@ def cpu_baseline(p, chunks):
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = "1"
     workers = max(1, min(16, os.cpu_count() or 1, chunks))
-    tokens = max(1, (1 << 19) // (p.kv_heads * p.head_dim))  # 2 x 2^19 elements per chunk
+    tokens = sample_tokens(p)
     jobs = [(p.name, i % max(1, p.layers), tokens) for i in range(chunks)]
     ctx = mp.get_context("spawn")
     t0 = time.perf_counter()
@@ -180,6 +197,33 @@ def cpu_baseline(p, chunks):
                   "%d processes x 1 BLAS thread" % (chunks, tokens, p.kv_heads, p.head_dim, p.dtype,
                                                     raw / 2 ** 20, cpu, workers),
     }
+
+
+def sample_tokens(p):
+    return max(1, (1 << 19) // (p.kv_heads * p.head_dim))   # 2 x 2^19 elements per chunk
+
+
+def sample_parity(kvc, p, dev, layer=0):
+    """Criteria (2)-(4) of the GPU encode / decode of one oracle sample chunk
+    (layer `layer`, both K and V, the chunk cpu_baseline times) against the
+    oracle: meta and codes by the boundary rule, flips counted, and the
+    decode's relative RMS against the oracle's decode."""
+    import torch
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity
+    from kv_cache_compression_kvc_amd import inputs
+    tokens = sample_tokens(p)
+    x = torch.stack([inputs.kv_chunk(p, layer, kv, (tokens,), device="cpu") for kv in (0, 1)])[None]
+    xg = x.to(dev)
+    blob = kvc.encode(xg, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    xd = kvc.decode(blob, x.shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    torch.cuda.synchronize()
+    res = parity.check_blob(inputs.as_u16(x), blob.cpu().numpy(), p.dtype, p.bits_k, p.bits_v, p.group, p.seed)
+    rr = parity.check_decode(inputs.as_u16(xd), res.reference, p.dtype)
+    r = res.report.as_dict()
+    r.update(decode_rrms=rr, chunk="[1,2,%d,%d,%d] of layer %d" % (tokens, p.kv_heads, p.head_dim, layer),
+             rule="codes equal the nearest level except within 1e-5 of a rounding boundary (counted)")
+    return r
 
 
 # ---------------------------------------------------------------------------
@@ -336,6 +380,151 @@ def copy_probe(kvc, dev, stream, reps=40):
     return gbps
 
 
+class Leg:
+    """Device inputs and encode / decode closures of one workload."""
+
+    def __init__(self, kvc, p, dev, nsets):
+        import torch
+        from kv_cache_compression_kvc_amd import inputs
+        L, H, D = p.layers, p.kv_heads, p.head_dim
+        self.p, self.nsets = p, nsets
+        if p.paged:
+            lens = inputs.request_lengths(p)
+            table, nb = inputs.block_table(p, lens)
+            offs, total = kvc.paged_layout(lens, L, H, D, p.bits_k, p.bits_v, p.group, p.dtype)
+            self.src = [inputs.make_pool(p, nb, device=dev) for _ in range(nsets)]
+            self.outs = [torch.empty(total, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+            self.dsts = [torch.empty_like(self.src[0]) for _ in range(nsets)]
+            self.bt, self.sl, self.of = (torch.from_numpy(a).to(dev) for a in (table, lens, offs))
+            self.total = total
+            tokens = int(lens.sum())
+            self.raw_bytes = L * 2 * tokens * H * D * 2
+            self.config = {"workload": p.name, "layers": L, "requests": len(lens), "tokens": tokens,
+                           "kv_heads": H, "head_dim": D, "storage": p.dtype, "bits_k": p.bits_k,
+                           "bits_v": p.bits_v, "group": p.group,
+                           "layout": "paged, %d-token blocks" % p.block_size}
+        else:
+            self.src = [inputs.make_kv(p, device=dev) for _ in range(nsets)]
+            total, _ = kvc.encoded_size(L, p.tokens, H, D, p.bits_k, p.bits_v, p.group, p.dtype)
+            self.outs = [torch.empty(total, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+            self.dsts = [torch.empty_like(self.src[0]) for _ in range(nsets)]
+            self.total = total
+            self.raw_bytes = self.src[0].numel() * 2
+            self.config = {"workload": p.name, "shape": [L, 2, p.tokens, H, D], "storage": p.dtype,
+                           "bits_k": p.bits_k, "bits_v": p.bits_v, "group": p.group, "layout": "contiguous"}
+        self.enc_bytes = self.total
+        self.algo_bytes = self.raw_bytes + self.enc_bytes   # read + write of one encode (or decode)
+        self.kvc = kvc
+
+    def enc(self, i):
+        p, k = self.p, i % self.nsets
+        if p.paged:
+            self.kvc.encode_paged(self.src[k], self.bt, self.sl, self.of, self.total, p.bits_k, p.bits_v, p.group,
+                                  seed=p.seed, out=self.outs[k])
+        else:
+            self.kvc.encode(self.src[k], p.bits_k, p.bits_v, p.group, seed=p.seed, out=self.outs[k])
+
+    def dec(self, i):
+        p, k = self.p, i % self.nsets
+        if p.paged:
+            self.kvc.decode_paged(self.outs[k], self.dsts[k], self.bt, self.sl, self.of, p.bits_k, p.bits_v, p.group,
+                                  seed=p.seed)
+        else:
+            self.kvc.decode(self.outs[k], self.src[k].shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed,
+                            out=self.dsts[k])
+
+    def prewarm(self, seconds):
+        """Encode + decode back to back for `seconds` of wall time; returns the steps run."""
+        import torch
+        n, t0 = 0, time.perf_counter()
+        while True:
+            for _ in range(8):
+                self.enc(n)
+                self.dec(n)
+                n += 1
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return n
+
+    def timed(self, steps, stream):
+        """K steps between device synchronizations: (wall s, encode ms list, decode ms list)."""
+        import torch
+        ev = TimingEvents(3 * steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev.record(3 * i, stream)
+            self.enc(i)
+            ev.record(3 * i + 1, stream)
+            self.dec(i)
+            ev.record(3 * i + 2, stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        enc_ms = [ev.ms(3 * i, 3 * i + 1) for i in range(steps)]
+        dec_ms = [ev.ms(3 * i + 1, 3 * i + 2) for i in range(steps)]
+        ev.close()
+        return wall, enc_ms, dec_ms
+
+    def close(self):
+        import torch
+        del self.src, self.outs, self.dsts
+        torch.cuda.empty_cache()
+
+
+def _stats(ms):
+    srt = sorted(ms)
+    return sum(ms) / len(ms), srt[len(srt) // 2], srt[0]
+
+
+def kernel_summary(leg, ms, copy_gbps=None):
+    mean, med, mn = _stats(ms)
+    t = mean / 1e3
+    alg = leg.algo_bytes / t / 1e9
+    out = {"raw_GBps": leg.raw_bytes / t / 1e9, "hbm_GBps": alg, "frac_hbm_peak": alg / HBM_PEAK_GBPS,
+           "frac_hbm_peak_median": leg.algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS,
+           "ms": mean, "ms_median": med, "ms_min": mn}
+    if copy_gbps:
+        out["frac_copy_probe"] = alg / copy_gbps
+    return out
+
+
+def break_even(leg, t_enc, t_dec):
+    saved = leg.raw_bytes - leg.enc_bytes
+    be = {}
+    for gbit in (100, 400):
+        wire_saved_s = saved * 8 / (gbit * 1e9)
+        be["%dGbit" % gbit] = {"wire_time_saved_ms": wire_saved_s * 1e3,
+                               "encode_plus_decode_ms": (t_enc + t_dec) * 1e3,
+                               "pays": (t_enc + t_dec) < wire_saved_s,
+                               "required_raw_GBps_each": 2 * gbit / 8 / (1 - leg.enc_bytes / leg.raw_bytes)}
+    return be
+
+
+def other_workload(kvc, name, dev, stream, steps):
+    """The same protocol on another workload: a short pre-warm, 3 warm-up
+    steps, `steps` timed steps; tiny reports latency."""
+    from kv_cache_compression_kvc_amd import presets
+    p = presets.preset(name)
+    leg = Leg(kvc, p, dev, nsets=1)
+    leg.prewarm(0.05)
+    for i in range(3):
+        leg.enc(i)
+        leg.dec(i)
+    wall, enc_ms, dec_ms = leg.timed(steps, stream)
+    e, d = kernel_summary(leg, enc_ms), kernel_summary(leg, dec_ms)
+    out = {"config": leg.config, "steps": steps, "bytes": {"raw": leg.raw_bytes, "encoded": leg.enc_bytes}}
+    if name == "tiny":   # launch-bound: latency, not a roofline figure
+        out.update(encode_us={"mean": e["ms"] * 1e3, "median": e["ms_median"] * 1e3, "min": e["ms_min"] * 1e3},
+                   decode_us={"mean": d["ms"] * 1e3, "median": d["ms_median"] * 1e3, "min": d["ms_min"] * 1e3})
+    else:
+        out.update(encode=e, decode=d, ms_per_step=wall / steps * 1e3,
+                   raw_GBps_step=leg.raw_bytes / (wall / steps) / 1e9,
+                   traffic={"encode": counter_traffic(name, "encode"), "decode": counter_traffic(name, "decode")})
+    out["break_even"] = break_even(leg, e["ms"] / 1e3, d["ms"] / 1e3)
+    leg.close()
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -347,108 +536,42 @@ def main():
 
     import torch
     import kv_cache_compression_kvc_amd as kvc
-    from kv_cache_compression_kvc_amd import presets, inputs
+    from kv_cache_compression_kvc_amd import presets
 
     p = presets.preset(a.workload)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    D, H, L = p.head_dim, p.kv_heads, p.layers
-    nsets = 2
-
-    if p.paged:
-        lens = inputs.request_lengths(p)
-        table, nb = inputs.block_table(p, lens)
-        offs, total = kvc.paged_layout(lens, L, H, D, p.bits_k, p.bits_v, p.group, p.dtype)
-        pools = [inputs.make_pool(p, nb, device=dev) for _ in range(nsets)]
-        outs = [torch.empty(total, dtype=torch.uint8, device=dev) for _ in range(nsets)]
-        dsts = [torch.empty_like(pools[0]) for _ in range(nsets)]
-        bt = torch.from_numpy(table).to(dev)
-        sl = torch.from_numpy(lens).to(dev)
-        of = torch.from_numpy(offs).to(dev)
-        tokens = int(lens.sum())
-        raw_bytes = L * 2 * tokens * H * D * 2
-        enc_bytes = total
-
-        def enc(i):
-            kvc.encode_paged(pools[i], bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=outs[i])
-
-        def dec(i):
-            kvc.decode_paged(outs[i], dsts[i], bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed)
-        workload = {"workload": p.name, "layers": L, "requests": len(lens), "tokens": tokens,
-                    "kv_heads": H, "head_dim": D, "storage": p.dtype, "bits_k": p.bits_k,
-                    "bits_v": p.bits_v, "group": p.group, "layout": "paged, 16-token blocks"}
-    else:
-        xs = [inputs.make_kv(p, device=dev) for _ in range(nsets)]
-        total, _ = kvc.encoded_size(L, p.tokens, H, D, p.bits_k, p.bits_v, p.group, p.dtype)
-        outs = [torch.empty(total, dtype=torch.uint8, device=dev) for _ in range(nsets)]
-        dsts = [torch.empty_like(xs[0]) for _ in range(nsets)]
-        raw_bytes = xs[0].numel() * 2
-        enc_bytes = total
-
-        def enc(i):
-            kvc.encode(xs[i], p.bits_k, p.bits_v, p.group, seed=p.seed, out=outs[i])
-
-        def dec(i):
-            kvc.decode(outs[i], xs[i].shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed, out=dsts[i])
-        workload = {"workload": p.name, "shape": [L, 2, p.tokens, H, D], "storage": p.dtype,
-                    "bits_k": p.bits_k, "bits_v": p.bits_v, "group": p.group, "layout": "contiguous"}
-
-    algo_bytes = raw_bytes + enc_bytes     # read + write of one encode (or one decode)
     stream = torch.cuda.current_stream()
+    leg = Leg(kvc, p, dev, nsets=2)
 
-    # copy probe: achievable streaming bandwidth in the same run.  It runs
-    # before the warm-up steps on purpose: after an idle period the GPU needs
-    # some tens of milliseconds of load to reach its steady state (the first
-    # ~50 encode + decode steps run up to 10% slower), which the probe's
-    # copies and the default 50 warm-up steps cover.
-    copy_gbps = copy_probe(kvc, dev, stream)
-
-    for i in range(a.warmup):
-        enc(i % nsets)
-        dec(i % nsets)
-    torch.cuda.synchronize()
-
-    ev = TimingEvents(3 * a.steps)
-    torch.cuda.synchronize()
+    # pre-warm to steady clocks (time-based, independent of --warmup), then
+    # the copy probe, then the warm-up steps
     t0 = time.perf_counter()
-    for i in range(a.steps):
-        ev.record(3 * i, stream)
-        enc(i % nsets)
-        ev.record(3 * i + 1, stream)
-        dec(i % nsets)
-        ev.record(3 * i + 2, stream)
+    prewarm_steps = leg.prewarm(a.prewarm_s)
+    prewarm = {"seconds": time.perf_counter() - t0, "steps": prewarm_steps}
+    copy_gbps = copy_probe(kvc, dev, stream)
+    for i in range(a.warmup):
+        leg.enc(i)
+        leg.dec(i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    enc_ms = sorted(ev.ms(3 * i, 3 * i + 1) for i in range(a.steps))
-    dec_ms = sorted(ev.ms(3 * i + 1, 3 * i + 2) for i in range(a.steps))
-    ev.close()
-    t_enc = sum(enc_ms) / a.steps / 1e3   # s per encode (mean)
-    t_dec = sum(dec_ms) / a.steps / 1e3
+
+    wall, enc_ms, dec_ms = leg.timed(a.steps, stream)
     ms_per_step = wall / a.steps * 1e3
+    enc, dec = kernel_summary(leg, enc_ms, copy_gbps), kernel_summary(leg, dec_ms, copy_gbps)
+    t_enc, t_dec = enc["ms"] / 1e3, dec["ms"] / 1e3
 
     unfused = pipeline = None
     if not p.paged and not a.no_unfused:
-        unfused = unfused_leg(kvc, p, xs, outs, dsts, a, stream, t_enc, t_dec, raw_bytes)
+        unfused = unfused_leg(kvc, p, leg.src, leg.outs, leg.dsts, a, stream, t_enc, t_dec, leg.raw_bytes)
     if not p.paged and not a.no_pipeline:
-        pipeline = pipeline_leg(kvc, p, xs[0], dsts[0], stream, raw_bytes)
-
-    enc_alg = algo_bytes / t_enc / 1e9
-    dec_alg = algo_bytes / t_dec / 1e9
+        pipeline = pipeline_leg(kvc, p, leg.src[0], leg.dsts[0], stream, leg.raw_bytes)
     dominant = "encode" if t_enc >= t_dec else "decode"
     t_dom = max(t_enc, t_dec)
-    achieved = algo_bytes / t_dom / 1e9
-    saved = raw_bytes - enc_bytes
-    be = {}
-    for gbit in (100, 400):
-        wire_saved_s = saved * 8 / (gbit * 1e9)
-        be["%dGbit" % gbit] = {"wire_time_saved_ms": wire_saved_s * 1e3,
-                               "encode_plus_decode_ms": (t_enc + t_dec) * 1e3,
-                               "pays": (t_enc + t_dec) < wire_saved_s,
-                               "required_raw_GBps_each": 2 * gbit / 8 / (1 - enc_bytes / raw_bytes)}
+    achieved = leg.algo_bytes / t_dom / 1e9
     result = {
         "metric": "encode+decode throughput of raw bf16 KV input (GB/s); per-kernel % of HBM peak; "
                   "break-even at 400 Gbit",
-        "value": raw_bytes / (t_enc + t_dec) / 1e9,
+        "value": leg.raw_bytes / (ms_per_step / 1e3) / 1e9,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": a.steps,
@@ -459,26 +582,29 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded Gaussian KV with K outlier channels; no model weights)",
-        "config": workload,
-        "encode": {"raw_GBps": raw_bytes / t_enc / 1e9, "hbm_GBps": enc_alg,
-                   "frac_hbm_peak": enc_alg / HBM_PEAK_GBPS, "frac_copy_probe": enc_alg / copy_gbps,
-                   "ms": t_enc * 1e3, "ms_median": enc_ms[len(enc_ms) // 2], "ms_min": enc_ms[0]},
-        "decode": {"raw_GBps": raw_bytes / t_dec / 1e9, "hbm_GBps": dec_alg,
-                   "frac_hbm_peak": dec_alg / HBM_PEAK_GBPS, "frac_copy_probe": dec_alg / copy_gbps,
-                   "ms": t_dec * 1e3, "ms_median": dec_ms[len(dec_ms) // 2], "ms_min": dec_ms[0]},
-        "bytes": {"raw": raw_bytes, "encoded": enc_bytes, "ratio": raw_bytes / enc_bytes},
+        "config": leg.config,
+        "prewarm": prewarm,
+        "encode": enc,
+        "decode": dec,
+        "bytes": {"raw": leg.raw_bytes, "encoded": leg.enc_bytes, "ratio": leg.raw_bytes / leg.enc_bytes},
         "copy_probe_GBps": copy_gbps,
-        "break_even": be,
+        "break_even": break_even(leg, t_enc, t_dec),
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counter_traffic(p.name, dominant),
-                     "algorithmic_bytes_per_launch": algo_bytes, "launch_ms": t_dom * 1e3},
+                     "algorithmic_bytes_per_launch": leg.algo_bytes, "launch_ms": t_dom * 1e3},
         "unfused": unfused,
         "pipeline": pipeline,
+        "workloads": None,
         "cpu_baseline": None,
     }
+    leg.close()
+    if a.other_steps > 0:
+        result["workloads"] = {name: other_workload(kvc, name, dev, stream, a.other_steps)
+                               for name in presets.ORDER if name != p.name}
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, a.cpu_sample_chunks)
+        result["cpu_baseline"]["parity_sample"] = sample_parity(kvc, p, dev)
     print(json.dumps(result), flush=True)
 
 

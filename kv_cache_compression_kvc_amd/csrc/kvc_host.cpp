@@ -233,6 +233,8 @@ int plan_paged(Op op, const kvc_desc* d, const void* src, void* dst,
   if (pg->block_size < 1 || pg->block_size > 1024) return KVC_ERANGE;
   if (pg->num_reqs < 0 || pg->max_blocks < 0 || pg->num_blocks < 0 || pg->reserved != 0)
     return KVC_ERANGE;
+  // token positions (j * block_size, lengths) are 32-bit in the kernels
+  if (static_cast<int64_t>(pg->max_blocks) * pg->block_size > INT32_MAX) return KVC_ERANGE;
   uint64_t vecs_per_block;
   if (!mul_ok(static_cast<uint64_t>(pg->block_size), static_cast<uint64_t>(d->kv_heads), &vecs_per_block) ||
       vecs_per_block > (1ull << 30))

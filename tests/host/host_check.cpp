@@ -75,6 +75,21 @@ int main() {
   lens[5] = -1;
   CHECK(kvc_paged_layout(&d, lens, 64, offs, &total) == KVC_EINVAL);
   CHECK(kvc_paged_layout(&d, nullptr, 0, nullptr, &total) == KVC_OK && total == 0);
+  // paged plans: a table row whose token span overflows 32 bits is refused
+  {
+    alignas(16) static char pbuf[64];
+    int32_t table[1] = {0}, plen[1] = {16};
+    int64_t poff[1] = {0};
+    kvc_paged pg = {8, 16, 1, 1, 0, table, plen, poff, nullptr};
+    kvc::Plan plan;
+    CHECK(kvc::plan_paged(kvc::Op::Encode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_OK);
+    pg.block_size = 1024;
+    pg.max_blocks = (int32_t)(INT32_MAX / 1024);
+    CHECK(kvc::plan_paged(kvc::Op::Encode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_OK);
+    pg.max_blocks += 1;
+    CHECK(kvc::plan_paged(kvc::Op::Encode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_ERANGE);
+    CHECK(kvc::plan_paged(kvc::Op::Decode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_ERANGE);
+  }
   // sign mask: 128 bits, the first 64 equal for head_dim 64
   uint64_t m128[2], m64[1];
   CHECK(kvc_sign_mask(7, 128, m128) == KVC_OK && kvc_sign_mask(7, 64, m64) == KVC_OK);

@@ -5,7 +5,10 @@ plain definition of the method (``oracle/``):
   (1) rotated values: |y_gpu - y_ref| <= 1e-5 * max(|y_ref|, rms of y_ref's vector);
   (2) meta: fp16 scale / zero within 1 ulp of the oracle's
       (RD16(min y), RU16((max y - zero) / (2^b - 1))), as a distance of
-      ordered bit patterns;
+      ordered bit patterns.  The scale is defined from the zero, so where the
+      GPU's zero is the neighbouring fp16 value, its scale is compared with
+      RU16((max y - zero_gpu) / (2^b - 1)) as well (in a group with a tiny
+      range far from 0, one ulp of the zero is many ulps of the scale);
   (3) codes: equal to the code nearest to y among the levels of the GPU's own
       stored meta -- round-half-even of the exact t = (y - zero) / scale,
       computed in float64 from the oracle's y -- except where that t lies
@@ -101,23 +104,35 @@ class RowsResult:
     zero: np.ndarray
 
 
-def check_rows(x_bits, dtype, bits, group, seed, codes_gpu, meta_gpu, band=None):
+def check_rows(x_bits, dtype, bits, group, seed, codes_gpu, meta_gpu, band=None, y=None):
     """Criteria (2) and (3) for N vectors of one code width.
 
     x_bits: uint16 [N, D] storage; codes_gpu: uint8 [N, D*bits/8];
     meta_gpu: uint16 [N, D/group, 2] (scale, zero) bit patterns.
-    band: None for ``band_for(bits)``, a float, or an array shaped like the
-    codes.  Returns a RowsResult.
+    band: None for ``band_for(bits)``, a float, an array shaped like the
+    codes, or "fp32" for ``band_fp32`` of the GPU's meta.  A code is accepted
+    when it is the nearest level, or when |q - t| <= 1/2 + band (t clipped to
+    the code range).  y: the rotated values to judge the meta and codes
+    against; by default the oracle's, y = H (s * x) / sqrt(D).  Returns a
+    RowsResult.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     N, D = x_bits.shape
-    y = oracle.rotate(oracle.storage_to_f64(x_bits, dtype), oracle.sign_vector(seed, D))
+    if y is None:
+        y = oracle.rotate(oracle.storage_to_f64(x_bits, dtype), oracle.sign_vector(seed, D))
+    y = np.asarray(y, dtype=np.float64).reshape(N, D)
     scale, zero = oracle.group_meta(y, group, bits)
     q_ref, _ = oracle.quantize(y, scale, zero, group, bits)
     sg = np.asarray(meta_gpu[..., 0], dtype=np.uint16)
     zg = np.asarray(meta_gpu[..., 1], dtype=np.uint16)
-    ds = np.abs(ordered16(sg) - ordered16(scale.view(np.uint16)))
     dz = np.abs(ordered16(zg) - ordered16(zero.view(np.uint16)))
+    ds = np.abs(ordered16(sg) - ordered16(scale.view(np.uint16)))
+    if (dz > 0).any():   # the scale that belongs to the GPU's own zero
+        mx = y.reshape(N, -1, group).max(axis=-1)
+        zgf = zg.view(np.float16).astype(np.float64)
+        with np.errstate(over="ignore"):
+            s_zg = oracle.ru16(np.maximum(mx - zgf, 0.0) / float(2 ** bits - 1))
+        ds = np.minimum(ds, np.abs(ordered16(sg) - ordered16(s_zg.view(np.uint16))))
     assert ds.max(initial=0) <= 1 and dz.max(initial=0) <= 1, \
         "meta differs by more than one fp16 ulp (scale %d, zero %d)" % (ds.max(), dz.max())
     meta_diff = (ds > 0) | (dz > 0)
@@ -129,18 +144,22 @@ def check_rows(x_bits, dtype, bits, group, seed, codes_gpu, meta_gpu, band=None)
     q_exp = oracle.nearest_codes(t, bits)
     if band is None:
         band = band_for(bits)
-    dist = np.abs(t - (np.floor(t) + 0.5))
-    near = dist < band
-    neighbor = (q_gpu == np.floor(t)) | (q_gpu == np.floor(t) + 1)
+    elif isinstance(band, str):
+        assert band == "fp32", band
+        band = band_fp32(y, z_g, s_g, group, bits)
+    t_c = np.clip(t, 0.0, float(2 ** bits - 1))
+    # a flip's excess over one half: its distance from the boundary between
+    # the GPU's code and the nearest one (for a neighbouring code)
+    excess = np.abs(q_gpu - t_c) - 0.5
     flips = q_gpu != q_exp
-    bad = flips & ~(near & neighbor)
+    bad = flips & (excess > band)
     assert not bad.any(), "%d codes differ away from a rounding boundary (t=%s, gpu=%s)" % (
         bad.sum(), t[bad][:4], q_gpu[bad][:4])
     rep.code_mismatches = int((q_gpu != q_ref).sum())
     rep.boundary_flips = int(flips.sum())
     if flips.any():
-        rep.worst_boundary_distance = float(dist[flips].max())
-        rep.flips_beyond_1e5 = int((flips & (dist >= BOUNDARY)).sum())
+        rep.worst_boundary_distance = float(excess[flips].max())
+        rep.flips_beyond_1e5 = int((flips & (excess >= BOUNDARY)).sum())
     # the oracle's encode with the allowed differences replaced by the GPU's
     group_of = np.repeat(meta_diff, group, axis=-1)
     q_sub = np.where(group_of | flips, q_gpu, q_ref).astype(np.uint8)

@@ -181,6 +181,17 @@ def test_full_size_sampled(name):
     torch.cuda.synchronize()
     assert gpu_util.canaries_intact(whole)
     idx = gpu_util.sample_vectors(p, rng)
+    # criterion (1) on the sampled vectors of the full-size transform
+    D = p.head_dim
+    _say("full size", name, "rotate")
+    y = kvc.debug_rotate(x, seed=p.seed)
+    gi = torch.from_numpy(idx).to(DEV)
+    ys = y.view(-1, D)[gi].cpu().numpy()
+    del y
+    torch.cuda.empty_cache()
+    xs = inputs.as_u16(x.view(-1, D)[gi])
+    yref = oracle.rotate(oracle.storage_to_f64(xs, p.dtype), oracle.sign_vector(p.seed, D))
+    _say("  sampled rotation worst/allowed: %.3f over %d vectors" % (parity.check_rotation(ys, yref), len(idx)))
     rep, reference = gpu_util.check_sampled_encode(p, x, out, idx)
     _say("  sampled codes vs oracle:", rep)
     _say("full size", name, "decode")
@@ -191,7 +202,6 @@ def test_full_size_sampled(name):
     assert ratio <= 1.0
     # criterion (4) on the sampled vectors: the GPU decode against the oracle's
     # decode of its own encode (allowed differences substituted)
-    D = p.head_dim
     got_all = inputs.as_u16(xd.view(-1, D)[torch.from_numpy(idx).to(DEV)])
     rr = parity.check_decode(got_all, reference, p.dtype, axis_slices=(1,))
     _say("  sampled decode vs the oracle's decode: rrms %.3g over %d vectors" % (rr, len(idx)))
