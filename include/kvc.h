@@ -236,6 +236,25 @@ kvc_status kvc_decode_unfused(const kvc_desc* desc, const void* in, uint64_t in_
                               void* workspace, uint64_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * encode of kvc_encode_unfused with its workspace taken from a static
+ * device array of KVC_NOALLOC_WORKSPACE_BYTES that the library holds on
+ * every device it runs on until the process ends.  Arguments as kvc_encode;
+ * the blob is bit-identical to kvc_encode_unfused's (and kvc_encode's).
+ * A shape whose workspace (kvc_unfused_workspace_size) exceeds the array
+ * returns KVC_ENOSPC before anything is enqueued -- 5 bytes per element, so
+ * up to about 13.4 million elements.  The call allocates nothing; it needs
+ * no zeroed memory (every workspace byte it reads it has written), and the
+ * array keeps the last call's contents.  All calls on one device share the
+ * one array: calls that overlap on a device (other streams, other host
+ * threads) race and must be ordered by the caller.
+ */
+#define KVC_NOALLOC_WORKSPACE_BYTES (64ull << 20)
+kvc_status kvc_encode_unfused_noalloc(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes,
+                                      void* stream);
+
+/*
  * Chunked encode overlapped with the transfer of its output, and the
  * receiving side.  The episode notes of "FastKVComp: checking whether
  * high-throughput KV compression pays off" give the break-even rule

@@ -26,7 +26,7 @@ from ._lib import KvcDesc, KvcPaged, KvcError, DTYPE
 __all__ = [
     "KvcError", "DTYPE", "abi_version", "encoded_size", "sign_mask", "encode", "decode",
     "paged_layout", "encode_paged", "decode_paged", "debug_rotate", "probe_copy",
-    "unfused_workspace_size", "encode_unfused", "decode_unfused",
+    "unfused_workspace_size", "encode_unfused", "decode_unfused", "encode_unfused_noalloc",
     "chunked_size", "encode_send", "receive_decode",
 ]
 
@@ -163,6 +163,22 @@ def encode_unfused(kv, bits_k, bits_v, group, seed=0, out=None, workspace=None, 
     d = _desc(L, T, H, D, dt, bits_k, bits_v, group, seed)
     _lib.check(_lib.lib().kvc_encode_unfused(ctypes.byref(d), _ptr(kv), _ptr(out), _nbytes(out), _ptr(ws),
                                              _nbytes(ws), _stream(stream)))
+    return out
+
+
+def encode_unfused_noalloc(kv, bits_k, bits_v, group, seed=0, out=None, stream=None):
+    """Comparator encode whose workspace is the library's static device array
+    (allocates nothing in the call itself; ``out`` must then be given by
+    callers that cannot allocate).  Calls that overlap on one device race."""
+    L, T, H, D = _kv_shape(kv.shape, "kv")
+    dt = _dtype_name(kv)
+    _check_cuda(kv, out)
+    if out is None:
+        total, _ = encoded_size(L, T, H, D, bits_k, bits_v, group, dt)
+        out = torch.empty(total, dtype=torch.uint8, device=kv.device)
+    d = _desc(L, T, H, D, dt, bits_k, bits_v, group, seed)
+    _lib.check(_lib.lib().kvc_encode_unfused_noalloc(ctypes.byref(d), _ptr(kv), _ptr(out), _nbytes(out),
+                                                     _stream(stream)))
     return out
 
 

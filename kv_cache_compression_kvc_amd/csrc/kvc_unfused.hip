@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/kvc.h"
 #include "kvc_device.h"
@@ -458,10 +459,55 @@ int split_workspace(const kvc_desc* d, void* ws, uint64_t ws_bytes, uint8_t** q8
   return KVC_OK;
 }
 
+/*
+ * Workspace of kvc_encode_unfused_noalloc: a static device array, so that
+ * the call allocates nothing.  Every device the library runs on holds its
+ * own copy for the life of the process.  In host code `scratch` names a
+ * host-side stand-in, not device memory: its device address on the current
+ * device comes from hipGetSymbolAddress, taken once per device and kept.
+ * The encode stages write every byte of the workspace they read, so nothing
+ * in it has to start at zero, and it keeps the last call's contents.
+ */
+constexpr uint64_t kStaticWorkspaceBytes = uint64_t(KVC_NOALLOC_WORKSPACE_BYTES);
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int static_workspace(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVC_EHIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVC_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVC_OK;
+}
+
 }  // namespace uf
 }  // namespace kvc
 
 extern "C" {
+
+kvc_status kvc_encode_unfused_noalloc(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes,
+                                      void* stream) {
+  kvc::Plan plan;
+  int st = kvc::plan_contiguous(kvc::Op::Encode, desc, kv, out, out_bytes, &plan);
+  uint64_t need = 0;
+  if (st == KVC_OK) st = kvc::unfused_workspace(desc, &need, nullptr);
+  if (st == KVC_OK && need > kvc::uf::kStaticWorkspaceBytes) st = KVC_ENOSPC;
+  void* ws = nullptr;
+  if (st == KVC_OK && need > 0) st = kvc::uf::static_workspace(&ws);
+  uint8_t* q8 = nullptr;
+  float* f = nullptr;
+  if (st == KVC_OK) st = kvc::uf::split_workspace(desc, ws, kvc::uf::kStaticWorkspaceBytes, &q8, &f);
+  if (st == KVC_OK) st = kvc::uf::run<true>(plan, static_cast<hipStream_t>(stream), q8, f);
+  return static_cast<kvc_status>(st);
+}
 
 kvc_status kvc_encode_unfused(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes, void* workspace,
                               uint64_t workspace_bytes, void* stream) {
