@@ -258,66 +258,165 @@ __device__ __forceinline__ T ld_const(const T* p) {
 
 /*
  * Wave-uniform position in a launch's item space, advanced by the grid size
- * without divisions.  Contiguous items walk the launch's slabs tile by tile
- * (kvc_cursor.h: slab offsets carried along, no products per step); paged
- * items are (slab i, request r, block j, subtile sub) in radices (num_reqs,
- * max_blocks, subtiles).  k.item is the item of either layout.
+ * without divisions.
+ *
+ * Contiguous items walk the launch's slabs tile by tile (kvc_cursor.h: slab
+ * offsets carried along, no products per step).
+ *
+ * Paged items: a launch covers requests [req_first, req_first + nreq), at
+ * most one per lane.  At its start every wave loads the lengths and blob
+ * offsets of those requests into its lanes (lane r: request req_first + r),
+ * checks them, and numbers the items of a slab request by request with a
+ * prefix sum over the lanes: request r owns ceil(len / block_size) *
+ * subtiles items, so there are no empty items.  An item's request is then
+ * the number of lanes whose running total is at or below it (one ballot),
+ * and its length and offset come from that lane (readlane).  The cursor runs
+ * one item ahead of the tile it hands out: the block-table entry of the
+ * next item is loaded while the current one is worked on.
  */
-struct Cursor {
-  ContigCursor k;
-  int64_t i, di;
-  int32_t r, j, sub, dr, dj, dsub;
+struct PagedPos {
+  int64_t item;          // item of the launch (slab i, item b of the slab)
+  int64_t i, b;
+  int32_t r, j, sub;     // request (lane), block of the request, subtile of the block
+  int32_t blk;           // block-table entry of (r, j), loaded ahead
 };
 
-__device__ __forceinline__ void split_paged(const LaunchArgs& a, int64_t x, int64_t& i, int32_t& r,
-                                            int32_t& j, int32_t& sub) {
-  sub = static_cast<int32_t>(x % a.subtiles);
-  x /= a.subtiles;
-  j = static_cast<int32_t>(x % a.max_blocks);
-  x /= a.max_blocks;
-  r = static_cast<int32_t>(x % a.num_reqs);
-  i = x / a.num_reqs;
+struct Cursor {
+  ContigCursor k;
+  // paged: lane values (lane r = request req_first + r)
+  int32_t incl;          // items of requests 0..r of this launch (one slab); past nreq: INT32_MAX
+  int32_t len;           // tokens of request r, 0 when the request is invalid
+  int64_t off;           // byte offset of request r's blob
+  // paged: wave-uniform
+  int64_t per_slab, total, di, db;
+  PagedPos cur, ahead;
+};
+
+__device__ __forceinline__ int32_t lane_value(int32_t v, int32_t lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ int64_t lane_value64(int64_t v, int32_t lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int32_t>(static_cast<uint64_t>(v)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int32_t>(static_cast<uint64_t>(v) >> 32), lane);
+  return static_cast<int64_t>((uint64_t(hi) << 32) | lo);
+}
+
+/* Blob bytes of a request of `len` tokens: (code slab K, code slab V, meta
+ * slab, total); every slab padded to a multiple of 256 bytes. */
+struct ReqSizes {
+  uint64_t ck, cv, mslab, total;
+};
+__device__ __forceinline__ ReqSizes req_sizes(const LaunchArgs& a, int64_t len) {
+  ReqSizes z;
+  const uint64_t rows = uint64_t(len) * uint64_t(a.heads);
+  z.ck = align256(rows * uint64_t(a.row_k));
+  z.cv = align256(rows * uint64_t(a.row_v));
+  z.mslab = align256(rows * uint64_t(a.groups) * 4u);
+  z.total = uint64_t(a.layers) * (z.ck + z.cv) + uint64_t(a.layers) * 2u * z.mslab;
+  return z;
+}
+
+/* (request, block, subtile) of item b of a slab, and its table entry. */
+__device__ __forceinline__ void paged_resolve(const LaunchArgs& a, const Cursor& c, PagedPos& p) {
+  const uint64_t below = __builtin_amdgcn_ballot_w64(int64_t(c.incl) <= p.b);
+  p.r = __builtin_popcountll(below);
+  const int32_t first = p.r > 0 ? lane_value(c.incl, p.r - 1) : 0;
+  const int32_t e = static_cast<int32_t>(p.b) - first;
+  if (a.subtiles == 1) {
+    p.j = e;
+    p.sub = 0;
+  } else {
+    p.j = e / a.subtiles;
+    p.sub = e - p.j * a.subtiles;
+  }
+  p.blk = ld_const(a.table + int64_t(a.req_first + p.r) * a.max_blocks + p.j);
+}
+
+__device__ __forceinline__ void paged_step(const LaunchArgs& a, const Cursor& c, PagedPos& p) {
+  p.item += gridDim.x;
+  p.i += c.di;
+  p.b += c.db;
+  if (p.b >= c.per_slab) {
+    p.b -= c.per_slab;
+    p.i += 1;
+  }
+}
+
+/* Per-wave set-up of a paged launch: the lanes' requests, checked (a length
+ * outside [0, max_blocks * block_size] or a blob offset that is negative,
+ * not a multiple of 16 or whose blob would end past the buffer: the request
+ * is skipped and bit 0 of *err set), the item numbering, and the wave's
+ * first two items. */
+__device__ __forceinline__ void paged_init(const LaunchArgs& a, Cursor& c) {
+  const int lane = threadIdx.x;
+  int32_t len = 0;
+  int64_t off = 0;
+  int32_t items = 0;
+  if (lane < a.nreq) {
+    len = a.lens[a.req_first + lane];
+    off = a.offsets[a.req_first + lane];
+    bool ok = len >= 0 && int64_t(len) <= int64_t(a.max_blocks) * a.block_size;
+    if (ok) {
+      const ReqSizes z = req_sizes(a, len);
+      ok = off >= 0 && !(off & 15) && uint64_t(off) <= a.blob_bytes && z.total <= a.blob_bytes - uint64_t(off);
+    }
+    if (!ok) {
+      if (a.err) atomicOr(a.err, 1);
+      len = 0;
+    }
+    items = (len + a.block_size - 1) / a.block_size * a.subtiles;
+  }
+  // inclusive prefix sum of the items over the lanes
+  int32_t incl = items;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  c.per_slab = lane_value(incl, a.nreq - 1);
+  c.incl = lane < a.nreq ? incl : INT32_MAX;
+  c.len = len;
+  c.off = off;
+  c.total = c.per_slab * a.n_slabs;
+  c.cur.item = blockIdx.x;
+  if (c.per_slab == 0 || c.cur.item >= c.total) {
+    c.total = 0;
+    return;
+  }
+  const int64_t step = gridDim.x;
+  c.di = step / c.per_slab;
+  c.db = step - c.di * c.per_slab;
+  c.cur.i = c.cur.item / c.per_slab;
+  c.cur.b = c.cur.item - c.cur.i * c.per_slab;
+  paged_resolve(a, c, c.cur);
+  c.ahead = c.cur;
+  paged_step(a, c, c.ahead);
+  if (c.ahead.item < c.total) paged_resolve(a, c, c.ahead);
+}
+
+/* The ahead item becomes the current one; the next one is resolved and its
+ * table entry requested. */
+__device__ __forceinline__ void paged_advance(const LaunchArgs& a, Cursor& c) {
+  c.cur = c.ahead;
+  paged_step(a, c, c.ahead);
+  if (c.ahead.item < c.total) paged_resolve(a, c, c.ahead);
 }
 
 template <bool PAGED>
 __device__ __forceinline__ void cursor_init(const LaunchArgs& a, Cursor& c) {
-  const int64_t start = blockIdx.x, step = gridDim.x;
   if constexpr (!PAGED) {
-    contig_init(a, start, step, c.k);
+    contig_init(a, int64_t(blockIdx.x), int64_t(gridDim.x), c.k);
   } else {
-    c.k.item = start;
-    split_paged(a, start, c.i, c.r, c.j, c.sub);
-    split_paged(a, step, c.di, c.dr, c.dj, c.dsub);
+    paged_init(a, c);
   }
-}
-
-template <bool PAGED>
-__device__ __forceinline__ void cursor_next(const LaunchArgs& a, Cursor& c) {
-  if constexpr (!PAGED) {
-    contig_next(a, int64_t(gridDim.x), c.k);
-    return;
-  }
-  c.k.item += gridDim.x;
-  c.sub += c.dsub;
-  int32_t carry = c.sub >= a.subtiles;
-  if (carry) c.sub -= a.subtiles;
-  c.j += c.dj + carry;
-  carry = c.j >= a.max_blocks;
-  if (carry) c.j -= a.max_blocks;
-  c.r += c.dr + carry;
-  carry = c.r >= a.num_reqs;
-  if (carry) c.r -= a.num_reqs;
-  c.i += c.di + carry;
 }
 
 /*
- * The tile of the cursor's item.  Paged items past a request's length are
- * skipped (false), as are items whose table entry, length or blob extent is
- * invalid (bit 0 of *err is then set).  `tensor` is the KV side (source of
- * an encode, destination of a decode), `blob` the encoded side.  With PAD,
- * the last tile of each slab also zeroes the padding that follows the slab's
- * codes and its meta (each is padded to a multiple of 256 bytes), right when
- * it is found.
+ * The tile of the cursor's item.  Paged items whose subtile lies past the
+ * request's last token (the last block's tail) are skipped (false), as are
+ * items whose table entry lies outside the pool (bit 0 of *err is then
+ * set).  `tensor` is the KV side (source of an encode, destination of a
+ * decode), `blob` the encoded side.  With PAD, the last tile of each slab
+ * also zeroes the padding that follows the slab's codes and its meta (each
+ * is padded to a multiple of 256 bytes), right when it is found.
  */
 template <int D, bool PAD, bool PAGED>
 __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c, const uint8_t* tensor,
@@ -337,30 +436,22 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
     }
     return true;
   }
-  const int32_t len = ld_const(a.lens + c.r);
-  if (len < 0 || int64_t(len) > int64_t(a.max_blocks) * a.block_size) {
-    if (a.err && c.j == 0 && c.sub == 0) atomicOr(a.err, 1);
-    return false;
-  }
-  const int32_t first_tok = c.j * a.block_size;
-  if (first_tok >= len) return false;
+  const PagedPos& p = c.cur;
+  const int32_t len = lane_value(c.len, p.r);
+  const int32_t first_tok = p.j * a.block_size;  // < len: at most max_blocks * block_size <= INT32_MAX
   const int32_t ntok = min(a.block_size, len - first_tok);
-  const int32_t v0 = c.sub * kTileVectors;
+  const int32_t v0 = p.sub * kTileVectors;
   const int32_t nvec = ntok * a.heads;
   if (v0 >= nvec) return false;
-  const int32_t blk = ld_const(a.table + int64_t(c.r) * a.max_blocks + c.j);
-  const int64_t off = ld_const(a.offsets + c.r);
-  const int64_t rows = int64_t(len) * a.heads;
-  const uint64_t ck = align256(uint64_t(rows) * a.row_k), cv = align256(uint64_t(rows) * a.row_v);
-  const uint64_t mslab = align256(uint64_t(rows) * a.groups * 4);
-  const uint64_t meta_start = uint64_t(a.layers) * (ck + cv);
-  const uint64_t total = meta_start + uint64_t(a.layers) * 2 * mslab;
-  if (blk < 0 || blk >= a.num_blocks || off < 0 || (off & 15) || uint64_t(off) > a.blob_bytes ||
-      total > a.blob_bytes - uint64_t(off)) {
+  if (p.blk < 0 || p.blk >= a.num_blocks) {
     if (a.err) atomicOr(a.err, 1);
     return false;
   }
-  const int64_t s = c.i * a.slab_step + a.slab_first;
+  const int64_t off = lane_value64(c.off, p.r);
+  const ReqSizes z = req_sizes(a, len);
+  const int64_t rows = int64_t(len) * a.heads;
+  const uint64_t meta_start = uint64_t(a.layers) * (z.ck + z.cv);
+  const int64_t s = p.i * a.slab_step + a.slab_first;
   const int64_t l = s >> 1, kv = s & 1;
   const int64_t row = kv ? a.row_v : a.row_k;
   const int64_t row0 = int64_t(first_tok) * a.heads + v0;  // t*H + h of the tile's first vector
@@ -368,14 +459,14 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
   t.count = min(kTileVectors, nvec - v0);
   t.geom = code_geom(row0 - tile0, min<int64_t>(kTileVectors, rows - tile0),
                      min<int64_t>(kTileVectors, rows - tile0 - kTileVectors));
-  t.src = tensor + ((s * a.num_blocks + blk) * int64_t(a.block_size) * a.heads + v0) * vec_bytes;
-  uint8_t* cs = blob + off + l * (ck + cv) + (kv ? ck : 0);
-  uint8_t* ms = blob + off + meta_start + s * mslab;
+  t.src = tensor + ((s * a.num_blocks + p.blk) * int64_t(a.block_size) * a.heads + v0) * vec_bytes;
+  uint8_t* cs = blob + off + l * (z.ck + z.cv) + (kv ? z.ck : 0);
+  uint8_t* ms = blob + off + meta_start + s * z.mslab;
   t.codes = cs + tile0 * row;
   t.meta = ms + row0 * a.groups * 4;
   if (PAD && row0 + t.count == rows) {  // the slab's last tile also zeroes its padding
-    zero_tail(cs + rows * row, (kv ? cv : ck) - rows * row);
-    zero_tail(ms + rows * a.groups * 4, mslab - rows * a.groups * 4);
+    zero_tail(cs + rows * row, (kv ? z.cv : z.ck) - rows * row);
+    zero_tail(ms + rows * a.groups * 4, z.mslab - rows * a.groups * 4);
   }
   return true;
 }
@@ -384,12 +475,21 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
 template <int D, bool PAD, bool PAGED>
 __device__ __forceinline__ bool next_tile(const LaunchArgs& a, Cursor& c, const uint8_t* tensor, uint8_t* blob,
                                           Tile& t, bool first) {
-  if (!first) cursor_next<PAGED>(a, c);
-  while (c.k.item < a.total_items) {
-    if (cursor_tile<D, PAD, PAGED>(a, c, tensor, blob, t)) return true;
-    cursor_next<PAGED>(a, c);
+  if constexpr (!PAGED) {
+    if (!first) contig_next(a, int64_t(gridDim.x), c.k);
+    while (c.k.item < a.total_items) {
+      if (cursor_tile<D, PAD, PAGED>(a, c, tensor, blob, t)) return true;
+      contig_next(a, int64_t(gridDim.x), c.k);
+    }
+    return false;
+  } else {
+    if (!first) paged_advance(a, c);
+    while (c.cur.item < c.total) {
+      if (cursor_tile<D, PAD, PAGED>(a, c, tensor, blob, t)) return true;
+      paged_advance(a, c);
+    }
+    return false;
   }
-  return false;
 }
 
 /* ---- LDS staging ------------------------------------------------------------- */

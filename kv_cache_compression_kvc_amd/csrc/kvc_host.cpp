@@ -240,15 +240,19 @@ int plan_paged(Op op, const kvc_desc* d, const void* src, void* dst,
       vecs_per_block > (1ull << 30))
     return KVC_ESHAPE;
   uint64_t subtiles = (vecs_per_block + kTileVectors - 1) / kTileVectors;
+  // item counts of one request chunk are 32-bit in the kernels
+  if (static_cast<uint64_t>(pg->max_blocks) * subtiles * kReqChunk > static_cast<uint64_t>(INT32_MAX))
+    return KVC_ERANGE;
+  const uint64_t chunk = pg->num_reqs < kReqChunk ? static_cast<uint64_t>(pg->num_reqs) : kReqChunk;
   uint64_t per_slab, items;
-  if (!mul_ok(static_cast<uint64_t>(pg->num_reqs), static_cast<uint64_t>(pg->max_blocks), &per_slab) ||
-      !mul_ok(per_slab, subtiles, &per_slab) ||
+  if (!mul_ok(chunk, static_cast<uint64_t>(pg->max_blocks), &per_slab) || !mul_ok(per_slab, subtiles, &per_slab) ||
       !mul_ok(per_slab, 2ull * static_cast<uint64_t>(d->layers), &items) || items > (1ull << 62))
     return KVC_ESHAPE;
   if (items == 0) {
     plan->n_launch = 0;
     return KVC_OK;
   }
+  plan->req_chunks = (pg->num_reqs + kReqChunk - 1) / kReqChunk;
   if (!src || !dst || !pg->block_table || !pg->seq_lens || !pg->out_offsets) return KVC_EINVAL;
   if (!aligned16(src) || !aligned16(dst)) return KVC_EALIGN;
   if ((reinterpret_cast<uintptr_t>(pg->out_offsets) & 7u) ||
@@ -273,7 +277,7 @@ int plan_paged(Op op, const kvc_desc* d, const void* src, void* dst,
   base.offsets = pg->out_offsets;
   base.err = pg->err_flag;
   split_slabs(op, d, plan, base);
-  for (int i = 0; i < plan->n_launch; ++i)
+  for (int i = 0; i < plan->n_launch; ++i)   // per request chunk; run_plan sets req_first / nreq
     plan->args[i].total_items = static_cast<int64_t>(per_slab) * plan->args[i].n_slabs;
   return KVC_OK;
 }

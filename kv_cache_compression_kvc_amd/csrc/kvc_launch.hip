@@ -157,11 +157,19 @@ int run_plan(Op op, const Plan& plan, void* stream) {
     const int64_t waves =
         shape.waves_per_simd > 0 ? std::min<int64_t>(resident, int64_t(cus) * kSimdsPerCu * shape.waves_per_simd)
                                  : resident;
-    const int64_t grid = std::min<int64_t>(plan.args[i].total_items, waves);
-    if (grid <= 0) continue;
-    hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64), 0, static_cast<hipStream_t>(stream),
-                       plan.args[i]);
-    if (hipGetLastError() != hipSuccess) return KVC_EHIP;
+    // a paged call runs one launch per chunk of kReqChunk requests
+    const int chunks = plan.args[i].paged ? plan.req_chunks : 1;
+    for (int c = 0; c < chunks; ++c) {
+      LaunchArgs a = plan.args[i];
+      if (a.paged) {
+        a.req_first = c * kReqChunk;
+        a.nreq = std::min(kReqChunk, a.num_reqs - a.req_first);
+      }
+      const int64_t grid = std::min<int64_t>(a.total_items, waves);
+      if (grid <= 0) continue;
+      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64), 0, static_cast<hipStream_t>(stream), a);
+      if (hipGetLastError() != hipSuccess) return KVC_EHIP;
+    }
   }
   return KVC_OK;
 }

@@ -19,6 +19,7 @@
 namespace kvc {
 
 constexpr int kTileVectors = 64;   // one vector per lane of a wave64
+constexpr int kReqChunk = 64;      // requests of one paged launch: one per lane of a wave64
 
 /* Arguments of one encode / decode / rotate launch (passed by value). */
 struct LaunchArgs {
@@ -55,20 +56,25 @@ struct LaunchArgs {
   int32_t meta_tail;      // zero bytes after a meta slab's rows * groups * 4 bytes (< 256)
   int32_t pad1;
 
-  // paged layout
+  // paged layout: this launch covers requests [req_first, req_first + nreq),
+  // nreq <= kReqChunk; an item is (slab, request, block, subtile), and the
+  // items of a slab are numbered request by request, with no gaps (the
+  // kernel numbers them from the lengths)
   int64_t num_blocks;
   int32_t block_size;
   int32_t heads;
-  int32_t num_reqs;
+  int32_t num_reqs;       // all requests of the call
   int32_t max_blocks;
   int32_t subtiles;       // ceil(block_size * H / 64)
+  int32_t req_first;
+  int32_t nreq;
   int32_t pad0;
   const int32_t* table;
   const int32_t* lens;
   const int64_t* offsets;
   int32_t* err;
 
-  int64_t total_items;    // items of this launch
+  int64_t total_items;    // items of this launch (paged: an upper bound, for the grid size)
   uint32_t sign_words[64];// bit 15 / bit 31 of word m: sign of element 2m / 2m+1
 };
 
@@ -77,6 +83,7 @@ enum class Op { Encode, Decode, Rotate };
 /* Up to two launches: K and V run together when their code widths match. */
 struct Plan {
   int n_launch;
+  int req_chunks;         // paged: launches per entry of args, one per kReqChunk requests
   int bits[2];
   int head_dim;
   int dtype;

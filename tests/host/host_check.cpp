@@ -83,12 +83,29 @@ int main() {
     kvc_paged pg = {8, 16, 1, 1, 0, table, plen, poff, nullptr};
     kvc::Plan plan;
     CHECK(kvc::plan_paged(kvc::Op::Encode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_OK);
+    // one head, 1024-token blocks: 16 subtiles per block; both the token span
+    // (max_blocks * 1024) and a 64-request chunk's items (max_blocks * 16 * 64)
+    // reach INT32_MAX at the same row length
+    kvc_desc d1 = d;
+    d1.kv_heads = 1;
     pg.block_size = 1024;
     pg.max_blocks = (int32_t)(INT32_MAX / 1024);
+    CHECK(kvc::plan_paged(kvc::Op::Encode, &d1, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_OK);
+    pg.max_blocks += 1;
+    CHECK(kvc::plan_paged(kvc::Op::Encode, &d1, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_ERANGE);
+    CHECK(kvc::plan_paged(kvc::Op::Decode, &d1, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_ERANGE);
+    // 16-token blocks of 4 heads: one subtile per block; the chunk's items bound the row
+    pg.block_size = 16;
+    pg.max_blocks = (int32_t)(INT32_MAX / 64);
     CHECK(kvc::plan_paged(kvc::Op::Encode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_OK);
+    CHECK(plan.req_chunks == 1);
     pg.max_blocks += 1;
     CHECK(kvc::plan_paged(kvc::Op::Encode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_ERANGE);
-    CHECK(kvc::plan_paged(kvc::Op::Decode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_ERANGE);
+    // 130 requests: three launches of at most 64 requests per code width
+    pg.max_blocks = 4;
+    pg.num_reqs = 130;
+    CHECK(kvc::plan_paged(kvc::Op::Encode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_OK);
+    CHECK(plan.req_chunks == 3 && plan.n_launch == 2);
   }
   // sign mask: 128 bits, the first 64 equal for head_dim 64
   uint64_t m128[2], m64[1];

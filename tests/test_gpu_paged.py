@@ -107,6 +107,69 @@ def test_paged_matches_oracle(D, dtype, bk, bv, G, H, lens):
         assert torch.equal(dr.view(torch.int16).cpu(), got_t[:, :, blocks, offs_in]), "request %d" % r
 
 
+def test_paged_more_requests_than_one_launch():
+    """130 requests (lengths 0..40, some empty): three launches of at most 64
+    requests per code width; every request's blob against the oracle, and the
+    decode into a sentinel pool."""
+    p = presets.preset("qwen7b_paged").with_(name="paged-many", layers=2, kv_heads=2, head_dim=64,
+                                              dtype="fp16", bits_k=4, bits_v=2, group=32, seed=12)
+    rng = np.random.default_rng(12)
+    lens = rng.integers(0, 41, 130).astype(np.int32)
+    lens[[0, 63, 64, 129]] = [0, 17, 0, 40]
+    lens, table, pool, offs, total = _setup(p, lens)
+    bt, sl, of = _gpu(lens, table, offs)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    whole, out = gpu_util.guarded(total, DEV)
+    _say("paged encode, 130 requests")
+    kvc.encode_paged(pool.to(DEV), bt, sl, of, total, 4, 2, 32, seed=p.seed, out=out, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and gpu_util.canaries_intact(whole)
+    blob = out.cpu().numpy()
+    pool_b = inputs.as_u16(pool)
+    sblob = np.zeros(total, dtype=np.uint8)
+    for r, n in enumerate(lens):
+        size = oracle.blob_layout(p.layers, int(n), 2, 64, 4, 2, 32).total
+        if n:
+            x = oracle.gather_request(pool_b, table[r], int(n))
+            sblob[offs[r]:offs[r] + size] = parity.check_blob(x, blob[offs[r]:offs[r] + size], "fp16", 4, 2, 32,
+                                                              p.seed).blob
+    _say("paged decode, 130 requests")
+    sentinel_bits = inputs.as_u16(torch.tensor([7.0], dtype=pool.dtype))[0]
+    dst = torch.full(pool.shape, 7.0, dtype=pool.dtype, device=DEV)
+    kvc.decode_paged(out, dst, bt, sl, of, 4, 2, 32, seed=p.seed, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = inputs.as_u16(dst)
+    ref = oracle.decode_paged(sblob, np.full(pool_b.shape, sentinel_bits, dtype=np.uint16), table, lens,
+                              "fp16", 4, 2, 32, p.seed)
+    used = np.zeros(pool.shape[2:4], dtype=bool)
+    for r, n in enumerate(lens):
+        for t in range(int(n)):
+            used[table[r][t // p.block_size], t % p.block_size] = True
+    assert np.array_equal(got[:, :, ~used], ref[:, :, ~used])
+    parity.check_decode(got[:, :, used], ref[:, :, used], "fp16")
+
+
+def test_paged_bad_offset_is_flagged_not_faulted():
+    """A request blob offset that is not a multiple of 16, and one past the
+    buffer: those requests are skipped and flagged, the others encode."""
+    p = presets.preset("qwen7b_paged").with_(name="paged-badoff", layers=1, kv_heads=4, seed=1)
+    lens, table, pool, offs, total = _setup(p, [40, 20, 33])
+    offs = offs.copy()
+    offs[1] += 8
+    offs[2] = total + 4096
+    bt, sl, of = _gpu(lens, table, offs)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    whole, out = gpu_util.guarded(total, DEV)
+    kvc.encode_paged(pool.to(DEV), bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=1, out=out, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 1 and gpu_util.canaries_intact(whole)
+    pool_b = inputs.as_u16(pool)
+    x = oracle.gather_request(pool_b, table[0], 40)
+    sub = out.cpu().numpy()[offs[0]:offs[0] + oracle.blob_layout(1, 40, 4, 128, p.bits_k, p.bits_v, p.group).total]
+    parity.check_blob(x, sub, p.dtype, p.bits_k, p.bits_v, p.group, 1)
+
+
 def test_paged_bad_table_entry_is_flagged_not_faulted():
     p = presets.preset("qwen7b_paged").with_(name="paged-bad", layers=1, kv_heads=4, seed=1)
     lens, table, pool, offs, total = _setup(p, [40, 20])
