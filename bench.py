@@ -12,8 +12,8 @@ cache-resident data.  Prints ONE JSON line.
 Warm-up: after an idle period the GPU needs some hundreds of milliseconds
 of load to reach its steady clocks, so before the W warm-up steps the
 headline workload runs encode + decode back to back for --prewarm-s seconds
-of wall time (reported as "prewarm"), whatever W is; the copy probe runs
-after that.
+of wall time (reported as "prewarm"), whatever W is; the probes run after
+the timed steps.
 
 Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
   value          raw bytes per step / ms_per_step, GB/s (1e9); ms_per_step is
@@ -21,7 +21,11 @@ Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
                  on both sides)
   encode/decode  per-kernel time (HIP events on the launch stream, mean,
                  median, min), raw GB/s and algorithmic-HBM GB/s (bytes read
-                 plus bytes written) as a fraction of the 8 TB/s peak
+                 plus bytes written) as a fraction of the 8 TB/s peak and of
+                 the same-mix streaming probe
+  probes         the library's streaming probe moving each kernel's bytes in
+                 its read:write ratio: what a plain streaming kernel achieves
+                 for that mix on this chip
   roofline       the dominant kernel: algorithmic bytes per launch / mean
                  launch time, vs 8 TB/s
   break_even     encode + decode time vs the wire time the compression saves
@@ -113,8 +117,10 @@ def parse(argv=None):
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="seconds of back-to-back encode + decode before the warm-up steps")
     ap.add_argument("--workload", default="llama3_8b_4k")
-    ap.add_argument("--other-steps", type=int, default=10,
+    ap.add_argument("--other-steps", type=int, default=20,
                     help="timed steps of each other workload (0: skip them)")
+    ap.add_argument("--other-prewarm-s", type=float, default=0.3,
+                    help="seconds of back-to-back encode + decode before each other workload's steps")
     ap.add_argument("--cpu-sample-chunks", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true", help="skip the separate-kernel comparator")
@@ -359,25 +365,43 @@ def pipeline_leg(kvc, p, x, xout, stream, raw_bytes, reps=3, chunk_layers=8):
     }
 
 
-def copy_probe(kvc, dev, stream, reps=40):
-    """GB/s (read + write) of a 1 GiB device copy by the library's streaming
-    copy kernel, averaged over the last half of `reps` copies."""
+def mix_probe(kvc, src, read_bytes, dst, write_bytes, stream, reps=5):
+    """Best GB/s (read + write) of the library's streaming probe moving the
+    same bytes in the same read:write ratio, over 4, 8 and 16 waves per CU:
+    the achievable-bandwidth yardstick for a kernel with that traffic mix.
+    It overwrites dst."""
     import torch
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(reps // 2):
-        kvc.probe_copy(src, dst)
-    ev = TimingEvents(2)
-    ev.record(0, stream)
-    for _ in range(reps - reps // 2):
-        kvc.probe_copy(src, dst)
-    ev.record(1, stream)
-    torch.cuda.synchronize()
-    gbps = 2 * src.numel() * (reps - reps // 2) / (ev.ms(0, 1) / 1e3) / 1e9
-    ev.close()
-    del src, dst
-    torch.cuda.empty_cache()
-    return gbps
+    rb, wb = read_bytes // 1024 * 1024, write_bytes // 1024 * 1024
+    best = None
+    for wpc in (4, 8, 16):
+        for _ in range(2):
+            kvc.probe_stream(src, rb, dst, wb, waves_per_cu=wpc)
+        ev = TimingEvents(2)
+        ev.record(0, stream)
+        for _ in range(reps):
+            kvc.probe_stream(src, rb, dst, wb, waves_per_cu=wpc)
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        gbps = (rb + wb) * reps / (ev.ms(0, 1) / 1e3) / 1e9
+        ev.close()
+        if best is None or gbps > best["GBps"]:
+            best = {"GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS, "waves_per_cu": wpc}
+    best.update(read_bytes=rb, write_bytes=wb)
+    return best
+
+
+def leg_probes(kvc, leg, stream, enc, dec):
+    """Same-mix yardsticks of the encode and the decode of a leg, and each
+    kernel's fraction of its yardstick."""
+    src = leg.src[0].view(-1).view(__import__("torch").uint8)
+    dst = leg.dsts[0].view(-1).view(__import__("torch").uint8)
+    pe = mix_probe(kvc, src, leg.raw_bytes, leg.outs[0], leg.enc_bytes, stream)
+    pd = mix_probe(kvc, leg.outs[0], leg.enc_bytes, dst, leg.raw_bytes, stream)
+    enc["frac_same_mix_probe"] = enc["hbm_GBps"] / pe["GBps"]
+    dec["frac_same_mix_probe"] = dec["hbm_GBps"] / pd["GBps"]
+    return {"encode_mix": pe, "decode_mix": pd,
+            "what": "library streaming probe reading and writing the kernel's bytes in its ratio, "
+                    "best of 4/8/16 waves per CU"}
 
 
 class Leg:
@@ -476,16 +500,13 @@ def _stats(ms):
     return sum(ms) / len(ms), srt[len(srt) // 2], srt[0]
 
 
-def kernel_summary(leg, ms, copy_gbps=None):
+def kernel_summary(leg, ms):
     mean, med, mn = _stats(ms)
     t = mean / 1e3
     alg = leg.algo_bytes / t / 1e9
-    out = {"raw_GBps": leg.raw_bytes / t / 1e9, "hbm_GBps": alg, "frac_hbm_peak": alg / HBM_PEAK_GBPS,
-           "frac_hbm_peak_median": leg.algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS,
-           "ms": mean, "ms_median": med, "ms_min": mn}
-    if copy_gbps:
-        out["frac_copy_probe"] = alg / copy_gbps
-    return out
+    return {"raw_GBps": leg.raw_bytes / t / 1e9, "hbm_GBps": alg, "frac_hbm_peak": alg / HBM_PEAK_GBPS,
+            "frac_hbm_peak_median": leg.algo_bytes / (med / 1e3) / 1e9 / HBM_PEAK_GBPS,
+            "ms": mean, "ms_median": med, "ms_min": mn}
 
 
 def break_even(leg, t_enc, t_dec):
@@ -500,13 +521,13 @@ def break_even(leg, t_enc, t_dec):
     return be
 
 
-def other_workload(kvc, name, dev, stream, steps):
-    """The same protocol on another workload: a short pre-warm, 3 warm-up
+def other_workload(kvc, name, dev, stream, steps, prewarm_s):
+    """The same protocol on another workload: a shorter pre-warm, 3 warm-up
     steps, `steps` timed steps; tiny reports latency."""
     from kv_cache_compression_kvc_amd import presets
     p = presets.preset(name)
     leg = Leg(kvc, p, dev, nsets=1)
-    leg.prewarm(0.05)
+    leg.prewarm(prewarm_s)
     for i in range(3):
         leg.enc(i)
         leg.dec(i)
@@ -520,6 +541,7 @@ def other_workload(kvc, name, dev, stream, steps):
         out.update(encode=e, decode=d, ms_per_step=wall / steps * 1e3,
                    raw_GBps_step=leg.raw_bytes / (wall / steps) / 1e9,
                    traffic={"encode": counter_traffic(name, "encode"), "decode": counter_traffic(name, "decode")})
+        out["probes"] = leg_probes(kvc, leg, stream, e, d)
     out["break_even"] = break_even(leg, e["ms"] / 1e3, d["ms"] / 1e3)
     leg.close()
     return out
@@ -545,11 +567,12 @@ def main():
     leg = Leg(kvc, p, dev, nsets=2)
 
     # pre-warm to steady clocks (time-based, independent of --warmup), then
-    # the copy probe, then the warm-up steps
+    # the warm-up steps, then the timed steps; the copy probe runs after them
+    # (a 2 GiB copy right before the timed steps slowed the next ones by up
+    # to 10%)
     t0 = time.perf_counter()
     prewarm_steps = leg.prewarm(a.prewarm_s)
     prewarm = {"seconds": time.perf_counter() - t0, "steps": prewarm_steps}
-    copy_gbps = copy_probe(kvc, dev, stream)
     for i in range(a.warmup):
         leg.enc(i)
         leg.dec(i)
@@ -557,8 +580,9 @@ def main():
 
     wall, enc_ms, dec_ms = leg.timed(a.steps, stream)
     ms_per_step = wall / a.steps * 1e3
-    enc, dec = kernel_summary(leg, enc_ms, copy_gbps), kernel_summary(leg, dec_ms, copy_gbps)
+    enc, dec = kernel_summary(leg, enc_ms), kernel_summary(leg, dec_ms)
     t_enc, t_dec = enc["ms"] / 1e3, dec["ms"] / 1e3
+    probes = leg_probes(kvc, leg, stream, enc, dec)
 
     unfused = pipeline = None
     if not p.paged and not a.no_unfused:
@@ -587,7 +611,7 @@ def main():
         "encode": enc,
         "decode": dec,
         "bytes": {"raw": leg.raw_bytes, "encoded": leg.enc_bytes, "ratio": leg.raw_bytes / leg.enc_bytes},
-        "copy_probe_GBps": copy_gbps,
+        "probes": probes,
         "break_even": break_even(leg, t_enc, t_dec),
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
@@ -600,7 +624,7 @@ def main():
     }
     leg.close()
     if a.other_steps > 0:
-        result["workloads"] = {name: other_workload(kvc, name, dev, stream, a.other_steps)
+        result["workloads"] = {name: other_workload(kvc, name, dev, stream, a.other_steps, a.other_prewarm_s)
                                for name in presets.ORDER if name != p.name}
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, a.cpu_sample_chunks)

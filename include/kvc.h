@@ -303,6 +303,19 @@ kvc_status kvc_receive_decode(const kvc_desc* desc, const void* src, uint64_t sr
  */
 kvc_status kvc_probe_copy(const void* src, void* dst, uint64_t bytes, void* stream);
 
+/*
+ * Measurement helper: read `read_bytes` of src and write `write_bytes` of
+ * dst (both multiples of 1024; pointers 16-byte aligned; src and dst must
+ * not overlap) with 16-byte streaming accesses, the two streams interleaved
+ * at their ratio (4 KiB runs of the larger one, grid-strided) across
+ * waves_per_cu (1..32) one-wave workgroups per CU.  With the read and write sizes of an encode or a
+ * decode it is the achievable-bandwidth yardstick for that traffic mix.
+ * dst receives unspecified bytes.  Errors: KVC_EINVAL (null pointer with a
+ * nonzero size, waves_per_cu out of range), KVC_EALIGN.
+ */
+kvc_status kvc_probe_stream(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes,
+                            int32_t waves_per_cu, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ from ._lib import KvcDesc, KvcPaged, KvcError, DTYPE
 
 __all__ = [
     "KvcError", "DTYPE", "abi_version", "encoded_size", "sign_mask", "encode", "decode",
-    "paged_layout", "encode_paged", "decode_paged", "debug_rotate", "probe_copy",
+    "paged_layout", "encode_paged", "decode_paged", "debug_rotate", "probe_copy", "probe_stream",
     "unfused_workspace_size", "encode_unfused", "decode_unfused", "encode_unfused_noalloc",
     "chunked_size", "encode_send", "receive_decode",
 ]
@@ -334,4 +334,15 @@ def probe_copy(src, dst, stream=None):
     if _nbytes(dst) < nbytes:
         raise ValueError("destination too small")
     _lib.check(_lib.lib().kvc_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+    return dst
+
+
+def probe_stream(src, read_bytes, dst, write_bytes, waves_per_cu=8, stream=None):
+    """Streaming yardstick: read ``read_bytes`` of ``src`` and write
+    ``write_bytes`` of ``dst`` (multiples of 1024, within the tensors)."""
+    _check_cuda(src, dst)
+    if read_bytes > _nbytes(src) or write_bytes > _nbytes(dst):
+        raise ValueError("probe sizes exceed the tensors")
+    _lib.check(_lib.lib().kvc_probe_stream(_ptr(src), int(read_bytes), _ptr(dst), int(write_bytes),
+                                           int(waves_per_cu), _stream(stream)))
     return dst

@@ -28,7 +28,7 @@ EXPORTS = [
     "kvc_decode", "kvc_paged_layout", "kvc_encode_paged", "kvc_decode_paged",
     "kvc_debug_rotate", "kvc_unfused_workspace_size", "kvc_encode_unfused", "kvc_decode_unfused",
     "kvc_chunked_size", "kvc_encode_send", "kvc_receive_decode", "kvc_probe_copy",
-    "kvc_encode_unfused_noalloc",
+    "kvc_encode_unfused_noalloc", "kvc_probe_stream",
 ]
 NOALLOC_WORKSPACE_BYTES = 64 << 20   # KVC_NOALLOC_WORKSPACE_BYTES
 HOST_EXPORTS = ["kvc_abi_version", "kvc_strerror", "kvc_encoded_size", "kvc_sign_mask",
@@ -105,6 +105,8 @@ def _declare(lib, names):
         "kvc_receive_decode": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                                 ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p]),
+        "kvc_probe_stream": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
+                                              ctypes.c_int32, ctypes.c_void_p]),
         "kvc_probe_copy": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                             ctypes.c_void_p]),
     }

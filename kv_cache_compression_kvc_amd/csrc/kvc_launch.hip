@@ -34,6 +34,59 @@ __global__ __launch_bounds__(256) void copy_kernel(const v4u* __restrict__ src, 
   for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+/* Streaming mix of reads and writes at a fixed ratio: nr 1 KiB chunks of src
+ * read and nw written to dst (a chunk: 64 lanes x 16 bytes).  The larger
+ * stream is walked in runs of 4 consecutive chunks, grid-strided; the run
+ * covering chunks [4u, 4u + 4) of it also moves chunks [floor(4u * ns / nl),
+ * floor((4u + 4) * ns / nl)) of the smaller stream, so the two keep their
+ * ratio at every point.  The stored data does not depend on the loads.  The
+ * yardstick for a kernel with the same traffic mix. */
+__global__ __launch_bounds__(64) void stream_kernel(const v4u* __restrict__ src, uint64_t nr, v4u* __restrict__ dst,
+                                                    uint64_t nw) {
+  const uint64_t nl = nr > nw ? nr : nw, ns = nr > nw ? nw : nr;
+  const bool reads_lead = nr >= nw;
+  const int lane = threadIdx.x;
+  v4u acc = {0, 0, 0, 0};
+  const uint64_t nu = (nl + 3) / 4, u0 = blockIdx.x, g = gridDim.x;
+  // lo = floor(4u * ns / nl) with remainder, carried along without divisions
+  uint64_t lo = 4 * u0 * ns / nl, rem = 4 * u0 * ns - lo * nl;
+  const uint64_t dq = 4 * g * ns / nl, dr = 4 * g * ns - dq * nl;
+  for (uint64_t u = u0; u < nu; u += g) {
+    const uint64_t c0 = 4 * u;
+    uint64_t hi = ns;
+    if (c0 + 4 <= nl) {  // floor((4u + 4) * ns / nl) = lo + floor((rem + 4 ns) / nl), at most lo + 4
+      uint64_t t = rem + 4 * ns;
+      hi = lo;
+      while (t >= nl) {
+        t -= nl;
+        ++hi;
+      }
+    }
+    const uint64_t n_lead = nl - c0 < 4 ? nl - c0 : 4;
+    for (uint64_t k = 0; k < n_lead; ++k) {
+      const uint64_t c = c0 + k;
+      if (reads_lead)
+        acc ^= __builtin_nontemporal_load(src + c * 64 + lane);
+      else
+        __builtin_nontemporal_store(v4u{uint32_t(c), uint32_t(lane), 0u, 0u}, dst + c * 64 + lane);
+    }
+    for (uint64_t c = lo; c < hi; ++c) {
+      if (reads_lead)
+        __builtin_nontemporal_store(v4u{uint32_t(c), uint32_t(lane), 0u, 0u}, dst + c * 64 + lane);
+      else
+        acc ^= __builtin_nontemporal_load(src + c * 64 + lane);
+    }
+    lo += dq;
+    rem += dr;
+    if (rem >= nl) {
+      rem -= nl;
+      lo += 1;
+    }
+  }
+  // the loaded data is consumed here, so the loads stay
+  asm volatile("" ::"v"(acc.x), "v"(acc.y), "v"(acc.z), "v"(acc.w));
+}
+
 }  // namespace dev
 
 namespace {
@@ -116,7 +169,8 @@ constexpr uint64_t kDecodeLargeBlobD128 = uint64_t(512) << 20;
  *     2-11% faster than kDecodeLarge on 0.3-2 GB blobs of 2-bit, 8-bit or
  *     grouped codes and on 4-bit G128 blobs up to 408 MiB; only 4-bit codes
  *     with G = 128 past kDecodeLargeBlobD128 keep kDecodeLarge (1.4-3.8%
- *     faster from 544 MiB up);
+ *     faster from 544 MiB up).  From kDecodeThreePerCuBlob of blob, three
+ *     waves per CU rather than one per SIMD (below);
  *   - a smaller blob: kDecodeWaitStores at one wave per SIMD, 5.6-6.6%
  *     faster than kDecodeWaitTop at two waves (8B-4k, and head_dim 64 at 8k
  *     tokens);
@@ -125,12 +179,23 @@ constexpr uint64_t kDecodeLargeBlobD128 = uint64_t(512) << 20;
  *     at head_dim 64, where one wave lost 16%.
  * Grids between one and two waves per SIMD leave some SIMDs with a wave more
  * than others; with a static tile split those finish last, and such grids
- * measured slower than either.
+ * measured slower than either -- except the write-heavy large decode, where
+ * three waves per CU (fewer concurrent write streams) beat one per SIMD.
+ * For scale: plain streaming kernels on this chip reach about 0.68 of the
+ * 8 TB/s peak for the decode's mix of one byte read to four written, 0.78
+ * for the encode's four to one, and 0.72 for writes alone.
  */
 struct LaunchShape {
   int waves_per_simd;
   int mode;
+  int waves_per_cu;   // when > 0, the grid is this many waves per CU instead
 };
+
+/* Blob size from which a contiguous decode in kDecodeWaitStores mode runs
+ * three waves per CU instead of one per SIMD: on the 4 GiB 2-bit G32 cache
+ * (1.02 GB blob) that measured 2-3% faster; at 512 MiB of input (136 MiB of
+ * blob) one wave per SIMD stays the faster. */
+constexpr uint64_t kDecodeThreePerCuBlob = uint64_t(384) << 20;
 
 /* Whether a contiguous decode launch of `bits`-bit codes takes kDecodeLarge. */
 bool decode_large(const LaunchArgs& a, int head_dim, int bits) {
@@ -139,10 +204,12 @@ bool decode_large(const LaunchArgs& a, int head_dim, int bits) {
 }
 
 LaunchShape launch_shape(Op op, const LaunchArgs& a, int head_dim, int bits) {
-  if (op == Op::Encode) return {(a.paged && head_dim == 64) ? 0 : 1, 0};
-  if (op != Op::Decode) return {0, 0};
-  if (a.paged) return head_dim == 64 ? LaunchShape{2, dev::kDecodeWaitTop} : LaunchShape{1, dev::kDecodeWaitStores};
-  return decode_large(a, head_dim, bits) ? LaunchShape{1, dev::kDecodeLarge} : LaunchShape{1, dev::kDecodeWaitStores};
+  if (op == Op::Encode) return {(a.paged && head_dim == 64) ? 0 : 1, 0, 0};
+  if (op != Op::Decode) return {0, 0, 0};
+  if (a.paged)
+    return head_dim == 64 ? LaunchShape{2, dev::kDecodeWaitTop, 0} : LaunchShape{1, dev::kDecodeWaitStores, 0};
+  if (decode_large(a, head_dim, bits)) return {1, dev::kDecodeLarge, 0};
+  return {1, dev::kDecodeWaitStores, a.blob_total >= kDecodeThreePerCuBlob ? 3 : 0};
 }
 
 int run_plan(Op op, const Plan& plan, void* stream) {
@@ -154,9 +221,10 @@ int run_plan(Op op, const Plan& plan, void* stream) {
     int cus = 0;
     int st = resident_groups(k, 64, &resident, &cus);
     if (st != KVC_OK) return st;
-    const int64_t waves =
+    int64_t waves =
         shape.waves_per_simd > 0 ? std::min<int64_t>(resident, int64_t(cus) * kSimdsPerCu * shape.waves_per_simd)
                                  : resident;
+    if (shape.waves_per_cu > 0) waves = std::min<int64_t>(resident, int64_t(cus) * shape.waves_per_cu);
     // a paged call runs one launch per chunk of kReqChunk requests
     const int chunks = plan.args[i].paged ? plan.req_chunks : 1;
     for (int c = 0; c < chunks; ++c) {
@@ -214,6 +282,25 @@ kvc_status kvc_debug_rotate(const kvc_desc* desc, const void* kv, float* y_out, 
   int st = kvc::plan_contiguous(kvc::Op::Rotate, desc, kv, y_out, 0, &plan);
   if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Rotate, plan, stream);
   return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_probe_stream(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes,
+                            int32_t waves_per_cu, void* stream) {
+  if (read_bytes == 0 && write_bytes == 0) return KVC_OK;
+  if ((read_bytes && !src) || (write_bytes && !dst) || waves_per_cu < 1 || waves_per_cu > 32) return KVC_EINVAL;
+  if ((read_bytes & 1023u) || (write_bytes & 1023u) || (reinterpret_cast<uintptr_t>(src) & 15u) ||
+      (reinterpret_cast<uintptr_t>(dst) & 15u))
+    return KVC_EALIGN;
+  int device = 0, cus = 0;
+  if (hipGetDevice(&device) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+    return KVC_EHIP;
+  const uint64_t nr = read_bytes / 1024, nw = write_bytes / 1024;
+  const uint64_t grid = std::min<uint64_t>(uint64_t(cus) * uint64_t(waves_per_cu), std::max(nr, nw));
+  hipLaunchKernelGGL(kvc::dev::stream_kernel, dim3(static_cast<unsigned>(grid)), dim3(64), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const kvc::dev::v4u*>(src), nr,
+                     static_cast<kvc::dev::v4u*>(dst), nw);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_EHIP;
 }
 
 kvc_status kvc_probe_copy(const void* src, void* dst, uint64_t bytes, void* stream) {

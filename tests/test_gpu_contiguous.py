@@ -145,6 +145,24 @@ def test_side_stream_and_seeds():
     parity.check_blob(inputs.as_u16(x), blob.cpu().numpy(), "bf16", 4, 4, 128, p.seed)
 
 
+def test_probe_stream_stays_in_bounds():
+    """The same-mix yardstick reads and writes only the sizes it is given, at
+    any ratio, with any grid."""
+    src = torch.randint(0, 255, (1 << 22,), dtype=torch.uint8, device=DEV)
+    for rb, wb, wpc in ((1 << 22, 1 << 20, 4), (1 << 20, 1 << 22, 8), (1 << 22, 0, 16), (0, 1 << 21, 8),
+                        (1024 * 37, 1024 * 5, 1), (1024 * 5, 1024 * 37, 32)):
+        whole, dst = gpu_util.guarded(max(wb, 1024) + 4096, DEV)
+        dst.fill_(0x5A)
+        kvc.probe_stream(src, rb, dst, wb, waves_per_cu=wpc)
+        torch.cuda.synchronize()
+        assert gpu_util.canaries_intact(whole), (rb, wb)
+        assert bool((dst[wb:] == 0x5A).all()), (rb, wb)
+    with pytest.raises(kvc.KvcError, match="KVC_EALIGN"):
+        kvc.probe_stream(src, 1000, src, 0)
+    with pytest.raises(kvc.KvcError, match="KVC_EINVAL"):
+        kvc.probe_stream(src, 1024, src, 0, waves_per_cu=33)
+
+
 def test_probe_copy():
     a = torch.randint(0, 255, (1 << 24,), dtype=torch.uint8, device=DEV)
     b = torch.zeros_like(a)
@@ -260,15 +278,19 @@ def _tokens_for(D, bk, bv, G, H, target):
 # (head_dim, bits_k, bits_v, group, MiB of one layer's blob, line in MiB)
 LARGE_GRID = [(64, b, b, G, 120, 192) for b in (2, 4, 8) for G in (32, 64)]
 LARGE_GRID += [(128, 4, 4, 128, 300, 512), (128, 2, 4, 128, 300, 512)]
+# from 384 MiB of blob the matrix-core decode runs three waves per CU instead
+# of one per SIMD: a two-layer blob past that line against each layer alone
+LARGE_GRID += [(128, 2, 2, 32, 250, 384), (128, 8, 4, 64, 250, 384)]
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("D,bk,bv,G,layer_mib,line_mib", LARGE_GRID)
 def test_large_blob_decode_matches_per_layer(D, bk, bv, G, layer_mib, line_mib):
-    """Two layers whose blob is past the line decode with the butterfly
-    variant (one wave per SIMD); each layer alone, below the line, decodes on
-    the matrix cores.  Both must give the same bits; the slabs end in a
-    partial tile (8 heads, tokens 3 past a multiple of 64)."""
+    """Two layers whose blob is past the line decode with another launch
+    shape (the butterfly variant at one wave per SIMD, or the matrix cores at
+    three waves per CU); each layer alone, below the line, decodes on the
+    matrix cores at one wave per SIMD.  Both must give the same bits; the
+    slabs end in a partial tile (8 heads, tokens 3 past a multiple of 64)."""
     dtype = "bf16" if G != 64 else "fp16"
     T = _tokens_for(D, bk, bv, G, 8, layer_mib << 20)
     p = _small(D, dtype, bk, bv, G, L=2, T=T, H=8)
