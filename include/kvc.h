@@ -67,6 +67,18 @@
  * the rotated values y must fit the fp16 range of the meta (|y| <= 65504);
  * a group that breaks this gets unspecified meta and codes (nothing is read
  * or written out of bounds).  Subnormal inputs are handled exactly.
+ *
+ * Precision.  The transform's sums are binary32, and the meta and the codes
+ * are decided in binary32 (1/sqrt(D) folded into the meta, t = fma(u, A, B)
+ * with A = rs / scale and B = -zero / scale, each rounded once).  A stored
+ * zero or scale is then within one fp16 step of the definition above, and a
+ * code is the nearest level of the stored meta except where the exact t
+ * lies within a few 2^-24 of (|y| + |zero|) / scale of a rounding boundary
+ * k + 1/2: within 1e-5 for 2- and 4-bit codes of ordinary data, about 1e-4
+ * (2^-13) for 8-bit codes, whose t reaches 255.  In a group whose range is
+ * comparable with the binary32 resolution of its values (a huge offset
+ * with a tiny range) the codes are only as good as that resolution; they
+ * always stay within [0, 2^b - 1].
  */
 #ifndef KVC_H
 #define KVC_H
@@ -118,20 +130,24 @@ typedef struct kvc_desc {
  * those offsets.  All three arrays live in device memory.
  *
  * Device-side checks: an entry of block_table outside [0, num_blocks), a
- * length above max_blocks*block_size or below 0, or a request blob that
- * would end past the output buffer makes the kernel skip that work and
- * set bit 0 of *err_flag (if err_flag is not NULL); such work is never
- * read or written out of bounds.
+ * length above max_blocks*block_size or below 0, or a request blob offset
+ * that is negative, not a multiple of 16 or whose blob would end past the
+ * output buffer makes the kernel skip that work (the block, or the whole
+ * request) and set bit 0 of *err_flag (if err_flag is not NULL); such work
+ * is never read or written out of bounds.  Overlap between request blobs
+ * is not checked (the caller's guarantee).
  */
 typedef struct kvc_paged {
   int64_t num_blocks;          /* physical blocks in the pool               */
   int32_t block_size;          /* tokens per block, 1..1024                 */
   int32_t num_reqs;            /* R >= 0                                    */
-  int32_t max_blocks;          /* row length of block_table, >= 0           */
+  int32_t max_blocks;          /* row length of block_table, >= 0;
+                                  max_blocks * block_size <= INT32_MAX      */
   int32_t reserved;            /* must be 0                                 */
   const int32_t* block_table;  /* device, [num_reqs][max_blocks]            */
   const int32_t* seq_lens;     /* device, [num_reqs]                        */
-  const int64_t* out_offsets;  /* device, [num_reqs]; multiples of 16       */
+  const int64_t* out_offsets;  /* device, [num_reqs]; multiples of 16, the
+                                  request blobs disjoint                    */
   int32_t* err_flag;           /* device, optional: bit 0 set on bad input  */
 } kvc_paged;
 
@@ -144,7 +160,11 @@ const char* kvc_strerror(int32_t status);
 /*
  * Blob size for `tokens` tokens of the shape in `desc` (desc->tokens is
  * ignored).  *total receives the size in bytes, *meta_offset (may be
- * NULL) the byte offset of the meta section.  Host only.
+ * NULL) the byte offset of the meta section.  Host only.  The byte format
+ * is this library's own (the layout above): the pages describe compressing
+ * the KV cache before it crosses the prefill-to-decode link but define no
+ * format.  Errors: KVC_EINVAL (null total), the descriptor's errors,
+ * KVC_ESHAPE when a size overflows.
  */
 kvc_status kvc_encoded_size(const kvc_desc* desc, int64_t tokens,
                             uint64_t* total, uint64_t* meta_offset);
@@ -152,23 +172,38 @@ kvc_status kvc_encoded_size(const kvc_desc* desc, int64_t tokens,
 /*
  * The D signs of the transform as a bit mask: bit j of mask_words[j / 64]
  * is set iff s_j = -1.  mask_words holds (head_dim + 63) / 64 words.  Host
- * only; the same generator the kernels use.
+ * only; the same generator the kernels use.  The signs are the "randomized"
+ * part of the randomized Hadamard transform of the episode notes of
+ * "FastKVComp: checking whether high-throughput KV compression pays off";
+ * the pages do not say how they are drawn (SplitMix64 is this library's
+ * reading).  Errors: KVC_EINVAL (null mask, head_dim outside 1..4096).
  */
 kvc_status kvc_sign_mask(uint64_t seed, int64_t head_dim, uint64_t* mask_words);
 
 /*
- * Encode a contiguous KV tensor.  kv: device [L, 2, T, H, D] of desc->dtype.
- * out: device buffer of out_bytes >= kvc_encoded_size(desc, T); the blob is
- * written to its first `total` bytes (padding bytes are written as zero).
+ * Encode a contiguous KV tensor: the randomized Hadamard transform and the
+ * low-bit quantization of the episode notes of "FastKVComp: checking
+ * whether high-throughput KV compression pays off", fused in one pass with
+ * no full-size intermediate as the abstract of "Beyond Compression Ratio:
+ * High-Throughput KV Compression for Disaggregated LLM Serving" describes.
+ * kv: device [L, 2, T, H, D] of desc->dtype (read only).  out: device buffer
+ * of out_bytes >= kvc_encoded_size(desc, T), owned by the caller; the blob
+ * is written to its first `total` bytes (padding bytes as zero), nothing
+ * past them.  Errors: the descriptor's, KVC_EINVAL (null pointer with a
+ * nonempty tensor), KVC_EALIGN, KVC_ENOSPC, KVC_EHIP.
  */
 kvc_status kvc_encode(const kvc_desc* desc, const void* kv, void* out,
                       uint64_t out_bytes, void* stream);
 
 /*
  * Decode a blob written by kvc_encode (same desc) into a contiguous
- * device tensor kv_out [L, 2, T, H, D] of desc->dtype.  Its size is not
- * passed: the caller guarantees L*2*T*H*D elements of desc->dtype, all of
- * which are written.
+ * device tensor kv_out [L, 2, T, H, D] of desc->dtype: unpack, dequantize,
+ * inverse transform -- the receiving side whose time the episode notes of
+ * "FastKVComp: checking whether high-throughput KV compression pays off"
+ * add to the encode's in the break-even.  in: in_bytes >= the blob size
+ * (read only).  kv_out's size is not passed: the caller guarantees
+ * L*2*T*H*D elements of desc->dtype, all of which are written.  Errors as
+ * kvc_encode (KVC_ENOSPC: in_bytes too small).
  */
 kvc_status kvc_decode(const kvc_desc* desc, const void* in, uint64_t in_bytes,
                       void* kv_out, void* stream);
@@ -176,17 +211,30 @@ kvc_status kvc_decode(const kvc_desc* desc, const void* in, uint64_t in_bytes,
 /*
  * Host prologue of the paged calls: offsets_host[r] = sum of the blob
  * sizes of requests 0..r-1 (each a multiple of 256), *total = the sum of
- * all of them.  seq_lens_host and offsets_host are host arrays of
- * num_reqs entries.
+ * all of them; these offsets are disjoint by construction.  seq_lens_host
+ * and offsets_host are host arrays of num_reqs entries owned by the caller.
+ * Errors: KVC_EINVAL (null pointer, negative length), the descriptor's,
+ * KVC_ESHAPE on overflow.
  */
 kvc_status kvc_paged_layout(const kvc_desc* desc, const int32_t* seq_lens_host,
                             int32_t num_reqs, int64_t* offsets_host, uint64_t* total);
 
 /*
- * Encode every request of a paged pool.  pool: device
- * [L, 2, num_blocks, block_size, H, D] of desc->dtype; out: device buffer
- * of out_bytes; request r's blob at out + out_offsets[r].  Only the first
- * seq_lens[r] tokens of each request are read.
+ * Encode every request of a paged pool -- the KV cache as a serving engine
+ * holds it, in blocks, compressed per request before it crosses the
+ * prefill-to-decode link (abstract of "Beyond Compression Ratio:
+ * High-Throughput KV Compression for Disaggregated LLM Serving").  pool:
+ * device [L, 2, num_blocks, block_size, H, D] of desc->dtype (read only);
+ * out: device buffer of out_bytes; request r's blob (the contiguous layout
+ * with T = seq_lens[r]) at out + out_offsets[r].  Only the first
+ * seq_lens[r] tokens of each request are read.  The request blobs
+ * [out_offsets[r], out_offsets[r] + size_r) must be disjoint (the caller's
+ * guarantee; kvc_paged_layout's offsets are): overlapping blobs race.
+ * Requests are processed in launches of at most 64.  Errors (host): the
+ * descriptor's, KVC_EINVAL, KVC_EALIGN, KVC_ERANGE (block_size outside
+ * 1..1024, max_blocks * block_size above INT32_MAX, or more than INT32_MAX
+ * items of 64 vectors in a 64-request launch), KVC_EHIP; on the device,
+ * the checks of struct kvc_paged set *err_flag.
  */
 kvc_status kvc_encode_paged(const kvc_desc* desc, const void* pool,
                             const kvc_paged* paged, void* out, uint64_t out_bytes,
@@ -194,16 +242,21 @@ kvc_status kvc_encode_paged(const kvc_desc* desc, const void* pool,
 
 /*
  * Decode every request's blob back into the pool slots named by the block
- * table; slots past seq_lens[r] and blocks no request names are left
- * untouched.
+ * table (in: in_bytes, read only; pool written); slots past seq_lens[r]
+ * and blocks no request names are left untouched.  Two requests must not
+ * name the same pool slot.  Arguments and errors as kvc_encode_paged.
  */
 kvc_status kvc_decode_paged(const kvc_desc* desc, const void* in, uint64_t in_bytes,
                             const kvc_paged* paged, void* pool, void* stream);
 
 /*
  * Test hook: the rotated values y = H (s * x) / sqrt(D) of a contiguous KV
- * tensor, computed by the same device code as kvc_encode, written as fp32
- * to y_out (device, [L, 2, T, H, D]).
+ * tensor -- the randomized Hadamard transform of the episode notes of
+ * "FastKVComp: checking whether high-throughput KV compression pays off" --
+ * computed by the same device code as kvc_encode, written as fp32 to y_out
+ * (device, [L, 2, T, H, D], caller-owned; its size is the caller's
+ * guarantee).  desc's bits and group are validated but unused.  Errors as
+ * kvc_encode.
  */
 kvc_status kvc_debug_rotate(const kvc_desc* desc, const void* kv, float* y_out,
                             void* stream);
