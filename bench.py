@@ -32,7 +32,10 @@ Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
                  at 100 and 400 Gbit/s
   workloads      every other named workload (tiny as latency; the 8B-32k,
                  70B-16k and paged ones as encode / decode fractions of the
-                 peak and break-even), same event protocol, fewer steps
+                 peak and break-even), same event protocol, fewer steps; the
+                 paged pool is visited in pool order (kvc_paged_order, a host
+                 prologue like the offsets), and in request order for
+                 comparison
   pipeline       per-layer chunked encode overlapped with the copy of each
                  chunk to pinned host memory (PCIe standing in for the link),
                  and copy-in overlapped with decode, against the raw copy and
@@ -407,15 +410,20 @@ def leg_probes(kvc, leg, stream, enc, dec):
 class Leg:
     """Device inputs and encode / decode closures of one workload."""
 
-    def __init__(self, kvc, p, dev, nsets):
+    def __init__(self, kvc, p, dev, nsets, pool_order=True):
         import torch
         from kv_cache_compression_kvc_amd import inputs
         L, H, D = p.layers, p.kv_heads, p.head_dim
         self.p, self.nsets = p, nsets
+        self.order = None
         if p.paged:
             lens = inputs.request_lengths(p)
             table, nb = inputs.block_table(p, lens)
             offs, total = kvc.paged_layout(lens, L, H, D, p.bits_k, p.bits_v, p.group, p.dtype)
+            if pool_order:   # host prologue: the (request, block) items sorted by pool block
+                import numpy as np
+                items = kvc.paged_order(table, lens, offs, p.block_size, nb)
+                self.order = torch.from_numpy(items.view(np.uint8)).to(dev)
             self.src = [inputs.make_pool(p, nb, device=dev) for _ in range(nsets)]
             self.outs = [torch.empty(total, dtype=torch.uint8, device=dev) for _ in range(nsets)]
             self.dsts = [torch.empty_like(self.src[0]) for _ in range(nsets)]
@@ -426,7 +434,8 @@ class Leg:
             self.config = {"workload": p.name, "layers": L, "requests": len(lens), "tokens": tokens,
                            "kv_heads": H, "head_dim": D, "storage": p.dtype, "bits_k": p.bits_k,
                            "bits_v": p.bits_v, "group": p.group,
-                           "layout": "paged, %d-token blocks" % p.block_size}
+                           "layout": "paged, %d-token blocks, %s" % (
+                               p.block_size, "visited in pool order" if pool_order else "visited in request order")}
         else:
             self.src = [inputs.make_kv(p, device=dev) for _ in range(nsets)]
             total, _ = kvc.encoded_size(L, p.tokens, H, D, p.bits_k, p.bits_v, p.group, p.dtype)
@@ -444,7 +453,7 @@ class Leg:
         p, k = self.p, i % self.nsets
         if p.paged:
             self.kvc.encode_paged(self.src[k], self.bt, self.sl, self.of, self.total, p.bits_k, p.bits_v, p.group,
-                                  seed=p.seed, out=self.outs[k])
+                                  seed=p.seed, out=self.outs[k], order=self.order)
         else:
             self.kvc.encode(self.src[k], p.bits_k, p.bits_v, p.group, seed=p.seed, out=self.outs[k])
 
@@ -452,7 +461,7 @@ class Leg:
         p, k = self.p, i % self.nsets
         if p.paged:
             self.kvc.decode_paged(self.outs[k], self.dsts[k], self.bt, self.sl, self.of, p.bits_k, p.bits_v, p.group,
-                                  seed=p.seed)
+                                  seed=p.seed, order=self.order)
         else:
             self.kvc.decode(self.outs[k], self.src[k].shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed,
                             out=self.dsts[k])
@@ -491,7 +500,7 @@ class Leg:
 
     def close(self):
         import torch
-        del self.src, self.outs, self.dsts
+        del self.src, self.outs, self.dsts, self.order
         torch.cuda.empty_cache()
 
 
@@ -543,6 +552,11 @@ def other_workload(kvc, name, dev, stream, steps, prewarm_s):
                    traffic={"encode": counter_traffic(name, "encode"), "decode": counter_traffic(name, "decode")})
         out["probes"] = leg_probes(kvc, leg, stream, e, d)
     out["break_even"] = break_even(leg, e["ms"] / 1e3, d["ms"] / 1e3)
+    if p.paged:   # the same pool visited in request order (no host prologue), for comparison
+        leg.order = None
+        leg.prewarm(prewarm_s / 3)
+        _, e2, d2 = leg.timed(steps, stream)
+        out["request_order"] = {"encode": kernel_summary(leg, e2), "decode": kernel_summary(leg, d2)}
     leg.close()
     return out
 

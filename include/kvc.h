@@ -90,8 +90,9 @@
 extern "C" {
 #endif
 
-/* 2: every code and meta slab of the blob padded to a multiple of 256 bytes. */
-#define KVC_ABI_VERSION 2
+/* 2: every code and meta slab of the blob padded to a multiple of 256 bytes.
+ * 3: kvc_paged carries an optional pool-order item list (kvc_paged_order). */
+#define KVC_ABI_VERSION 3
 
 typedef enum kvc_status {
   KVC_OK = 0,
@@ -137,6 +138,20 @@ typedef struct kvc_desc {
  * is never read or written out of bounds.  Overlap between request blobs
  * is not checked (the caller's guarantee).
  */
+/*
+ * One work item of a paged call in pool order: logical block block_index
+ * of request req lives in pool block `block`; the request holds len tokens
+ * and its blob starts at byte offset of the output.  32 bytes.
+ */
+typedef struct kvc_paged_item {
+  int32_t block;        /* pool block                                     */
+  int32_t block_index;  /* logical block j of the request                 */
+  int32_t req;          /* request r                                      */
+  int32_t len;          /* seq_lens[r]                                    */
+  int64_t offset;       /* out_offsets[r]                                 */
+  int64_t reserved;     /* 0                                              */
+} kvc_paged_item;
+
 typedef struct kvc_paged {
   int64_t num_blocks;          /* physical blocks in the pool               */
   int32_t block_size;          /* tokens per block, 1..1024                 */
@@ -149,6 +164,12 @@ typedef struct kvc_paged {
   const int64_t* out_offsets;  /* device, [num_reqs]; multiples of 16, the
                                   request blobs disjoint                    */
   int32_t* err_flag;           /* device, optional: bit 0 set on bad input  */
+  const kvc_paged_item* order; /* device, optional: the call's items sorted
+                                  by pool block (kvc_paged_order); the
+                                  kernels then visit the pool in address
+                                  order and read the request's length and
+                                  offset from the item; NULL: request order */
+  int64_t order_len;           /* items in order (0 when order is NULL)     */
 } kvc_paged;
 
 /* KVC_ABI_VERSION of the built library. */
@@ -220,6 +241,24 @@ kvc_status kvc_paged_layout(const kvc_desc* desc, const int32_t* seq_lens_host,
                             int32_t num_reqs, int64_t* offsets_host, uint64_t* total);
 
 /*
+ * Host prologue of the pool-order paged calls: every (request, logical
+ * block) item of the call -- blocks 0 .. ceil(seq_lens[r] / block_size) - 1
+ * of each request -- with its pool block, length and blob offset, sorted by
+ * pool block (then request, then logical block), so that the kernels sweep
+ * the pool in address order instead of in the block table's random order.
+ * A block that several requests name appears once per request.  Host
+ * arrays: block_table_host [num_reqs][max_blocks], seq_lens_host and
+ * offsets_host [num_reqs] (kvc_paged_layout's offsets).  *n_items receives
+ * the item count; items_host (may be NULL to query it) receives the items.
+ * Errors: KVC_EINVAL (null pointer, negative length or count), KVC_ERANGE
+ * (block_size outside 1..1024, a length above max_blocks * block_size, a
+ * table entry outside [0, num_blocks)).
+ */
+kvc_status kvc_paged_order(const int32_t* block_table_host, int32_t num_reqs, int32_t max_blocks,
+                           const int32_t* seq_lens_host, const int64_t* offsets_host, int32_t block_size,
+                           int64_t num_blocks, kvc_paged_item* items_host, int64_t* n_items);
+
+/*
  * Encode every request of a paged pool -- the KV cache as a serving engine
  * holds it, in blocks, compressed per request before it crosses the
  * prefill-to-decode link (abstract of "Beyond Compression Ratio:
@@ -230,7 +269,11 @@ kvc_status kvc_paged_layout(const kvc_desc* desc, const int32_t* seq_lens_host,
  * seq_lens[r] tokens of each request are read.  The request blobs
  * [out_offsets[r], out_offsets[r] + size_r) must be disjoint (the caller's
  * guarantee; kvc_paged_layout's offsets are): overlapping blobs race.
- * Requests are processed in launches of at most 64.  Errors (host): the
+ * Without an order list, requests are processed in launches of at most 64
+ * and each request's blocks in table order; with one (paged->order), one
+ * launch per code width visits the items in the list's order, and the
+ * list's lengths and offsets are used (they must match seq_lens and
+ * out_offsets for the blobs to be those of the layout).  Errors (host): the
  * descriptor's, KVC_EINVAL, KVC_EALIGN, KVC_ERANGE (block_size outside
  * 1..1024, max_blocks * block_size above INT32_MAX, or more than INT32_MAX
  * items of 64 vectors in a 64-request launch), KVC_EHIP; on the device,

@@ -25,7 +25,7 @@ from ._lib import KvcDesc, KvcPaged, KvcError, DTYPE
 
 __all__ = [
     "KvcError", "DTYPE", "abi_version", "encoded_size", "sign_mask", "encode", "decode",
-    "paged_layout", "encode_paged", "decode_paged", "debug_rotate", "probe_copy", "probe_stream",
+    "paged_layout", "paged_order", "encode_paged", "decode_paged", "debug_rotate", "probe_copy", "probe_stream",
     "unfused_workspace_size", "encode_unfused", "decode_unfused", "encode_unfused_noalloc",
     "chunked_size", "encode_send", "receive_decode",
 ]
@@ -259,6 +259,33 @@ def paged_layout(seq_lens, layers, kv_heads, head_dim, bits_k, bits_v, group, dt
     return offs, total.value
 
 
+PAGED_ITEM = np.dtype([("block", "<i4"), ("block_index", "<i4"), ("req", "<i4"), ("len", "<i4"),
+                       ("offset", "<i8"), ("reserved", "<i8")])
+
+
+def paged_order(block_table, seq_lens, offsets, block_size, num_blocks, lib=None):
+    """Host prologue of the pool-order paged calls: the (request, block) items
+    of the call sorted by pool block, as a numpy array of PAGED_ITEM (upload
+    its bytes, e.g. ``torch.from_numpy(items.view(np.uint8))``, and pass them
+    as ``order=``)."""
+    lib = lib or _lib.lib()
+    table = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    offs = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    if table.ndim != 2 or lens.shape != (table.shape[0],) or offs.shape != lens.shape:
+        raise ValueError("block_table must be [R, max_blocks] with one length and offset per row")
+    R, MB = table.shape
+    P32, P64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    n = ctypes.c_int64()
+    args = (table.ctypes.data_as(P32), R, MB, lens.ctypes.data_as(P32), offs.ctypes.data_as(P64), int(block_size),
+            int(num_blocks))
+    _lib.check(lib.kvc_paged_order(*args, None, ctypes.byref(n)))
+    items = np.zeros(n.value, dtype=PAGED_ITEM)
+    if n.value:
+        _lib.check(lib.kvc_paged_order(*args, ctypes.c_void_p(items.ctypes.data), ctypes.byref(n)))
+    return items
+
+
 def _pool_shape(pool):
     """(L, NB, BS, H, D) of a [L, 2, NB, BS, H, D] pool."""
     if pool.dim() != 6 or pool.shape[1] != 2:
@@ -267,10 +294,11 @@ def _pool_shape(pool):
     return L, NB, BS, H, D
 
 
-def _paged(pool, block_table, seq_lens, out_offsets, err_flag):
+def _paged(pool, block_table, seq_lens, out_offsets, err_flag, order=None):
     """The kernels read seq_lens[r], out_offsets[r] and the first max_blocks
     entries of row r of block_table for every r < R, and write err_flag[0]:
-    the arrays must hold that much."""
+    the arrays must hold that much.  ``order``: an optional device tensor
+    holding PAGED_ITEM entries (a whole number of 32-byte items)."""
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or out_offsets.dtype != torch.int64:
         raise ValueError("block_table / seq_lens must be int32 and out_offsets int64")
     if block_table.dim() != 2:
@@ -280,18 +308,25 @@ def _paged(pool, block_table, seq_lens, out_offsets, err_flag):
         raise ValueError("seq_lens and out_offsets must hold one entry per block_table row (%d)" % R)
     if err_flag is not None and (err_flag.dtype != torch.int32 or err_flag.numel() < 1):
         raise ValueError("err_flag must be an int32 tensor of at least one element")
-    _check_cuda(block_table, seq_lens, out_offsets, err_flag)
+    _check_cuda(block_table, seq_lens, out_offsets, err_flag, order)
+    n_order = 0
+    if order is not None:
+        if _nbytes(order) % PAGED_ITEM.itemsize:
+            raise ValueError("order must hold whole %d-byte items" % PAGED_ITEM.itemsize)
+        n_order = _nbytes(order) // PAGED_ITEM.itemsize
     return KvcPaged(pool.shape[2], pool.shape[3], R, MB, 0, _ptr(block_table).value,
                     _ptr(seq_lens).value, _ptr(out_offsets).value,
-                    _ptr(err_flag).value if err_flag is not None else None)
+                    _ptr(err_flag).value if err_flag is not None else None,
+                    _ptr(order).value if n_order else None, n_order)
 
 
 def encode_paged(pool, block_table, seq_lens, out_offsets, total, bits_k, bits_v, group, seed=0,
-                 out=None, err_flag=None, stream=None):
-    """Encode every request of a [L, 2, NB, BS, H, D] pool into one blob buffer."""
+                 out=None, err_flag=None, stream=None, order=None):
+    """Encode every request of a [L, 2, NB, BS, H, D] pool into one blob buffer
+    (in pool order when ``order`` holds the call's :func:`paged_order` items)."""
     L, NB, BS, H, D = _pool_shape(pool)
     dt = _dtype_name(pool)
-    pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag)
+    pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag, order)
     _check_cuda(pool, out)
     if out is None:
         out = torch.empty(int(total), dtype=torch.uint8, device=pool.device)
@@ -302,11 +337,12 @@ def encode_paged(pool, block_table, seq_lens, out_offsets, total, bits_k, bits_v
 
 
 def decode_paged(blob, pool, block_table, seq_lens, out_offsets, bits_k, bits_v, group, seed=0,
-                 err_flag=None, stream=None):
-    """Decode every request's blob back into the pool slots of its block table."""
+                 err_flag=None, stream=None, order=None):
+    """Decode every request's blob back into the pool slots of its block table
+    (in pool order when ``order`` holds the call's :func:`paged_order` items)."""
     L, NB, BS, H, D = _pool_shape(pool)
     dt = _dtype_name(pool)
-    pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag)
+    pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag, order)
     _check_cuda(blob, pool)
     d = _desc(L, 0, H, D, dt, bits_k, bits_v, group, seed)
     _lib.check(_lib.lib().kvc_decode_paged(ctypes.byref(d), _ptr(blob), _nbytes(blob), ctypes.byref(pg),

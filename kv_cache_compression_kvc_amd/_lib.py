@@ -28,11 +28,11 @@ EXPORTS = [
     "kvc_decode", "kvc_paged_layout", "kvc_encode_paged", "kvc_decode_paged",
     "kvc_debug_rotate", "kvc_unfused_workspace_size", "kvc_encode_unfused", "kvc_decode_unfused",
     "kvc_chunked_size", "kvc_encode_send", "kvc_receive_decode", "kvc_probe_copy",
-    "kvc_encode_unfused_noalloc", "kvc_probe_stream",
+    "kvc_encode_unfused_noalloc", "kvc_probe_stream", "kvc_paged_order",
 ]
 NOALLOC_WORKSPACE_BYTES = 64 << 20   # KVC_NOALLOC_WORKSPACE_BYTES
 HOST_EXPORTS = ["kvc_abi_version", "kvc_strerror", "kvc_encoded_size", "kvc_sign_mask",
-                "kvc_paged_layout", "kvc_unfused_workspace_size", "kvc_chunked_size"]
+                "kvc_paged_layout", "kvc_unfused_workspace_size", "kvc_chunked_size", "kvc_paged_order"]
 
 
 class KvcDesc(ctypes.Structure):
@@ -60,6 +60,19 @@ class KvcPaged(ctypes.Structure):
         ("seq_lens", ctypes.c_void_p),
         ("out_offsets", ctypes.c_void_p),
         ("err_flag", ctypes.c_void_p),
+        ("order", ctypes.c_void_p),
+        ("order_len", ctypes.c_int64),
+    ]
+
+
+class KvcPagedItem(ctypes.Structure):
+    _fields_ = [
+        ("block", ctypes.c_int32),
+        ("block_index", ctypes.c_int32),
+        ("req", ctypes.c_int32),
+        ("len", ctypes.c_int32),
+        ("offset", ctypes.c_int64),
+        ("reserved", ctypes.c_int64),
     ]
 
 
@@ -82,6 +95,9 @@ def _declare(lib, names):
                                         ctypes.c_uint64, ctypes.c_void_p]),
         "kvc_decode": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_uint64,
                                         ctypes.c_void_p, ctypes.c_void_p]),
+        "kvc_paged_order": (ctypes.c_int32, [P(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32),
+                                             P(ctypes.c_int64), ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                             P(ctypes.c_int64)]),
         "kvc_paged_layout": (ctypes.c_int32, [P(KvcDesc), P(ctypes.c_int32), ctypes.c_int32,
                                               P(ctypes.c_int64), P(ctypes.c_uint64)]),
         "kvc_encode_paged": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, P(KvcPaged),

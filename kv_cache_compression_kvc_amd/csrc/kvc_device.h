@@ -273,12 +273,22 @@ __device__ __forceinline__ T ld_const(const T* p) {
  * and its length and offset come from that lane (readlane).  The cursor runs
  * one item ahead of the tile it hands out: the block-table entry of the
  * next item is loaded while the current one is worked on.
+ *
+ * Pool order: when the call brings a list of its (request, block) items
+ * sorted by pool block (kvc_paged_item), item b of a slab is entry
+ * b / subtiles of the list, and the entry carries the pool block, the
+ * request's length and its blob offset; the waves then sweep the pool in
+ * address order (neighbouring blocks at the same time) instead of in the
+ * table's random order.  The entry of the next item is loaded ahead, and
+ * its length and offset are checked per item.
  */
 struct PagedPos {
   int64_t item;          // item of the launch (slab i, item b of the slab)
   int64_t i, b;
-  int32_t r, j, sub;     // request (lane), block of the request, subtile of the block
-  int32_t blk;           // block-table entry of (r, j), loaded ahead
+  int32_t r, j, sub;     // request, block of the request, subtile of the block
+  int32_t blk;           // pool block of (r, j), loaded ahead
+  int32_t len;           // tokens of request r
+  int64_t off;           // blob offset of request r
 };
 
 struct Cursor {
@@ -314,8 +324,27 @@ __device__ __forceinline__ ReqSizes req_sizes(const LaunchArgs& a, int64_t len) 
   return z;
 }
 
-/* (request, block, subtile) of item b of a slab, and its table entry. */
+/* (request, block, subtile) of item b of a slab, its pool block, and the
+ * request's length and blob offset. */
 __device__ __forceinline__ void paged_resolve(const LaunchArgs& a, const Cursor& c, PagedPos& p) {
+  if (a.order) {  // pool order: entry b / subtiles of the list
+    int64_t e = p.b;
+    p.sub = 0;
+    if (a.subtiles != 1) {
+      e = p.b / a.subtiles;
+      p.sub = static_cast<int32_t>(p.b - e * a.subtiles);
+    }
+    // the 32-byte entry (block, block_index, req, len, offset, reserved) as two
+    // 16-byte scalar loads
+    const v4u* q = reinterpret_cast<const v4u*>(a.order + e);
+    const v4u w0 = ld_const(q), w1 = ld_const(q + 1);
+    p.blk = static_cast<int32_t>(w0.x);
+    p.j = static_cast<int32_t>(w0.y);
+    p.r = static_cast<int32_t>(w0.z);
+    p.len = static_cast<int32_t>(w0.w);
+    p.off = static_cast<int64_t>((uint64_t(w1.y) << 32) | w1.x);
+    return;
+  }
   const uint64_t below = __builtin_amdgcn_ballot_w64(int64_t(c.incl) <= p.b);
   p.r = __builtin_popcountll(below);
   const int32_t first = p.r > 0 ? lane_value(c.incl, p.r - 1) : 0;
@@ -328,6 +357,8 @@ __device__ __forceinline__ void paged_resolve(const LaunchArgs& a, const Cursor&
     p.sub = e - p.j * a.subtiles;
   }
   p.blk = ld_const(a.table + int64_t(a.req_first + p.r) * a.max_blocks + p.j);
+  p.len = lane_value(c.len, p.r);
+  p.off = lane_value64(c.off, p.r);
 }
 
 __device__ __forceinline__ void paged_step(const LaunchArgs& a, const Cursor& c, PagedPos& p) {
@@ -347,6 +378,25 @@ __device__ __forceinline__ void paged_step(const LaunchArgs& a, const Cursor& c,
  * first two items. */
 __device__ __forceinline__ void paged_init(const LaunchArgs& a, Cursor& c) {
   const int lane = threadIdx.x;
+  if (a.order) {  // pool order: the list numbers the items; nothing per lane
+    c.per_slab = a.order_len * a.subtiles;
+    c.total = c.per_slab * a.n_slabs;
+    c.cur.item = blockIdx.x;
+    if (c.per_slab == 0 || c.cur.item >= c.total) {
+      c.total = 0;
+      return;
+    }
+    const int64_t step = gridDim.x;
+    c.di = step / c.per_slab;
+    c.db = step - c.di * c.per_slab;
+    c.cur.i = c.cur.item / c.per_slab;
+    c.cur.b = c.cur.item - c.cur.i * c.per_slab;
+    paged_resolve(a, c, c.cur);
+    c.ahead = c.cur;
+    paged_step(a, c, c.ahead);
+    if (c.ahead.item < c.total) paged_resolve(a, c, c.ahead);
+    return;
+  }
   int32_t len = 0;
   int64_t off = 0;
   int32_t items = 0;
@@ -437,7 +487,18 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
     return true;
   }
   const PagedPos& p = c.cur;
-  const int32_t len = lane_value(c.len, p.r);
+  const int32_t len = p.len;
+  const int64_t off = p.off;
+  const ReqSizes z = req_sizes(a, len);
+  if (a.order) {  // a listed item carries its own length and offset: check them here
+    const bool ok = len >= 0 && int64_t(len) <= int64_t(a.max_blocks) * a.block_size && p.j >= 0 &&
+                    int64_t(p.j) * a.block_size < int64_t(len) && off >= 0 && !(off & 15) &&
+                    uint64_t(off) <= a.blob_bytes && z.total <= a.blob_bytes - uint64_t(off);
+    if (!ok) {
+      if (a.err) atomicOr(a.err, 1);
+      return false;
+    }
+  }
   const int32_t first_tok = p.j * a.block_size;  // < len: at most max_blocks * block_size <= INT32_MAX
   const int32_t ntok = min(a.block_size, len - first_tok);
   const int32_t v0 = p.sub * kTileVectors;
@@ -447,8 +508,6 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
     if (a.err) atomicOr(a.err, 1);
     return false;
   }
-  const int64_t off = lane_value64(c.off, p.r);
-  const ReqSizes z = req_sizes(a, len);
   const int64_t rows = int64_t(len) * a.heads;
   const uint64_t meta_start = uint64_t(a.layers) * (z.ck + z.cv);
   const int64_t s = p.i * a.slab_step + a.slab_first;

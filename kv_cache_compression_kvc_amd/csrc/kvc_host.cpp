@@ -13,6 +13,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "kvc_plan.h"
 
 namespace kvc {
@@ -240,25 +242,37 @@ int plan_paged(Op op, const kvc_desc* d, const void* src, void* dst,
       vecs_per_block > (1ull << 30))
     return KVC_ESHAPE;
   uint64_t subtiles = (vecs_per_block + kTileVectors - 1) / kTileVectors;
-  // item counts of one request chunk are 32-bit in the kernels
-  if (static_cast<uint64_t>(pg->max_blocks) * subtiles * kReqChunk > static_cast<uint64_t>(INT32_MAX))
-    return KVC_ERANGE;
-  const uint64_t chunk = pg->num_reqs < kReqChunk ? static_cast<uint64_t>(pg->num_reqs) : kReqChunk;
+  const bool ordered = pg->order != nullptr;
+  if (pg->order_len < 0 || (!ordered && pg->order_len != 0)) return KVC_EINVAL;
   uint64_t per_slab, items;
-  if (!mul_ok(chunk, static_cast<uint64_t>(pg->max_blocks), &per_slab) || !mul_ok(per_slab, subtiles, &per_slab) ||
-      !mul_ok(per_slab, 2ull * static_cast<uint64_t>(d->layers), &items) || items > (1ull << 62))
-    return KVC_ESHAPE;
+  if (ordered) {
+    // one launch per code width over the listed items
+    if (!mul_ok(static_cast<uint64_t>(pg->order_len), subtiles, &per_slab) || per_slab > (1ull << 40) ||
+        !mul_ok(per_slab, 2ull * static_cast<uint64_t>(d->layers), &items) || items > (1ull << 62))
+      return KVC_ESHAPE;
+    plan->req_chunks = 1;
+  } else {
+    // item counts of one request chunk are 32-bit in the kernels
+    if (static_cast<uint64_t>(pg->max_blocks) * subtiles * kReqChunk > static_cast<uint64_t>(INT32_MAX))
+      return KVC_ERANGE;
+    const uint64_t chunk = pg->num_reqs < kReqChunk ? static_cast<uint64_t>(pg->num_reqs) : kReqChunk;
+    if (!mul_ok(chunk, static_cast<uint64_t>(pg->max_blocks), &per_slab) || !mul_ok(per_slab, subtiles, &per_slab) ||
+        !mul_ok(per_slab, 2ull * static_cast<uint64_t>(d->layers), &items) || items > (1ull << 62))
+      return KVC_ESHAPE;
+    plan->req_chunks = (pg->num_reqs + kReqChunk - 1) / kReqChunk;
+  }
   if (items == 0) {
     plan->n_launch = 0;
     return KVC_OK;
   }
-  plan->req_chunks = (pg->num_reqs + kReqChunk - 1) / kReqChunk;
-  if (!src || !dst || !pg->block_table || !pg->seq_lens || !pg->out_offsets) return KVC_EINVAL;
+  if (!src || !dst) return KVC_EINVAL;
+  if (!ordered && (!pg->block_table || !pg->seq_lens || !pg->out_offsets)) return KVC_EINVAL;
   if (!aligned16(src) || !aligned16(dst)) return KVC_EALIGN;
   if ((reinterpret_cast<uintptr_t>(pg->out_offsets) & 7u) ||
       (reinterpret_cast<uintptr_t>(pg->block_table) & 3u) ||
       (reinterpret_cast<uintptr_t>(pg->seq_lens) & 3u) ||
-      (reinterpret_cast<uintptr_t>(pg->err_flag) & 3u))
+      (reinterpret_cast<uintptr_t>(pg->err_flag) & 3u) ||
+      (reinterpret_cast<uintptr_t>(pg->order) & 15u))
     return KVC_EALIGN;
   LaunchArgs base;
   common_args(d, &base);
@@ -276,6 +290,8 @@ int plan_paged(Op op, const kvc_desc* d, const void* src, void* dst,
   base.lens = pg->seq_lens;
   base.offsets = pg->out_offsets;
   base.err = pg->err_flag;
+  base.order = pg->order;
+  base.order_len = pg->order_len;
   split_slabs(op, d, plan, base);
   for (int i = 0; i < plan->n_launch; ++i)   // per request chunk; run_plan sets req_first / nreq
     plan->args[i].total_items = static_cast<int64_t>(per_slab) * plan->args[i].n_slabs;
@@ -336,6 +352,43 @@ kvc_status kvc_chunked_size(const kvc_desc* desc, int64_t chunk_layers, uint64_t
 
 kvc_status kvc_unfused_workspace_size(const kvc_desc* desc, uint64_t* bytes) {
   return static_cast<kvc_status>(kvc::unfused_workspace(desc, bytes, nullptr));
+}
+
+kvc_status kvc_paged_order(const int32_t* block_table_host, int32_t num_reqs, int32_t max_blocks,
+                           const int32_t* seq_lens_host, const int64_t* offsets_host, int32_t block_size,
+                           int64_t num_blocks, kvc_paged_item* items_host, int64_t* n_items) {
+  if (!n_items || num_reqs < 0 || max_blocks < 0 || num_blocks < 0) return KVC_EINVAL;
+  if (block_size < 1 || block_size > 1024) return KVC_ERANGE;
+  if (num_reqs > 0 && (!block_table_host || !seq_lens_host || !offsets_host)) return KVC_EINVAL;
+  int64_t n = 0;
+  for (int32_t r = 0; r < num_reqs; ++r) {
+    const int32_t len = seq_lens_host[r];
+    if (len < 0) return KVC_EINVAL;
+    if (static_cast<int64_t>(len) > static_cast<int64_t>(max_blocks) * block_size) return KVC_ERANGE;
+    const int32_t nb = static_cast<int32_t>((static_cast<int64_t>(len) + block_size - 1) / block_size);
+    for (int32_t j = 0; j < nb; ++j) {
+      const int32_t blk = block_table_host[static_cast<int64_t>(r) * max_blocks + j];
+      if (blk < 0 || blk >= num_blocks) return KVC_ERANGE;
+      if (items_host) {
+        kvc_paged_item& it = items_host[n];
+        it.block = blk;
+        it.block_index = j;
+        it.req = r;
+        it.len = len;
+        it.offset = offsets_host[r];
+        it.reserved = 0;
+      }
+      ++n;
+    }
+  }
+  if (items_host)
+    std::sort(items_host, items_host + n, [](const kvc_paged_item& a, const kvc_paged_item& b) {
+      if (a.block != b.block) return a.block < b.block;
+      if (a.req != b.req) return a.req < b.req;
+      return a.block_index < b.block_index;
+    });
+  *n_items = n;
+  return KVC_OK;
 }
 
 kvc_status kvc_paged_layout(const kvc_desc* desc, const int32_t* seq_lens_host,

@@ -12,6 +12,7 @@
 #ifndef KVC_PLAN_H
 #define KVC_PLAN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/kvc.h"
@@ -73,10 +74,16 @@ struct LaunchArgs {
   const int32_t* lens;
   const int64_t* offsets;
   int32_t* err;
+  // pool order: the call's items sorted by pool block (NULL: request order)
+  const kvc_paged_item* order;
+  int64_t order_len;
 
   int64_t total_items;    // items of this launch (paged: an upper bound, for the grid size)
   uint32_t sign_words[64];// bit 15 / bit 31 of word m: sign of element 2m / 2m+1
 };
+
+static_assert(sizeof(kvc_paged_item) == 32 && offsetof(kvc_paged_item, offset) == 16,
+              "the kernels read a paged item as two 16-byte words");
 
 enum class Op { Encode, Decode, Rotate };
 

@@ -107,6 +107,72 @@ def test_paged_matches_oracle(D, dtype, bk, bv, G, H, lens):
         assert torch.equal(dr.view(torch.int16).cpu(), got_t[:, :, blocks, offs_in]), "request %d" % r
 
 
+def _order(table, lens, offs, p, nb):
+    items = kvc.paged_order(table, lens, offs, p.block_size, nb)
+    return torch.from_numpy(items.view(np.uint8)).to(DEV)
+
+
+@pytest.mark.parametrize("D,dtype,bk,bv,G,H,lens", CASES)
+def test_paged_pool_order_equals_request_order(D, dtype, bk, bv, G, H, lens):
+    """The pool-order traversal (items sorted by pool block) writes the same
+    blob and decodes to the same pool, bit for bit, as the request-order
+    traversal (which the oracle tests above check)."""
+    p = presets.preset("qwen7b_paged").with_(name="order-%d-%s-%d%d-%d-%d" % (D, dtype, bk, bv, G, H),
+                                              layers=2, kv_heads=H, head_dim=D, dtype=dtype,
+                                              bits_k=bk, bits_v=bv, group=G, seed=5)
+    lens, table, pool, offs, total = _setup(p, lens)
+    bt, sl, of = _gpu(lens, table, offs)
+    order = _order(table, lens, offs, p, pool.shape[2])
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pg = pool.to(DEV)
+    _say("pool order", p.name, "items", order.numel() // 32)
+    w1, o1 = gpu_util.guarded(total, DEV)
+    w2, o2 = gpu_util.guarded(total, DEV)
+    kvc.encode_paged(pg, bt, sl, of, total, bk, bv, G, seed=p.seed, out=o1, err_flag=err)
+    kvc.encode_paged(pg, bt, sl, of, total, bk, bv, G, seed=p.seed, out=o2, err_flag=err, order=order)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and gpu_util.canaries_intact(w1) and gpu_util.canaries_intact(w2)
+    assert torch.equal(o1, o2), "pool-order blob differs from the request-order blob"
+    d1 = torch.full(pool.shape, 7.0, dtype=pool.dtype, device=DEV)
+    d2 = torch.full(pool.shape, 7.0, dtype=pool.dtype, device=DEV)
+    kvc.decode_paged(o1, d1, bt, sl, of, bk, bv, G, seed=p.seed, err_flag=err)
+    kvc.decode_paged(o1, d2, bt, sl, of, bk, bv, G, seed=p.seed, err_flag=err, order=order)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16)), "pool-order decode differs"
+
+
+def test_paged_pool_order_bad_items_are_flagged():
+    """Listed items whose length, offset or block is invalid are skipped and
+    flagged; the valid ones are encoded as in request order."""
+    p = presets.preset("qwen7b_paged").with_(name="order-bad", layers=1, kv_heads=4, seed=1)
+    lens, table, pool, offs, total = _setup(p, [40, 20, 33])
+    items = kvc.paged_order(table, lens, offs, p.block_size, pool.shape[2])
+    bt, sl, of = _gpu(lens, table, offs)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ref = torch.zeros(total, dtype=torch.uint8, device=DEV)
+    kvc.encode_paged(pool.to(DEV), bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=1, out=ref, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for field, value in (("len", 16 * 4 * 1000), ("offset", 8), ("block", pool.shape[2] + 3), ("block_index", 99)):
+        bad = items.copy()
+        k = int(np.nonzero(bad["req"] == 1)[0][0])
+        bad[k][field] = value if field != "offset" else bad[k]["offset"] + value
+        order = torch.from_numpy(bad.view(np.uint8)).to(DEV)
+        whole, out = gpu_util.guarded(total, DEV)
+        out.zero_()
+        err.zero_()
+        kvc.encode_paged(pool.to(DEV), bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=1, out=out,
+                         err_flag=err, order=order)
+        torch.cuda.synchronize()
+        assert int(err.item()) & 1, field
+        assert gpu_util.canaries_intact(whole), field
+        # request 0 and request 2 are encoded as in request order
+        for r in (0, 2):
+            size = oracle.blob_layout(1, int(lens[r]), 4, 128, p.bits_k, p.bits_v, p.group).total
+            assert torch.equal(out[offs[r]:offs[r] + size], ref[offs[r]:offs[r] + size]), (field, r)
+
+
 def test_paged_more_requests_than_one_launch():
     """130 requests (lengths 0..40, some empty): three launches of at most 64
     requests per code width; every request's blob against the oracle, and the
@@ -217,6 +283,13 @@ def test_paged_full_size_sampled():
     kvc.encode_paged(pool, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=out, err_flag=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0 and gpu_util.canaries_intact(whole)
+    _say("paged full size: encode in pool order")
+    out2 = torch.empty_like(out)
+    kvc.encode_paged(pool, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=out2, err_flag=err,
+                     order=_order(table, lens, offs, p, nb))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and torch.equal(out, out2), "pool-order blob differs"
+    del out2
     rng = np.random.default_rng(3)
     rep = parity.CodeReport()
     D, H, BS = p.head_dim, p.kv_heads, p.block_size

@@ -92,6 +92,13 @@ def test_random_paged(seed):
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     assert gpu_util.canaries_intact(whole), "paged encode wrote outside its blob"
+    # the pool-order traversal writes the same blob
+    items = kvc.paged_order(table, lens, offs, bs, nb)
+    w2, o2 = gpu_util.guarded(total, DEV)
+    kvc.encode_paged(pool.to(DEV), bt, sl, of, total, bk, bv, G, seed=seed, out=o2, err_flag=err,
+                     order=torch.from_numpy(items.view(np.uint8)).to(DEV) if len(items) else None)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and gpu_util.canaries_intact(w2) and torch.equal(out, o2)
     blob = out.cpu().numpy()
     pool_b = inputs.as_u16(pool)
     sblob = np.zeros(total, dtype=np.uint8)   # the oracle's encode, allowed differences substituted

@@ -42,7 +42,7 @@ def host_lib():
 def test_hip_library_exports_every_symbol(hip_lib):
     for name in declared():
         assert hasattr(hip_lib, name), name
-    assert hip_lib.kvc_abi_version() == 2
+    assert hip_lib.kvc_abi_version() == 3
 
 
 def test_host_library_exports_host_symbols(host_lib):
@@ -199,3 +199,36 @@ def test_chunked_size_validates(host_lib):
     assert host_lib.kvc_chunked_size(ctypes.byref(_desc(4, 16, 2, 128, 5, 4, 32)), 1, ctypes.byref(total), None) == -3
     assert host_lib.kvc_chunked_size(ctypes.byref(_desc(0, 16, 2, 128, 4, 4, 32)), 2, ctypes.byref(total), None) == 0
     assert total.value == 0
+
+
+def test_paged_order_lists_every_block_in_pool_order(host_lib):
+    """kvc_paged_order against a direct construction: every (request, block)
+    item with its length and offset, sorted by pool block, then request, then
+    logical block; shared blocks listed once per request."""
+    import numpy as np
+    import kv_cache_compression_kvc_amd as kvc
+    rng = np.random.default_rng(4)
+    R, MB, BS, NB = 9, 7, 16, 80
+    lens = rng.integers(0, MB * BS + 1, R).astype(np.int32)
+    lens[2] = 0
+    table = rng.integers(0, NB, (R, MB)).astype(np.int32)     # blocks shared between requests too
+    offs = np.cumsum(np.concatenate([[0], rng.integers(1, 9, R - 1) * 256])).astype(np.int64)
+    items = kvc.paged_order(table, lens, offs, BS, NB, lib=host_lib)
+    want = sorted((int(table[r, j]), r, j, int(lens[r]), int(offs[r]))
+                  for r in range(R) for j in range(-(-int(lens[r]) // BS)))
+    got = [(int(i["block"]), int(i["req"]), int(i["block_index"]), int(i["len"]), int(i["offset"])) for i in items]
+    assert got == want and not items["reserved"].any()
+    bad = table.copy()
+    bad[1, 0] = NB
+    if lens[1] > 0:
+        with pytest.raises(kvc.KvcError, match="KVC_ERANGE"):
+            kvc.paged_order(bad, lens, offs, BS, NB, lib=host_lib)
+    long = lens.copy()
+    long[0] = MB * BS + 1
+    with pytest.raises(kvc.KvcError, match="KVC_ERANGE"):
+        kvc.paged_order(table, long, offs, BS, NB, lib=host_lib)
+    neg = lens.copy()
+    neg[0] = -1
+    with pytest.raises(kvc.KvcError, match="KVC_EINVAL"):
+        kvc.paged_order(table, neg, offs, BS, NB, lib=host_lib)
+    assert len(kvc.paged_order(np.zeros((0, 3), np.int32), [], [], BS, NB, lib=host_lib)) == 0
