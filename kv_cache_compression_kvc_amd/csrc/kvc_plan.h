@@ -57,10 +57,12 @@ struct LaunchArgs {
   int32_t meta_tail;      // zero bytes after a meta slab's rows * groups * 4 bytes (< 256)
   int32_t pad1;
 
-  // paged layout: this launch covers requests [req_first, req_first + nreq),
-  // nreq <= kReqChunk; an item is (slab, request, block, subtile), and the
-  // items of a slab are numbered request by request, with no gaps (the
-  // kernel numbers them from the lengths)
+  // paged layout: an item is (slab, request, block, subtile).  In request
+  // order this launch covers requests [req_first, req_first + nreq), nreq <=
+  // kReqChunk, and the items of a slab are numbered request by request with
+  // no gaps (the kernel numbers them from the lengths); in pool order
+  // (order != NULL) the items of a slab are the order_len listed entries,
+  // each split into its subtiles
   int64_t num_blocks;
   int32_t block_size;
   int32_t heads;
