@@ -6,6 +6,7 @@ replays, and the input changes between replays (the graph reads it afresh
 each time)."""
 import sys
 
+import numpy as np
 import pytest
 import torch
 
@@ -63,13 +64,18 @@ def test_encode_decode_graph_replays(bk, bv, G):
     del g
 
 
-def test_paged_graph_replays():
+@pytest.mark.parametrize("pool_order", [False, True])
+def test_paged_graph_replays(pool_order):
     p = presets.preset("qwen7b_paged").with_(name="graph-paged", layers=2, num_requests=5,
                                               len_min=1, len_max=200, seed=4)
     lens = inputs.request_lengths(p)
     table, nb = inputs.block_table(p, lens)
     offs, total = kvc.paged_layout(lens, p.layers, p.kv_heads, p.head_dim, p.bits_k, p.bits_v, p.group, p.dtype)
     bt, sl, of = (torch.from_numpy(a).to(DEV) for a in (table, lens, offs))
+    order = None
+    if pool_order:
+        items = kvc.paged_order(table, lens, offs, p.block_size, nb)
+        order = torch.from_numpy(items.view(np.uint8)).to(DEV)
     pools = [inputs.make_pool(p, nb, device=DEV), inputs.make_pool(p.with_(k_sigma=2.0), nb, device=DEV)]
     refs = []
     for pool in pools:
@@ -80,15 +86,15 @@ def test_paged_graph_replays():
     pool_in = pools[0].clone()
     blob = torch.zeros(total, dtype=torch.uint8, device=DEV)
     out = torch.full_like(pool_in, 3.0)
-    kvc.encode_paged(pool_in, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=blob)
-    kvc.decode_paged(blob, out, bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    kvc.encode_paged(pool_in, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=blob, order=order)
+    kvc.decode_paged(blob, out, bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed, order=order)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
-    _say("graph: capture paged")
+    _say("graph: capture paged", "pool order" if pool_order else "request order")
     with torch.cuda.graph(g, stream=side):
-        kvc.encode_paged(pool_in, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=blob)
-        kvc.decode_paged(blob, out, bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed)
+        kvc.encode_paged(pool_in, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, out=blob, order=order)
+        kvc.decode_paged(blob, out, bt, sl, of, p.bits_k, p.bits_v, p.group, seed=p.seed, order=order)
     for r in range(6):
         k = r % 2
         pool_in.copy_(pools[k])
