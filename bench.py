@@ -129,6 +129,8 @@ def parse(argv=None):
     ap.add_argument("--no-unfused", action="store_true", help="skip the separate-kernel comparator")
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the transfer legs (they launch the fused kernels on layer chunks)")
+    ap.add_argument("--no-transform", action="store_true",
+                    help="skip the matrix-core / butterfly comparison (it launches the default kernels again)")
     return ap.parse_args(argv)
 
 
@@ -448,6 +450,7 @@ class Leg:
         self.enc_bytes = self.total
         self.algo_bytes = self.raw_bytes + self.enc_bytes   # read + write of one encode (or decode)
         self.kvc = kvc
+        self.transform = None   # contiguous: None runs kvc_encode / kvc_decode, else the *_with forms
 
     def enc(self, i):
         p, k = self.p, i % self.nsets
@@ -455,7 +458,8 @@ class Leg:
             self.kvc.encode_paged(self.src[k], self.bt, self.sl, self.of, self.total, p.bits_k, p.bits_v, p.group,
                                   seed=p.seed, out=self.outs[k], order=self.order)
         else:
-            self.kvc.encode(self.src[k], p.bits_k, p.bits_v, p.group, seed=p.seed, out=self.outs[k])
+            self.kvc.encode(self.src[k], p.bits_k, p.bits_v, p.group, seed=p.seed, out=self.outs[k],
+                            transform=self.transform)
 
     def dec(self, i):
         p, k = self.p, i % self.nsets
@@ -464,7 +468,7 @@ class Leg:
                                   seed=p.seed, order=self.order)
         else:
             self.kvc.decode(self.outs[k], self.src[k].shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed,
-                            out=self.dsts[k])
+                            out=self.dsts[k], transform=self.transform)
 
     def prewarm(self, seconds):
         """Encode + decode back to back for `seconds` of wall time; returns the steps run."""
@@ -530,7 +534,26 @@ def break_even(leg, t_enc, t_dec):
     return be
 
 
-def other_workload(kvc, name, dev, stream, steps, prewarm_s):
+def transform_leg(leg, stream, steps, prewarm_s):
+    """The same protocol with the transform forced to the matrix cores and to
+    the in-register butterfly (kvc_encode_with / kvc_decode_with), everything
+    else of the launches equal: the measurement behind the transform each
+    kernel runs by default."""
+    out = {}
+    for name in ("matrix", "butterfly"):
+        leg.transform = name
+        leg.prewarm(prewarm_s)
+        _, e, d = leg.timed(steps, stream)
+        out[name] = {k: {f: s[f] for f in ("frac_hbm_peak", "frac_hbm_peak_median", "ms", "ms_median")}
+                     for k, s in (("encode", kernel_summary(leg, e)), ("decode", kernel_summary(leg, d)))}
+    leg.transform = None
+    for k in ("encode", "decode"):
+        m, b = out["matrix"][k]["ms_median"], out["butterfly"][k]["ms_median"]
+        out[k + "_butterfly_over_matrix"] = b / m
+    return out
+
+
+def other_workload(kvc, name, dev, stream, steps, prewarm_s, with_transform=True):
     """The same protocol on another workload: a shorter pre-warm, 3 warm-up
     steps, `steps` timed steps; tiny reports latency."""
     from kv_cache_compression_kvc_amd import presets
@@ -551,6 +574,8 @@ def other_workload(kvc, name, dev, stream, steps, prewarm_s):
                    raw_GBps_step=leg.raw_bytes / (wall / steps) / 1e9,
                    traffic={"encode": counter_traffic(name, "encode"), "decode": counter_traffic(name, "decode")})
         out["probes"] = leg_probes(kvc, leg, stream, e, d)
+        if not p.paged and with_transform:
+            out["transform"] = transform_leg(leg, stream, steps, prewarm_s / 3)
     out["break_even"] = break_even(leg, e["ms"] / 1e3, d["ms"] / 1e3)
     if p.paged:   # the same pool visited in request order (no host prologue), for comparison
         leg.order = None
@@ -597,6 +622,7 @@ def main():
     enc, dec = kernel_summary(leg, enc_ms), kernel_summary(leg, dec_ms)
     t_enc, t_dec = enc["ms"] / 1e3, dec["ms"] / 1e3
     probes = leg_probes(kvc, leg, stream, enc, dec)
+    transform = None if (p.paged or a.no_transform) else transform_leg(leg, stream, a.steps, min(a.prewarm_s, 1.0))
 
     unfused = pipeline = None
     if not p.paged and not a.no_unfused:
@@ -626,6 +652,7 @@ def main():
         "decode": dec,
         "bytes": {"raw": leg.raw_bytes, "encoded": leg.enc_bytes, "ratio": leg.raw_bytes / leg.enc_bytes},
         "probes": probes,
+        "transform": transform,
         "break_even": break_even(leg, t_enc, t_dec),
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
@@ -638,7 +665,8 @@ def main():
     }
     leg.close()
     if a.other_steps > 0:
-        result["workloads"] = {name: other_workload(kvc, name, dev, stream, a.other_steps, a.other_prewarm_s)
+        result["workloads"] = {name: other_workload(kvc, name, dev, stream, a.other_steps, a.other_prewarm_s,
+                                                    not a.no_transform)
                                for name in presets.ORDER if name != p.name}
     if not a.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p, a.cpu_sample_chunks)

@@ -91,8 +91,9 @@ extern "C" {
 #endif
 
 /* 2: every code and meta slab of the blob padded to a multiple of 256 bytes.
- * 3: kvc_paged carries an optional pool-order item list (kvc_paged_order). */
-#define KVC_ABI_VERSION 3
+ * 3: kvc_paged carries an optional pool-order item list (kvc_paged_order).
+ * 4: kvc_encode_with / kvc_decode_with choose the transform. */
+#define KVC_ABI_VERSION 4
 
 typedef enum kvc_status {
   KVC_OK = 0,
@@ -228,6 +229,37 @@ kvc_status kvc_encode(const kvc_desc* desc, const void* kv, void* out,
  */
 kvc_status kvc_decode(const kvc_desc* desc, const void* in, uint64_t in_bytes,
                       void* kv_out, void* stream);
+
+/*
+ * How the contiguous kernels compute the Walsh-Hadamard transform of the
+ * episode notes of "FastKVComp: checking whether high-throughput KV
+ * compression pays off": KVC_TRANSFORM_MATRIX as exact products with +-1 on
+ * the matrix cores (a GEMM against H), KVC_TRANSFORM_BUTTERFLY as the
+ * log2(D)-stage butterfly in each lane's registers, KVC_TRANSFORM_AUTO the
+ * one kvc_encode / kvc_decode run for that shape (the faster one measured).
+ */
+typedef enum kvc_transform {
+  KVC_TRANSFORM_AUTO = 0,
+  KVC_TRANSFORM_MATRIX = 1,
+  KVC_TRANSFORM_BUTTERFLY = 2
+} kvc_transform;
+
+/*
+ * kvc_encode / kvc_decode with the transform chosen (a kvc_transform
+ * value), everything else of the launch as the automatic choice makes it:
+ * the pair the design choice of the transform is measured with.  The
+ * butterfly and matrix-core encodes sum the same +-1 products in different
+ * orders, so their blobs may differ where a rotated value rounds across a
+ * code or meta boundary (both meet the oracle's criteria); every decode
+ * transforms integer codes within groups exactly, so decodes of one blob
+ * are bit-identical whichever transform runs.  Arguments and errors as
+ * kvc_encode / kvc_decode, plus KVC_EINVAL for a transform outside the
+ * enum.
+ */
+kvc_status kvc_encode_with(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes,
+                           int32_t transform, void* stream);
+kvc_status kvc_decode_with(const kvc_desc* desc, const void* in, uint64_t in_bytes, void* kv_out,
+                           int32_t transform, void* stream);
 
 /*
  * Host prologue of the paged calls: offsets_host[r] = sum of the blob

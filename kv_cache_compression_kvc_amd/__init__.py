@@ -111,8 +111,15 @@ def sign_mask(seed, head_dim):
     return sum(int(w) << (64 * i) for i, w in enumerate(words))
 
 
-def encode(kv, bits_k, bits_v, group, seed=0, out=None, stream=None):
-    """Encode a contiguous [L, 2, T, H, D] GPU tensor; returns the uint8 blob."""
+def _transform(transform):
+    if transform not in _lib.TRANSFORM:
+        raise ValueError("transform must be one of %s" % sorted(_lib.TRANSFORM))
+    return _lib.TRANSFORM[transform]
+
+
+def encode(kv, bits_k, bits_v, group, seed=0, out=None, stream=None, transform=None):
+    """Encode a contiguous [L, 2, T, H, D] GPU tensor; returns the uint8 blob.
+    ``transform`` ("auto", "matrix" or "butterfly") calls kvc_encode_with."""
     L, T, H, D = _kv_shape(kv.shape, "kv")
     dt = _dtype_name(kv)
     _check_cuda(kv, out)
@@ -120,19 +127,28 @@ def encode(kv, bits_k, bits_v, group, seed=0, out=None, stream=None):
     if out is None:
         out = torch.empty(total, dtype=torch.uint8, device=kv.device)
     d = _desc(L, T, H, D, dt, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_encode(ctypes.byref(d), _ptr(kv), _ptr(out), _nbytes(out), _stream(stream)))
+    if transform is None:
+        _lib.check(_lib.lib().kvc_encode(ctypes.byref(d), _ptr(kv), _ptr(out), _nbytes(out), _stream(stream)))
+    else:
+        _lib.check(_lib.lib().kvc_encode_with(ctypes.byref(d), _ptr(kv), _ptr(out), _nbytes(out),
+                                              _transform(transform), _stream(stream)))
     return out
 
 
-def decode(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, stream=None):
-    """Decode a blob into a [L, 2, T, H, D] GPU tensor of ``dtype``."""
+def decode(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, stream=None, transform=None):
+    """Decode a blob into a [L, 2, T, H, D] GPU tensor of ``dtype``.
+    ``transform`` ("auto", "matrix" or "butterfly") calls kvc_decode_with."""
     L, T, H, D = _kv_shape(shape, "shape")
     _check_out(out, shape, _torch_dtype(dtype))
     _check_cuda(blob, out)
     if out is None:
         out = torch.empty(tuple(shape), dtype=_torch_dtype(dtype), device=blob.device)
     d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_decode(ctypes.byref(d), _ptr(blob), _nbytes(blob), _ptr(out), _stream(stream)))
+    if transform is None:
+        _lib.check(_lib.lib().kvc_decode(ctypes.byref(d), _ptr(blob), _nbytes(blob), _ptr(out), _stream(stream)))
+    else:
+        _lib.check(_lib.lib().kvc_decode_with(ctypes.byref(d), _ptr(blob), _nbytes(blob), _ptr(out),
+                                              _transform(transform), _stream(stream)))
     return out
 
 

@@ -28,8 +28,10 @@ EXPORTS = [
     "kvc_decode", "kvc_paged_layout", "kvc_encode_paged", "kvc_decode_paged",
     "kvc_debug_rotate", "kvc_unfused_workspace_size", "kvc_encode_unfused", "kvc_decode_unfused",
     "kvc_chunked_size", "kvc_encode_send", "kvc_receive_decode", "kvc_probe_copy",
-    "kvc_encode_unfused_noalloc", "kvc_probe_stream", "kvc_paged_order",
+    "kvc_encode_unfused_noalloc", "kvc_probe_stream", "kvc_paged_order", "kvc_encode_with",
+    "kvc_decode_with",
 ]
+TRANSFORM = {"auto": 0, "matrix": 1, "butterfly": 2}   # kvc_transform
 NOALLOC_WORKSPACE_BYTES = 64 << 20   # KVC_NOALLOC_WORKSPACE_BYTES
 HOST_EXPORTS = ["kvc_abi_version", "kvc_strerror", "kvc_encoded_size", "kvc_sign_mask",
                 "kvc_paged_layout", "kvc_unfused_workspace_size", "kvc_chunked_size", "kvc_paged_order"]
@@ -95,6 +97,10 @@ def _declare(lib, names):
                                         ctypes.c_uint64, ctypes.c_void_p]),
         "kvc_decode": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_uint64,
                                         ctypes.c_void_p, ctypes.c_void_p]),
+        "kvc_encode_with": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p]),
+        "kvc_decode_with": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_uint64,
+                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
         "kvc_paged_order": (ctypes.c_int32, [P(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32),
                                              P(ctypes.c_int64), ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                              P(ctypes.c_int64)]),

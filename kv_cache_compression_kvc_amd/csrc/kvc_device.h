@@ -412,7 +412,8 @@ __device__ __forceinline__ void paged_init(const LaunchArgs& a, Cursor& c) {
       if (a.err) atomicOr(a.err, 1);
       len = 0;
     }
-    items = (len + a.block_size - 1) / a.block_size * a.subtiles;
+    // at most max_blocks * subtiles, which the host keeps below INT32_MAX / 64
+    items = static_cast<int32_t>((int64_t(len) + a.block_size - 1) / a.block_size * a.subtiles);
   }
   // inclusive prefix sum of the items over the lanes
   int32_t incl = items;
@@ -792,6 +793,25 @@ __device__ __forceinline__ void hadamard_mfma(v4u (&xc)[D / 8], const HadamardA&
   }
 }
 
+/* Butterfly stages h = H0, 2 H0, ... < H1 of the in-place Sylvester
+ * transform: stages below G stay inside groups of G elements, the others
+ * combine groups. */
+template <int D, int H0, int H1>
+__device__ __forceinline__ void butterfly_stages(float (&y)[D]) {
+#pragma unroll
+  for (int h = H0; h < H1; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < D; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float p0 = y[j], p1 = y[j + h];
+        y[j] = p0 + p1;
+        y[j + h] = p0 - p1;
+      }
+    }
+  }
+}
+
 /* Sign words into LDS (word m: bit 15 / 31 set when element 2m / 2m + 1 flips). */
 __device__ __forceinline__ void load_signs(const LaunchArgs& a, uint32_t* signs) {
   signs[threadIdx.x] = a.sign_words[threadIdx.x];
@@ -898,12 +918,18 @@ __device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t) {
   }
 }
 
+/* The encode's transform: kEncodeMatrix runs u = H x on the matrix cores
+ * (hadamard_mfma), kEncodeButterfly as the in-register butterfly of each
+ * lane's own vector in fp32.  Both are exact products with +-1 and fp32
+ * sums, in different orders, so their u differ by rounding only. */
+constexpr int kEncodeMatrix = 0, kEncodeButterfly = 1;
+
 /*
  * Encode: per tile, the rows arrive in LDS by DMA; each lane reads its own
  * row into registers, the wave then starts the DMA of its next tile into the
  * same buffer and computes the current one while that load is in flight.
  */
-template <int D, int DT, int B, int G, bool PAGED>
+template <int D, int DT, int B, int G, bool PAGED, int XF = kEncodeMatrix>
 KVC_KERNEL void encode_kernel(const LaunchArgs a) {
   constexpr int CH = D / 8;
   __shared__ v4u lds[kTileVectors * CH];
@@ -919,7 +945,7 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
   wait_vmem<0>();
   lds_order();
   HadamardA had;
-  hadamard_operands<DT>(had);
+  if constexpr (XF == kEncodeMatrix) hadamard_operands<DT>(had);
   for (;;) {
     v4u xc[D / 8];
     read_row_signed<D>(lds, signs, xc);
@@ -930,7 +956,16 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
     if (more) dma_rows<D, !PAGED>(nxt.src, nxt.count, (lds_v4u*)lds);
     KVC_PHASE();
     float y[D];
-    hadamard_mfma<D, DT>(xc, had, y);
+    if constexpr (XF == kEncodeButterfly) {
+#pragma unroll
+      for (int p = 0; p < D / 8; ++p) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) unpack_pair<DT>(xc[p][m], y[8 * p + 2 * m], y[8 * p + 2 * m + 1]);
+      }
+      butterfly_stages<D, 1, D>(y);
+    } else {
+      hadamard_mfma<D, DT>(xc, had, y);
+    }
     KVC_PHASE();
     encode_vector<D, B, G, PAGED>(y, cur);
     if (!more) break;
@@ -1021,25 +1056,6 @@ __device__ __forceinline__ v4u code_chunk_f16(const uint32_t (&w)[NW], int p) {
   return r;
 }
 
-/* Butterfly stages h = H0, 2 H0, ... < H1 of the in-place Sylvester
- * transform: stages below G stay inside groups of G elements, the others
- * combine groups. */
-template <int D, int H0, int H1>
-__device__ __forceinline__ void butterfly_stages(float (&y)[D]) {
-#pragma unroll
-  for (int h = H0; h < H1; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < D; i += 2 * h) {
-#pragma unroll
-      for (int j = i; j < i + h; ++j) {
-        const float p0 = y[j], p1 = y[j + h];
-        y[j] = p0 + p1;
-        y[j + h] = p0 - p1;
-      }
-    }
-  }
-}
-
 /*
  * Decode.  With q the codes of a vector, group g holding elements
  * [gG, gG + G), and H_D = H_{D/G} (x) H_G in Sylvester order:
@@ -1082,12 +1098,16 @@ __device__ __forceinline__ void butterfly_stages(float (&y)[D]) {
  *     one group per vector past 512 MiB at head_dim 128): the butterfly,
  *     stores overlapped with no extra wait; its arithmetic spaces the stores
  *     by itself, and it measured 1-4% faster there than the matrix cores.
+ *   kDecodeButterfly (contiguous, on request only): the butterfly with the
+ *     waits of kDecodeWaitStores, so that the two in-group transforms can be
+ *     timed against each other with everything else equal.
  */
-constexpr int kDecodeWaitTop = 0, kDecodeWaitStores = 1, kDecodeLarge = 2;
+constexpr int kDecodeWaitTop = 0, kDecodeWaitStores = 1, kDecodeLarge = 2, kDecodeButterfly = 3;
 
 template <int D, int DT, int B, int G, bool PAGED, int MODE>
 KVC_KERNEL void decode_kernel(const LaunchArgs a) {
-  constexpr bool LARGE = MODE == kDecodeLarge;
+  constexpr bool BFLY = MODE == kDecodeLarge || MODE == kDecodeButterfly;  // in-group transform: butterfly
+  constexpr bool WAIT_STORES = MODE == kDecodeWaitStores || MODE == kDecodeButterfly;
   constexpr int CH = D / 8, NG = D / G, NW = D * B / 32, VPW = 32 / B;
   constexpr float RS = Norm<D>::inv_sqrt;
   constexpr int HALF = 8;                         // chunks per row staged at a time: one line
@@ -1099,7 +1119,7 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   const int lane = threadIdx.x;
   load_signs(a, signs);
   HadamardA had;
-  if constexpr (!LARGE) hadamard_operands<KVC_FP16>(had);
+  if constexpr (!BFLY) hadamard_operands<KVC_FP16>(had);
   Cursor c;
   cursor_init<PAGED>(a, c);
   Tile cur;
@@ -1118,8 +1138,8 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
       ze[g] = f16_value(cr.meta[g] >> 16) * RS;
     }
     float y[D];
-    v4u xq[LARGE ? 1 : CH];
-    if constexpr (LARGE) {
+    v4u xq[BFLY ? 1 : CH];
+    if constexpr (BFLY) {
 #pragma unroll
       for (int wi = 0; wi < NW; ++wi) unpack_word<B>(cr.codes[wi / 4][wi % 4], y + wi * VPW);
     } else {
@@ -1134,7 +1154,7 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
     const bool more = next_tile<D, false, PAGED>(a, c, tensor, blob, nxt, false);
     if (more) load_codes<D, B, G, PAGED>(nxt, cr);
     KVC_PHASE();
-    if constexpr (LARGE) {
+    if constexpr (BFLY) {
       butterfly_stages<D, 1, G>(y);
     } else {
       hadamard_mfma<D, KVC_FP16, G>(xq, had, y);
@@ -1149,7 +1169,7 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
     }
     butterfly_stages<D, G, D>(y);
     KVC_PHASE();
-    if constexpr (MODE == kDecodeWaitStores) {
+    if constexpr (WAIT_STORES) {
       // outstanding: the last tile's stores, then the next tile's code and
       // meta loads (NL instructions, none after the last tile)
       constexpr int NL = D * B / 128 + 1;

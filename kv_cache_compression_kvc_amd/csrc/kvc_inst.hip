@@ -20,13 +20,20 @@ namespace {
 
 template <int D, int DT, int B, int G, bool PAGED>
 Kernel pick_op(Op op, int mode) {
-  if (op == Op::Encode) return dev::encode_kernel<D, DT, B, G, PAGED>;
+  if (op == Op::Encode) {
+    if (mode == dev::kEncodeMatrix) return dev::encode_kernel<D, DT, B, G, PAGED, dev::kEncodeMatrix>;
+    // the butterfly encode is a contiguous comparator only
+    if constexpr (!PAGED)
+      if (mode == dev::kEncodeButterfly) return dev::encode_kernel<D, DT, B, G, false, dev::kEncodeButterfly>;
+    return nullptr;
+  }
   if constexpr (!PAGED) {
-    // the butterfly decode is picked at head_dim 64, and for 4-bit codes in
-    // one group per vector at head_dim 128 (the launch rule in kvc_launch.hip)
+    // kDecodeLarge is picked at head_dim 64, and for 4-bit codes in one
+    // group per vector at head_dim 128 (the launch rule in kvc_launch.hip)
     if constexpr (D == 64 || (B == 4 && G == D))
       if (mode == dev::kDecodeLarge) return dev::decode_kernel<D, DT, B, G, false, dev::kDecodeLarge>;
     if (mode == dev::kDecodeWaitStores) return dev::decode_kernel<D, DT, B, G, false, dev::kDecodeWaitStores>;
+    if (mode == dev::kDecodeButterfly) return dev::decode_kernel<D, DT, B, G, false, dev::kDecodeButterfly>;
   } else {
     constexpr int M = D == 64 ? dev::kDecodeWaitTop : dev::kDecodeWaitStores;
     if (mode == M) return dev::decode_kernel<D, DT, B, G, true, M>;

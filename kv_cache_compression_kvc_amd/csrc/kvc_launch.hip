@@ -203,18 +203,25 @@ bool decode_large(const LaunchArgs& a, int head_dim, int bits) {
   return bits == 4 && a.groups == 1 && a.blob_total > kDecodeLargeBlobD128;
 }
 
-LaunchShape launch_shape(Op op, const LaunchArgs& a, int head_dim, int bits) {
-  if (op == Op::Encode) return {(a.paged && head_dim == 64) ? 0 : 1, 0, 0};
+/* `transform` (kvc_transform) overrides the transform of a contiguous
+ * launch and keeps the rest of its shape: a forced matrix-core decode of a
+ * kDecodeLarge-sized blob runs as kDecodeWaitStores, a forced butterfly
+ * decode of a smaller one as kDecodeButterfly with the waves that
+ * kDecodeWaitStores would take. */
+LaunchShape launch_shape(Op op, const LaunchArgs& a, int head_dim, int bits, int transform) {
+  const bool bfly = transform == KVC_TRANSFORM_BUTTERFLY;
+  if (op == Op::Encode)
+    return {(a.paged && head_dim == 64) ? 0 : 1, bfly ? dev::kEncodeButterfly : dev::kEncodeMatrix, 0};
   if (op != Op::Decode) return {0, 0, 0};
   if (a.paged)
     return head_dim == 64 ? LaunchShape{2, dev::kDecodeWaitTop, 0} : LaunchShape{1, dev::kDecodeWaitStores, 0};
-  if (decode_large(a, head_dim, bits)) return {1, dev::kDecodeLarge, 0};
-  return {1, dev::kDecodeWaitStores, a.blob_total >= kDecodeThreePerCuBlob ? 3 : 0};
+  if (transform != KVC_TRANSFORM_MATRIX && decode_large(a, head_dim, bits)) return {1, dev::kDecodeLarge, 0};
+  return {1, bfly ? dev::kDecodeButterfly : dev::kDecodeWaitStores, a.blob_total >= kDecodeThreePerCuBlob ? 3 : 0};
 }
 
-int run_plan(Op op, const Plan& plan, void* stream) {
+int run_plan(Op op, const Plan& plan, void* stream, int transform = KVC_TRANSFORM_AUTO) {
   for (int i = 0; i < plan.n_launch; ++i) {
-    const LaunchShape shape = launch_shape(op, plan.args[i], plan.head_dim, plan.bits[i]);
+    const LaunchShape shape = launch_shape(op, plan.args[i], plan.head_dim, plan.bits[i], transform);
     Kernel k = pick(op, plan.head_dim, plan.dtype, plan.bits[i], plan.group, plan.args[i].paged != 0, shape.mode);
     if (!k) return KVC_ESHAPE;
     int64_t resident = 0;
@@ -258,6 +265,24 @@ kvc_status kvc_decode(const kvc_desc* desc, const void* in, uint64_t in_bytes, v
   kvc::Plan plan;
   int st = kvc::plan_contiguous(kvc::Op::Decode, desc, in, kv_out, in_bytes, &plan);
   if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Decode, plan, stream);
+  return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_encode_with(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes, int32_t transform,
+                           void* stream) {
+  if (transform < KVC_TRANSFORM_AUTO || transform > KVC_TRANSFORM_BUTTERFLY) return KVC_EINVAL;
+  kvc::Plan plan;
+  int st = kvc::plan_contiguous(kvc::Op::Encode, desc, kv, out, out_bytes, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Encode, plan, stream, transform);
+  return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_decode_with(const kvc_desc* desc, const void* in, uint64_t in_bytes, void* kv_out, int32_t transform,
+                           void* stream) {
+  if (transform < KVC_TRANSFORM_AUTO || transform > KVC_TRANSFORM_BUTTERFLY) return KVC_EINVAL;
+  kvc::Plan plan;
+  int st = kvc::plan_contiguous(kvc::Op::Decode, desc, in, kv_out, in_bytes, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Decode, plan, stream, transform);
   return static_cast<kvc_status>(st);
 }
 

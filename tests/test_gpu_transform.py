@@ -1,0 +1,134 @@
+"""The two transforms of the contiguous kernels, chosen through
+kvc_encode_with / kvc_decode_with: the matrix cores (the default) and the
+in-register butterfly.  Each encode is checked against the oracle; the
+decodes of one blob must be bit-identical whichever transform runs (the
+in-group transform of integer codes is exact either way)."""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+import gpu_util
+import kv_cache_compression_kvc_amd as kvc
+from kv_cache_compression_kvc_amd import _lib, inputs, presets
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _small(D, dtype, bk, bv, G, L=2, T=37, H=3, seed=5):
+    return presets.preset("llama3_8b_4k").with_(
+        name="xf-%d-%s-%d%d-%d" % (D, dtype, bk, bv, G), layers=L, tokens=T, kv_heads=H,
+        head_dim=D, dtype=dtype, bits_k=bk, bits_v=bv, group=G, seed=seed)
+
+
+def _decode_all(blob, x, p):
+    """Decodes of `blob` with each transform, each into a guarded buffer."""
+    outs = {}
+    for xf in ("auto", "matrix", "butterfly"):
+        whole, raw = gpu_util.guarded(x.numel() * 2, DEV)
+        xd = raw.view(x.dtype).view(x.shape)
+        kvc.decode(blob, x.shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed, out=xd, transform=xf)
+        torch.cuda.synchronize()
+        assert gpu_util.canaries_intact(whole), "decode (%s) wrote outside its output" % xf
+        outs[xf] = xd
+    return outs
+
+
+GRID = [(D, dt, bk, bv, G)
+        for D in (64, 128) for dt in ("bf16", "fp16")
+        for bk, bv in [(2, 2), (4, 4), (8, 8), (2, 4)]
+        for G in (32, 64, 128) if G <= D]
+
+
+@pytest.mark.parametrize("D,dtype,bk,bv,G", GRID)
+def test_butterfly_encode_and_decodes(D, dtype, bk, bv, G):
+    p = _small(D, dtype, bk, bv, G)
+    x = inputs.make_kv(p)
+    xb = inputs.as_u16(x)
+    xg = x.to(DEV)
+    total, _ = kvc.encoded_size(p.layers, p.tokens, p.kv_heads, D, bk, bv, G, dtype)
+    _say("transform", p.name)
+    blobs = {}
+    for xf in ("butterfly", "matrix"):
+        whole, out = gpu_util.guarded(total, DEV)
+        kvc.encode(xg, bk, bv, G, seed=p.seed, out=out, transform=xf)
+        torch.cuda.synchronize()
+        assert gpu_util.canaries_intact(whole), "encode (%s) wrote outside its blob" % xf
+        blobs[xf] = out
+    # the default encode runs the matrix cores: the same bytes
+    auto = kvc.encode(xg, bk, bv, G, seed=p.seed)
+    assert torch.equal(auto, blobs["matrix"])
+    res = parity.check_blob(xb, blobs["butterfly"].cpu().numpy(), dtype, bk, bv, G, p.seed)
+    _say("  butterfly encode vs oracle:", res.report)
+    outs = _decode_all(blobs["butterfly"], xg, p)
+    for xf in ("matrix", "butterfly"):
+        assert torch.equal(outs[xf].view(torch.int16), outs["auto"].view(torch.int16)), xf
+    parity.check_decode(inputs.as_u16(outs["butterfly"]), res.reference, dtype)
+
+
+def test_transform_argument_is_checked():
+    x = torch.zeros((1, 2, 4, 1, 128), dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)
+    d = _lib.KvcDesc(1, 4, 1, 128, 0, 4, 4, 128, 0)
+    lib = _lib.lib()
+    for bad in (-1, 3):
+        assert lib.kvc_encode_with(ctypes.byref(d), x.data_ptr(), out.data_ptr(), out.numel(), bad, None) == -1
+        assert lib.kvc_decode_with(ctypes.byref(d), out.data_ptr(), out.numel(), x.data_ptr(), bad, None) == -1
+    with pytest.raises(ValueError):
+        kvc.encode(x, 4, 4, 128, transform="fft")
+
+
+@pytest.mark.slow
+def test_full_size_butterfly_encode():
+    """The butterfly encode at the 8B-4k size: sampled vectors against the
+    oracle; the decodes of its blob bit-identical over the whole tensor."""
+    p = presets.preset("llama3_8b_4k")
+    x = inputs.make_kv(p, device=DEV)
+    _say("full size butterfly encode", p.name)
+    blob = kvc.encode(x, p.bits_k, p.bits_v, p.group, seed=p.seed, transform="butterfly")
+    torch.cuda.synchronize()
+    idx = gpu_util.sample_vectors(p, np.random.default_rng(17))
+    rep, reference = gpu_util.check_sampled_encode(p, x, blob, idx)
+    _say("  sampled codes vs oracle:", rep)
+    xm = kvc.decode(blob, x.shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed, transform="matrix")
+    xbf = kvc.decode(blob, x.shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed, transform="butterfly")
+    assert torch.equal(xm.view(torch.int16), xbf.view(torch.int16))
+    got = inputs.as_u16(xbf.view(-1, p.head_dim)[torch.from_numpy(idx).to(DEV)])
+    _say("  sampled decode rrms %.3g" % parity.check_decode(got, reference, p.dtype, axis_slices=(1,)))
+    del x, blob, xm, xbf
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+def test_large_blob_decode_transforms_agree():
+    """A 4-bit G128 blob past 512 MiB: the default decode takes the butterfly
+    with overlapped stores, a forced matrix-core decode the three-waves-per-CU
+    shape; both must give the same bits."""
+    T = 32 * 1024 + 3
+    p = _small(128, "bf16", 4, 4, 128, L=16, T=T, H=8, seed=9)
+    total, _ = kvc.encoded_size(p.layers, T, 8, 128, 4, 4, 128, "bf16")
+    assert total > 512 << 20
+    _say("large blob transforms", T)
+    x = inputs.make_kv(p, device=DEV)
+    blob = kvc.encode(x, 4, 4, 128, seed=p.seed)
+    del x
+    shape = (p.layers, 2, T, 8, 128)
+    xa = kvc.decode(blob, shape, "bf16", 4, 4, 128, seed=p.seed)
+    xm = kvc.decode(blob, shape, "bf16", 4, 4, 128, seed=p.seed, transform="matrix")
+    assert torch.equal(xa.view(torch.int16), xm.view(torch.int16))
+    del xm
+    xbf = kvc.decode(blob, shape, "bf16", 4, 4, 128, seed=p.seed, transform="butterfly")
+    assert torch.equal(xa.view(torch.int16), xbf.view(torch.int16))
+    del xa, xbf, blob
+    torch.cuda.empty_cache()
