@@ -101,6 +101,11 @@ class TimingEvents:
     def record(self, k, stream):
         self._check(self._hip.hipEventRecord(self._ev[k], ctypes.c_void_p(stream.cuda_stream)), "record")
 
+    def pair(self, a, b):
+        """Handles of events a and b, for a library call to attach to its first
+        kernel's start and its last kernel's end."""
+        return self._ev[a], self._ev[b]
+
     def ms(self, a, b):
         t = ctypes.c_float()
         self._check(self._hip.hipEventElapsedTime(ctypes.byref(t), self._ev[a], self._ev[b]), "elapsed time")
@@ -241,6 +246,8 @@ def sample_parity(kvc, p, dev, layer=0):
 # Separate-kernel comparator (same results, intermediates through HBM)
 
 def unfused_leg(kvc, p, xs, outs, dsts, a, stream, t_enc, t_dec, raw_bytes):
+    """The comparator timed with events around each call (its kernels and the
+    gaps between them); t_enc / t_dec are the fused calls timed the same way."""
     import torch
     L, T, H, D = p.layers, p.tokens, p.kv_heads, p.head_dim
     ws_bytes = kvc.unfused_workspace_size(L, T, H, D, p.bits_k, p.bits_v, p.group, p.dtype)
@@ -452,23 +459,23 @@ class Leg:
         self.kvc = kvc
         self.transform = None   # contiguous: None runs kvc_encode / kvc_decode, else the *_with forms
 
-    def enc(self, i):
+    def enc(self, i, events=None):
         p, k = self.p, i % self.nsets
         if p.paged:
             self.kvc.encode_paged(self.src[k], self.bt, self.sl, self.of, self.total, p.bits_k, p.bits_v, p.group,
-                                  seed=p.seed, out=self.outs[k], order=self.order)
+                                  seed=p.seed, out=self.outs[k], order=self.order, events=events)
         else:
             self.kvc.encode(self.src[k], p.bits_k, p.bits_v, p.group, seed=p.seed, out=self.outs[k],
-                            transform=self.transform)
+                            transform=self.transform, events=events)
 
-    def dec(self, i):
+    def dec(self, i, events=None):
         p, k = self.p, i % self.nsets
         if p.paged:
             self.kvc.decode_paged(self.outs[k], self.dsts[k], self.bt, self.sl, self.of, p.bits_k, p.bits_v, p.group,
-                                  seed=p.seed, order=self.order)
+                                  seed=p.seed, order=self.order, events=events)
         else:
             self.kvc.decode(self.outs[k], self.src[k].shape, p.dtype, p.bits_k, p.bits_v, p.group, seed=p.seed,
-                            out=self.dsts[k], transform=self.transform)
+                            out=self.dsts[k], transform=self.transform, events=events)
 
     def prewarm(self, seconds):
         """Encode + decode back to back for `seconds` of wall time; returns the steps run."""
@@ -484,11 +491,31 @@ class Leg:
                 return n
 
     def timed(self, steps, stream):
-        """K steps between device synchronizations: (wall s, encode ms list, decode ms list)."""
+        """K steps between device synchronizations: (wall s, encode ms list,
+        decode ms list).  Each call's time is its kernels' own: the library
+        attaches the events to the start of its first and the end of its last
+        kernel dispatch."""
+        import torch
+        ev = TimingEvents(4 * steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.enc(i, events=ev.pair(4 * i, 4 * i + 1))
+            self.dec(i, events=ev.pair(4 * i + 2, 4 * i + 3))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        enc_ms = [ev.ms(4 * i, 4 * i + 1) for i in range(steps)]
+        dec_ms = [ev.ms(4 * i + 2, 4 * i + 3) for i in range(steps)]
+        ev.close()
+        return wall, enc_ms, dec_ms
+
+    def bracketed(self, steps, stream):
+        """(encode ms list, decode ms list) with events recorded on the stream
+        around each call instead: what the separate-kernel comparator is timed
+        with, gaps between calls included."""
         import torch
         ev = TimingEvents(3 * steps)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for i in range(steps):
             ev.record(3 * i, stream)
             self.enc(i)
@@ -496,11 +523,10 @@ class Leg:
             self.dec(i)
             ev.record(3 * i + 2, stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         enc_ms = [ev.ms(3 * i, 3 * i + 1) for i in range(steps)]
         dec_ms = [ev.ms(3 * i + 1, 3 * i + 2) for i in range(steps)]
         ev.close()
-        return wall, enc_ms, dec_ms
+        return enc_ms, dec_ms
 
     def close(self):
         import torch
@@ -567,8 +593,12 @@ def other_workload(kvc, name, dev, stream, steps, prewarm_s, with_transform=True
     e, d = kernel_summary(leg, enc_ms), kernel_summary(leg, dec_ms)
     out = {"config": leg.config, "steps": steps, "bytes": {"raw": leg.raw_bytes, "encoded": leg.enc_bytes}}
     if name == "tiny":   # launch-bound: latency, not a roofline figure
-        out.update(encode_us={"mean": e["ms"] * 1e3, "median": e["ms_median"] * 1e3, "min": e["ms_min"] * 1e3},
-                   decode_us={"mean": d["ms"] * 1e3, "median": d["ms_median"] * 1e3, "min": d["ms_min"] * 1e3})
+        us = lambda ms: dict(zip(("mean", "median", "min"), (v * 1e3 for v in _stats(ms))))
+        be, bd = leg.bracketed(steps, stream)
+        out.update(encode_us=us(enc_ms), decode_us=us(dec_ms),
+                   encode_us_call=us(be), decode_us_call=us(bd),
+                   what="kernel time (events on the dispatches) and call time (events on the stream around "
+                        "each call, launch included)")
     else:
         out.update(encode=e, decode=d, ms_per_step=wall / steps * 1e3,
                    raw_GBps_step=leg.raw_bytes / (wall / steps) / 1e9,
@@ -626,7 +656,10 @@ def main():
 
     unfused = pipeline = None
     if not p.paged and not a.no_unfused:
-        unfused = unfused_leg(kvc, p, leg.src, leg.outs, leg.dsts, a, stream, t_enc, t_dec, leg.raw_bytes)
+        be, bd = leg.bracketed(a.steps, stream)
+        unfused = unfused_leg(kvc, p, leg.src, leg.outs, leg.dsts, a, stream, _stats(be)[0] / 1e3,
+                              _stats(bd)[0] / 1e3, leg.raw_bytes)
+        unfused["fused_bracketed_ms"] = {"encode": _stats(be)[0], "decode": _stats(bd)[0]}
     if not p.paged and not a.no_pipeline:
         pipeline = pipeline_leg(kvc, p, leg.src[0], leg.dsts[0], stream, leg.raw_bytes)
     dominant = "encode" if t_enc >= t_dec else "decode"

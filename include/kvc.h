@@ -92,7 +92,7 @@ extern "C" {
 
 /* 2: every code and meta slab of the blob padded to a multiple of 256 bytes.
  * 3: kvc_paged carries an optional pool-order item list (kvc_paged_order).
- * 4: kvc_encode_with / kvc_decode_with choose the transform. */
+ * 4: the *_with calls, whose kvc_launch_opts carries the transform and kernel timing events. */
 #define KVC_ABI_VERSION 4
 
 typedef enum kvc_status {
@@ -245,21 +245,41 @@ typedef enum kvc_transform {
 } kvc_transform;
 
 /*
- * kvc_encode / kvc_decode with the transform chosen (a kvc_transform
- * value), everything else of the launch as the automatic choice makes it:
- * the pair the design choice of the transform is measured with.  The
+ * Options of the *_with calls (a NULL pointer means all defaults).
+ *   transform: a kvc_transform value.  Paged calls accept AUTO and MATRIX
+ *     (their kernels run on the matrix cores).
+ *   start_event, stop_event: hipEvent_t handles created by the caller on the
+ *     current device, or NULL.  start_event takes the time the call's first
+ *     kernel starts, stop_event the time its last kernel ends (a call runs
+ *     one kernel, or one per code width and per group of 64 requests), so
+ *     that their elapsed time is the call's kernel time without the gaps of
+ *     events recorded on the stream around it.  A call that launches nothing
+ *     records both on the stream.  The events must not be recorded elsewhere
+ *     until the call's work has completed.
+ */
+typedef struct kvc_launch_opts {
+  int32_t transform;
+  int32_t reserved;     /* 0 */
+  void* start_event;
+  void* stop_event;
+} kvc_launch_opts;
+
+/*
+ * kvc_encode / kvc_decode with options: the transform chosen, everything
+ * else of the launch as the automatic choice makes it (the pair the choice
+ * of the transform is measured with), and kernel timing events.  The
  * butterfly and matrix-core encodes sum the same +-1 products in different
  * orders, so their blobs may differ where a rotated value rounds across a
  * code or meta boundary (both meet the oracle's criteria); every decode
  * transforms integer codes within groups exactly, so decodes of one blob
  * are bit-identical whichever transform runs.  Arguments and errors as
- * kvc_encode / kvc_decode, plus KVC_EINVAL for a transform outside the
- * enum.
+ * kvc_encode / kvc_decode, plus KVC_EINVAL for a transform outside the enum
+ * or a nonzero reserved field, and KVC_EHIP if an event cannot be used.
  */
 kvc_status kvc_encode_with(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes,
-                           int32_t transform, void* stream);
+                           const kvc_launch_opts* opts, void* stream);
 kvc_status kvc_decode_with(const kvc_desc* desc, const void* in, uint64_t in_bytes, void* kv_out,
-                           int32_t transform, void* stream);
+                           const kvc_launch_opts* opts, void* stream);
 
 /*
  * Host prologue of the paged calls: offsets_host[r] = sum of the blob
@@ -323,6 +343,18 @@ kvc_status kvc_encode_paged(const kvc_desc* desc, const void* pool,
  */
 kvc_status kvc_decode_paged(const kvc_desc* desc, const void* in, uint64_t in_bytes,
                             const kvc_paged* paged, void* pool, void* stream);
+
+/*
+ * kvc_encode_paged / kvc_decode_paged with the options of kvc_launch_opts
+ * (transform AUTO or MATRIX, else KVC_EINVAL).  Results are those of the
+ * calls without options.
+ */
+kvc_status kvc_encode_paged_with(const kvc_desc* desc, const void* pool, const kvc_paged* paged,
+                                 void* out, uint64_t out_bytes, const kvc_launch_opts* opts,
+                                 void* stream);
+kvc_status kvc_decode_paged_with(const kvc_desc* desc, const void* in, uint64_t in_bytes,
+                                 const kvc_paged* paged, void* pool, const kvc_launch_opts* opts,
+                                 void* stream);
 
 /*
  * Test hook: the rotated values y = H (s * x) / sqrt(D) of a contiguous KV

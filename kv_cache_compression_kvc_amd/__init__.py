@@ -111,15 +111,22 @@ def sign_mask(seed, head_dim):
     return sum(int(w) << (64 * i) for i, w in enumerate(words))
 
 
-def _transform(transform):
-    if transform not in _lib.TRANSFORM:
+def _opts(transform, events):
+    """kvc_launch_opts for the *_with calls, or None when neither is given.
+    ``events``: (start, stop) hipEvent_t handles (ints or c_void_p; either may be None)."""
+    if transform is None and events is None:
+        return None
+    if transform is not None and transform not in _lib.TRANSFORM:
         raise ValueError("transform must be one of %s" % sorted(_lib.TRANSFORM))
-    return _lib.TRANSFORM[transform]
+    start, stop = events if events is not None else (None, None)
+    val = lambda e: e.value if isinstance(e, ctypes.c_void_p) else e
+    return _lib.KvcLaunchOpts(_lib.TRANSFORM[transform or "auto"], 0, val(start), val(stop))
 
 
-def encode(kv, bits_k, bits_v, group, seed=0, out=None, stream=None, transform=None):
+def encode(kv, bits_k, bits_v, group, seed=0, out=None, stream=None, transform=None, events=None):
     """Encode a contiguous [L, 2, T, H, D] GPU tensor; returns the uint8 blob.
-    ``transform`` ("auto", "matrix" or "butterfly") calls kvc_encode_with."""
+    ``transform`` ("auto", "matrix" or "butterfly") or ``events`` (start,
+    stop hipEvent_t handles for the kernels' own times) call kvc_encode_with."""
     L, T, H, D = _kv_shape(kv.shape, "kv")
     dt = _dtype_name(kv)
     _check_cuda(kv, out)
@@ -127,28 +134,30 @@ def encode(kv, bits_k, bits_v, group, seed=0, out=None, stream=None, transform=N
     if out is None:
         out = torch.empty(total, dtype=torch.uint8, device=kv.device)
     d = _desc(L, T, H, D, dt, bits_k, bits_v, group, seed)
-    if transform is None:
+    o = _opts(transform, events)
+    if o is None:
         _lib.check(_lib.lib().kvc_encode(ctypes.byref(d), _ptr(kv), _ptr(out), _nbytes(out), _stream(stream)))
     else:
         _lib.check(_lib.lib().kvc_encode_with(ctypes.byref(d), _ptr(kv), _ptr(out), _nbytes(out),
-                                              _transform(transform), _stream(stream)))
+                                              ctypes.byref(o), _stream(stream)))
     return out
 
 
-def decode(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, stream=None, transform=None):
+def decode(blob, shape, dtype, bits_k, bits_v, group, seed=0, out=None, stream=None, transform=None, events=None):
     """Decode a blob into a [L, 2, T, H, D] GPU tensor of ``dtype``.
-    ``transform`` ("auto", "matrix" or "butterfly") calls kvc_decode_with."""
+    ``transform`` / ``events`` as for :func:`encode` (kvc_decode_with)."""
     L, T, H, D = _kv_shape(shape, "shape")
     _check_out(out, shape, _torch_dtype(dtype))
     _check_cuda(blob, out)
     if out is None:
         out = torch.empty(tuple(shape), dtype=_torch_dtype(dtype), device=blob.device)
     d = _desc(L, T, H, D, dtype, bits_k, bits_v, group, seed)
-    if transform is None:
+    o = _opts(transform, events)
+    if o is None:
         _lib.check(_lib.lib().kvc_decode(ctypes.byref(d), _ptr(blob), _nbytes(blob), _ptr(out), _stream(stream)))
     else:
         _lib.check(_lib.lib().kvc_decode_with(ctypes.byref(d), _ptr(blob), _nbytes(blob), _ptr(out),
-                                              _transform(transform), _stream(stream)))
+                                              ctypes.byref(o), _stream(stream)))
     return out
 
 
@@ -337,9 +346,10 @@ def _paged(pool, block_table, seq_lens, out_offsets, err_flag, order=None):
 
 
 def encode_paged(pool, block_table, seq_lens, out_offsets, total, bits_k, bits_v, group, seed=0,
-                 out=None, err_flag=None, stream=None, order=None):
+                 out=None, err_flag=None, stream=None, order=None, transform=None, events=None):
     """Encode every request of a [L, 2, NB, BS, H, D] pool into one blob buffer
-    (in pool order when ``order`` holds the call's :func:`paged_order` items)."""
+    (in pool order when ``order`` holds the call's :func:`paged_order` items).
+    ``transform`` / ``events`` as for :func:`encode` (kvc_encode_paged_with)."""
     L, NB, BS, H, D = _pool_shape(pool)
     dt = _dtype_name(pool)
     pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag, order)
@@ -347,22 +357,33 @@ def encode_paged(pool, block_table, seq_lens, out_offsets, total, bits_k, bits_v
     if out is None:
         out = torch.empty(int(total), dtype=torch.uint8, device=pool.device)
     d = _desc(L, 0, H, D, dt, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_encode_paged(ctypes.byref(d), _ptr(pool), ctypes.byref(pg), _ptr(out),
-                                           _nbytes(out), _stream(stream)))
+    o = _opts(transform, events)
+    if o is None:
+        _lib.check(_lib.lib().kvc_encode_paged(ctypes.byref(d), _ptr(pool), ctypes.byref(pg), _ptr(out),
+                                               _nbytes(out), _stream(stream)))
+    else:
+        _lib.check(_lib.lib().kvc_encode_paged_with(ctypes.byref(d), _ptr(pool), ctypes.byref(pg), _ptr(out),
+                                                    _nbytes(out), ctypes.byref(o), _stream(stream)))
     return out
 
 
 def decode_paged(blob, pool, block_table, seq_lens, out_offsets, bits_k, bits_v, group, seed=0,
-                 err_flag=None, stream=None, order=None):
+                 err_flag=None, stream=None, order=None, transform=None, events=None):
     """Decode every request's blob back into the pool slots of its block table
-    (in pool order when ``order`` holds the call's :func:`paged_order` items)."""
+    (in pool order when ``order`` holds the call's :func:`paged_order` items).
+    ``transform`` / ``events`` as for :func:`encode` (kvc_decode_paged_with)."""
     L, NB, BS, H, D = _pool_shape(pool)
     dt = _dtype_name(pool)
     pg = _paged(pool, block_table, seq_lens, out_offsets, err_flag, order)
     _check_cuda(blob, pool)
     d = _desc(L, 0, H, D, dt, bits_k, bits_v, group, seed)
-    _lib.check(_lib.lib().kvc_decode_paged(ctypes.byref(d), _ptr(blob), _nbytes(blob), ctypes.byref(pg),
-                                           _ptr(pool), _stream(stream)))
+    o = _opts(transform, events)
+    if o is None:
+        _lib.check(_lib.lib().kvc_decode_paged(ctypes.byref(d), _ptr(blob), _nbytes(blob), ctypes.byref(pg),
+                                               _ptr(pool), _stream(stream)))
+    else:
+        _lib.check(_lib.lib().kvc_decode_paged_with(ctypes.byref(d), _ptr(blob), _nbytes(blob), ctypes.byref(pg),
+                                                    _ptr(pool), ctypes.byref(o), _stream(stream)))
     return pool
 
 

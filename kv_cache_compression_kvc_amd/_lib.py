@@ -29,7 +29,7 @@ EXPORTS = [
     "kvc_debug_rotate", "kvc_unfused_workspace_size", "kvc_encode_unfused", "kvc_decode_unfused",
     "kvc_chunked_size", "kvc_encode_send", "kvc_receive_decode", "kvc_probe_copy",
     "kvc_encode_unfused_noalloc", "kvc_probe_stream", "kvc_paged_order", "kvc_encode_with",
-    "kvc_decode_with",
+    "kvc_decode_with", "kvc_encode_paged_with", "kvc_decode_paged_with",
 ]
 TRANSFORM = {"auto": 0, "matrix": 1, "butterfly": 2}   # kvc_transform
 NOALLOC_WORKSPACE_BYTES = 64 << 20   # KVC_NOALLOC_WORKSPACE_BYTES
@@ -78,6 +78,15 @@ class KvcPagedItem(ctypes.Structure):
     ]
 
 
+class KvcLaunchOpts(ctypes.Structure):
+    _fields_ = [
+        ("transform", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("start_event", ctypes.c_void_p),
+        ("stop_event", ctypes.c_void_p),
+    ]
+
+
 class KvcError(RuntimeError):
     def __init__(self, status, lib=None):
         text = lib.kvc_strerror(status).decode() if lib is not None else ""
@@ -98,9 +107,13 @@ def _declare(lib, names):
         "kvc_decode": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_uint64,
                                         ctypes.c_void_p, ctypes.c_void_p]),
         "kvc_encode_with": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_void_p,
-                                             ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p]),
+                                             ctypes.c_uint64, P(KvcLaunchOpts), ctypes.c_void_p]),
         "kvc_decode_with": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_uint64,
-                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+                                             ctypes.c_void_p, P(KvcLaunchOpts), ctypes.c_void_p]),
+        "kvc_encode_paged_with": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, P(KvcPaged), ctypes.c_void_p,
+                                                   ctypes.c_uint64, P(KvcLaunchOpts), ctypes.c_void_p]),
+        "kvc_decode_paged_with": (ctypes.c_int32, [P(KvcDesc), ctypes.c_void_p, ctypes.c_uint64, P(KvcPaged),
+                                                   ctypes.c_void_p, P(KvcLaunchOpts), ctypes.c_void_p]),
         "kvc_paged_order": (ctypes.c_int32, [P(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32),
                                              P(ctypes.c_int64), ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                              P(ctypes.c_int64)]),

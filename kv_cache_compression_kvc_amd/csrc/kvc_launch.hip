@@ -3,6 +3,7 @@
  * kernel instance for a validated plan and launch it on the caller's stream
  * with a persistent grid (one or all resident waves per SIMD, per kernel).
  */
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -219,9 +220,31 @@ LaunchShape launch_shape(Op op, const LaunchArgs& a, int head_dim, int bits, int
   return {1, bfly ? dev::kDecodeButterfly : dev::kDecodeWaitStores, a.blob_total >= kDecodeThreePerCuBlob ? 3 : 0};
 }
 
-int run_plan(Op op, const Plan& plan, void* stream, int transform = KVC_TRANSFORM_AUTO) {
+/* A call's options: the transform (kvc_transform) and the events that take
+ * the first kernel's start and the last kernel's end (either may be null). */
+struct CallOpts {
+  int transform = KVC_TRANSFORM_AUTO;
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+int read_opts(const kvc_launch_opts* o, bool paged, CallOpts* out) {
+  if (!o) return KVC_OK;
+  const int tf = o->transform;
+  if (o->reserved != 0 || tf < KVC_TRANSFORM_AUTO || tf > KVC_TRANSFORM_BUTTERFLY) return KVC_EINVAL;
+  if (paged && tf == KVC_TRANSFORM_BUTTERFLY) return KVC_EINVAL;
+  out->transform = tf;
+  out->start = static_cast<hipEvent_t>(o->start_event);
+  out->stop = static_cast<hipEvent_t>(o->stop_event);
+  return KVC_OK;
+}
+
+/* Calls fn(kernel, grid, args) for every launch of a plan, in order;
+ * stops at the first nonzero status fn returns. */
+template <typename F>
+int each_launch(Op op, const Plan& plan, const CallOpts& opts, F&& fn) {
   for (int i = 0; i < plan.n_launch; ++i) {
-    const LaunchShape shape = launch_shape(op, plan.args[i], plan.head_dim, plan.bits[i], transform);
+    const LaunchShape shape = launch_shape(op, plan.args[i], plan.head_dim, plan.bits[i], opts.transform);
     Kernel k = pick(op, plan.head_dim, plan.dtype, plan.bits[i], plan.group, plan.args[i].paged != 0, shape.mode);
     if (!k) return KVC_ESHAPE;
     int64_t resident = 0;
@@ -242,11 +265,43 @@ int run_plan(Op op, const Plan& plan, void* stream, int transform = KVC_TRANSFOR
       }
       const int64_t grid = std::min<int64_t>(a.total_items, waves);
       if (grid <= 0) continue;
-      hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(grid)), dim3(64), 0, static_cast<hipStream_t>(stream), a);
-      if (hipGetLastError() != hipSuccess) return KVC_EHIP;
+      if ((st = fn(k, static_cast<unsigned>(grid), a)) != KVC_OK) return st;
     }
   }
   return KVC_OK;
+}
+
+int run_plan(Op op, const Plan& plan, void* stream, const CallOpts& opts = CallOpts()) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!opts.start && !opts.stop)
+    return each_launch(op, plan, opts, [&](Kernel k, unsigned grid, LaunchArgs& a) {
+      hipLaunchKernelGGL(k, dim3(grid), dim3(64), 0, s, a);
+      return hipGetLastError() == hipSuccess ? KVC_OK : KVC_EHIP;
+    });
+  // timed: the events ride on the dispatches themselves, the start event on
+  // the first and the stop event on the last
+  int64_t n = 0;
+  int st = each_launch(op, plan, opts, [&](Kernel, unsigned, LaunchArgs&) {
+    ++n;
+    return KVC_OK;
+  });
+  if (st != KVC_OK) return st;
+  if (n == 0) {
+    if (opts.start && hipEventRecord(opts.start, s) != hipSuccess) return KVC_EHIP;
+    if (opts.stop && hipEventRecord(opts.stop, s) != hipSuccess) return KVC_EHIP;
+    return KVC_OK;
+  }
+  int64_t j = 0;
+  return each_launch(op, plan, opts, [&](Kernel k, unsigned grid, LaunchArgs& a) {
+    void* args[] = {&a};
+    hipEvent_t e0 = j == 0 ? opts.start : nullptr;
+    hipEvent_t e1 = j == n - 1 ? opts.stop : nullptr;
+    ++j;
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(64), args, 0, s, e0, e1, 0) ==
+                   hipSuccess
+               ? KVC_OK
+               : KVC_EHIP;
+  });
 }
 
 }  // namespace
@@ -268,21 +323,43 @@ kvc_status kvc_decode(const kvc_desc* desc, const void* in, uint64_t in_bytes, v
   return static_cast<kvc_status>(st);
 }
 
-kvc_status kvc_encode_with(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes, int32_t transform,
-                           void* stream) {
-  if (transform < KVC_TRANSFORM_AUTO || transform > KVC_TRANSFORM_BUTTERFLY) return KVC_EINVAL;
+kvc_status kvc_encode_with(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes,
+                           const kvc_launch_opts* opts, void* stream) {
+  kvc::CallOpts o;
+  int st = kvc::read_opts(opts, false, &o);
   kvc::Plan plan;
-  int st = kvc::plan_contiguous(kvc::Op::Encode, desc, kv, out, out_bytes, &plan);
-  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Encode, plan, stream, transform);
+  if (st == KVC_OK) st = kvc::plan_contiguous(kvc::Op::Encode, desc, kv, out, out_bytes, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Encode, plan, stream, o);
   return static_cast<kvc_status>(st);
 }
 
-kvc_status kvc_decode_with(const kvc_desc* desc, const void* in, uint64_t in_bytes, void* kv_out, int32_t transform,
-                           void* stream) {
-  if (transform < KVC_TRANSFORM_AUTO || transform > KVC_TRANSFORM_BUTTERFLY) return KVC_EINVAL;
+kvc_status kvc_decode_with(const kvc_desc* desc, const void* in, uint64_t in_bytes, void* kv_out,
+                           const kvc_launch_opts* opts, void* stream) {
+  kvc::CallOpts o;
+  int st = kvc::read_opts(opts, false, &o);
   kvc::Plan plan;
-  int st = kvc::plan_contiguous(kvc::Op::Decode, desc, in, kv_out, in_bytes, &plan);
-  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Decode, plan, stream, transform);
+  if (st == KVC_OK) st = kvc::plan_contiguous(kvc::Op::Decode, desc, in, kv_out, in_bytes, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Decode, plan, stream, o);
+  return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_encode_paged_with(const kvc_desc* desc, const void* pool, const kvc_paged* paged, void* out,
+                                 uint64_t out_bytes, const kvc_launch_opts* opts, void* stream) {
+  kvc::CallOpts o;
+  int st = kvc::read_opts(opts, true, &o);
+  kvc::Plan plan;
+  if (st == KVC_OK) st = kvc::plan_paged(kvc::Op::Encode, desc, pool, out, out_bytes, paged, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Encode, plan, stream, o);
+  return static_cast<kvc_status>(st);
+}
+
+kvc_status kvc_decode_paged_with(const kvc_desc* desc, const void* in, uint64_t in_bytes, const kvc_paged* paged,
+                                 void* pool, const kvc_launch_opts* opts, void* stream) {
+  kvc::CallOpts o;
+  int st = kvc::read_opts(opts, true, &o);
+  kvc::Plan plan;
+  if (st == KVC_OK) st = kvc::plan_paged(kvc::Op::Decode, desc, in, pool, in_bytes, paged, &plan);
+  if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Decode, plan, stream, o);
   return static_cast<kvc_status>(st);
 }
 

@@ -82,9 +82,15 @@ def test_transform_argument_is_checked():
     out = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)
     d = _lib.KvcDesc(1, 4, 1, 128, 0, 4, 4, 128, 0)
     lib = _lib.lib()
-    for bad in (-1, 3):
-        assert lib.kvc_encode_with(ctypes.byref(d), x.data_ptr(), out.data_ptr(), out.numel(), bad, None) == -1
-        assert lib.kvc_decode_with(ctypes.byref(d), out.data_ptr(), out.numel(), x.data_ptr(), bad, None) == -1
+    for bad, reserved in ((-1, 0), (3, 0), (0, 1)):
+        o = _lib.KvcLaunchOpts(bad, reserved, None, None)
+        assert lib.kvc_encode_with(ctypes.byref(d), x.data_ptr(), out.data_ptr(), out.numel(), ctypes.byref(o),
+                                   None) == -1
+        assert lib.kvc_decode_with(ctypes.byref(d), out.data_ptr(), out.numel(), x.data_ptr(), ctypes.byref(o),
+                                   None) == -1
+    # no options: the defaults
+    assert lib.kvc_encode_with(ctypes.byref(d), x.data_ptr(), out.data_ptr(), out.numel(), None, None) == 0
+    torch.cuda.synchronize()
     with pytest.raises(ValueError):
         kvc.encode(x, 4, 4, 128, transform="fft")
 
@@ -132,3 +138,55 @@ def test_large_blob_decode_transforms_agree():
     assert torch.equal(xa.view(torch.int16), xbf.view(torch.int16))
     del xa, xbf, blob
     torch.cuda.empty_cache()
+
+
+def _events(n):
+    import bench
+    return bench.TimingEvents(n)
+
+
+def test_timing_events_ride_on_the_kernels():
+    """Events handed to the *_with calls are set by the calls' own dispatches:
+    they read a positive time, the results are those of the calls without
+    them, and a call that launches nothing still records them."""
+    p = _small(128, "bf16", 2, 4, 64, L=3, T=300, H=4)
+    x = inputs.make_kv(p).to(DEV)
+    ref = kvc.encode(x, 2, 4, 64, seed=p.seed)
+    ev = _events(6)
+    blob = kvc.encode(x, 2, 4, 64, seed=p.seed, events=ev.pair(0, 1))       # K and V: two launches
+    xd = kvc.decode(blob, x.shape, "bf16", 2, 4, 64, seed=p.seed, events=ev.pair(2, 3))
+    empty = torch.zeros((2, 2, 0, 4, 128), dtype=torch.bfloat16, device=DEV)
+    kvc.encode(empty, 2, 4, 64, seed=p.seed, events=ev.pair(4, 5))
+    torch.cuda.synchronize()
+    assert torch.equal(blob, ref)
+    xr = kvc.decode(ref, x.shape, "bf16", 2, 4, 64, seed=p.seed)
+    assert torch.equal(xd.view(torch.int16), xr.view(torch.int16))
+    assert ev.ms(0, 1) > 0 and ev.ms(2, 3) > 0 and ev.ms(4, 5) >= 0
+    ev.close()
+
+
+def test_paged_calls_with_options():
+    """The paged *_with calls give the blobs and the pool of the plain calls;
+    the butterfly is refused for them."""
+    p = presets.preset("qwen7b_paged").with_(name="paged-opts", layers=2, num_requests=5, len_min=1,
+                                             len_max=200, seed=4)
+    lens = inputs.request_lengths(p)
+    table, nb = inputs.block_table(p, lens)
+    offs, total = kvc.paged_layout(lens, p.layers, p.kv_heads, p.head_dim, p.bits_k, p.bits_v, p.group, p.dtype)
+    pool = inputs.make_pool(p, nb, device=DEV)
+    bt, sl, of = (torch.from_numpy(a).to(DEV) for a in (table, lens, offs))
+    args = (bt, sl, of)
+    ref = kvc.encode_paged(pool, *args, total, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    ev = _events(4)
+    got = kvc.encode_paged(pool, *args, total, p.bits_k, p.bits_v, p.group, seed=p.seed, transform="matrix",
+                           events=ev.pair(0, 1))
+    back_ref = kvc.decode_paged(ref, torch.zeros_like(pool), *args, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    back = kvc.decode_paged(got, torch.zeros_like(pool), *args, p.bits_k, p.bits_v, p.group, seed=p.seed,
+                            events=ev.pair(2, 3))
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert torch.equal(back.view(torch.int16), back_ref.view(torch.int16))
+    assert ev.ms(0, 1) > 0 and ev.ms(2, 3) > 0
+    ev.close()
+    with pytest.raises(kvc.KvcError, match="KVC_EINVAL"):
+        kvc.encode_paged(pool, *args, total, p.bits_k, p.bits_v, p.group, seed=p.seed, transform="butterfly")
