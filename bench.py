@@ -54,7 +54,9 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -115,6 +117,36 @@ class TimingEvents:
         for e in self._ev:
             self._hip.hipEventDestroy(e)
         self._ev = []
+
+
+class ClockSample:
+    """The GPU's clocks as amd-smi reads them `delay_s` into the pre-warm,
+    while back-to-back encodes and decodes keep the GPU busy (a child
+    process on a thread; the result holds an error text if the tool is
+    missing or its output cannot be read)."""
+
+    def __init__(self, delay_s):
+        self.result = None
+        self._t = threading.Thread(target=self._run, args=(delay_s,), daemon=True)
+        self._t.start()
+
+    def _run(self, delay_s):
+        time.sleep(delay_s)
+        try:
+            p = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True, timeout=20)
+            text = p.stdout[p.stdout.index("{"):]
+            clock = json.loads(text)["gpu_data"][0]["clock"]
+            val = lambda v: v["value"] if isinstance(v, dict) else None
+            gfx = [val(v.get("clk")) for k, v in sorted(clock.items()) if k.startswith("gfx_")]
+            self.result = {"gfx_MHz_per_xcd": gfx, "gfx_max_MHz": val(clock.get("gfx_0", {}).get("max_clk")),
+                           "mem_MHz": val(clock.get("mem_0", {}).get("clk")), "read_at_s": delay_s,
+                           "tool": "amd-smi metric -c"}
+        except Exception as e:  # a missing tool or an unexpected format: report, do not fail the bench
+            self.result = {"error": "%s: %s" % (type(e).__name__, str(e)[:160])}
+
+    def get(self, timeout=25.0):
+        self._t.join(timeout)
+        return self.result
 
 
 def parse(argv=None):
@@ -640,6 +672,7 @@ def main():
     # (a 2 GiB copy right before the timed steps slowed the next ones by up
     # to 10%)
     t0 = time.perf_counter()
+    clocks = ClockSample(a.prewarm_s / 2)
     prewarm_steps = leg.prewarm(a.prewarm_s)
     prewarm = {"seconds": time.perf_counter() - t0, "steps": prewarm_steps}
     for i in range(a.warmup):
@@ -681,6 +714,7 @@ def main():
         "data": "synthetic (seeded Gaussian KV with K outlier channels; no model weights)",
         "config": leg.config,
         "prewarm": prewarm,
+        "clocks": clocks.get(),
         "encode": enc,
         "decode": dec,
         "bytes": {"raw": leg.raw_bytes, "encoded": leg.enc_bytes, "ratio": leg.raw_bytes / leg.enc_bytes},
