@@ -22,8 +22,10 @@
  *     every lane then owns one whole vector in registers;
  *   - encode: the Walsh-Hadamard transform of the tile runs on the matrix
  *     cores (exact bf16 / fp16 products against +-1, fp32 sums), after
- *     which every lane again holds its own vector; the group min/max, the
- *     fp16 meta, the quantization and the packing run inside the lane;
+ *     which every lane again holds its own vector -- or, when a caller asks
+ *     for it, as the in-register butterfly of each lane's vector; the group
+ *     min/max, the fp16 meta, the quantization and the packing run inside
+ *     the lane;
  *   - decode: the codes are transformed within their groups (exactly, on
  *     the matrix cores or as a butterfly), scaled, combined across groups
  *     and rounded to the storage type inside the lane; the rows leave
