@@ -1,5 +1,4 @@
 """GPU parity of the contiguous encode / decode against the oracle."""
-import itertools
 import sys
 
 import numpy as np

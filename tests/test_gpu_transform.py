@@ -10,7 +10,6 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import parity
 import gpu_util
 import kv_cache_compression_kvc_amd as kvc

@@ -1,6 +1,5 @@
 """Pins of the fp16 / bf16 rounding: library conversions, exhaustive search, IEEE facts."""
 import numpy as np
-import pytest
 import torch
 
 import oracle
