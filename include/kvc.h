@@ -59,8 +59,9 @@
  *   - kvc_encode, kvc_decode and their paged forms enqueue kernel launches
  *     only, so they may be captured into a HIP graph and replayed; make one
  *     call of the same kind on the device first, outside the capture (it
- *     fills the occupancy cache).  The chunked send / receive calls record
- *     events and are not meant for capture.
+ *     fills the occupancy cache).  The same holds for the *_with forms
+ *     called without timing events.  The chunked send / receive calls, and
+ *     *_with calls given events, set events and are not meant for capture.
  *
  * Supported: head_dim 64 or 128; bits 2, 4 or 8; group 32, 64 or 128 with
  * group <= head_dim; dtype bf16 or fp16.  Input values must be finite, and
