@@ -54,7 +54,6 @@ import hashlib
 import json
 import os
 import re
-import subprocess
 import sys
 import threading
 import time
@@ -120,33 +119,51 @@ class TimingEvents:
 
 
 class ClockSample:
-    """The GPU's clocks as amd-smi reads them `delay_s` into the pre-warm,
-    while back-to-back encodes and decodes keep the GPU busy (a child
-    process on a thread; the result holds an error text if the tool is
-    missing or its output cannot be read)."""
+    """The GPU's clocks during the pre-warm, while back-to-back encodes and
+    decodes keep it busy: the amdsmi library's GPU metrics (graphics clock
+    of each XCD, memory clock, graphics activity) read from a thread at the
+    given offsets in seconds.  Reading is all it does; an error text is
+    reported instead if the library or the metrics are unavailable."""
 
-    def __init__(self, delay_s):
-        self.result = None
-        self._t = threading.Thread(target=self._run, args=(delay_s,), daemon=True)
+    def __init__(self, offsets_s):
+        self.samples, self.error, self._t, self._smi = [], None, None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:  # no library or no device: report, do not fail the bench
+            self.error = "%s: %s" % (type(e).__name__, str(e)[:160])
+            return
+        self._t = threading.Thread(target=self._run, args=(offsets_s,), daemon=True)
         self._t.start()
 
-    def _run(self, delay_s):
-        time.sleep(delay_s)
-        try:
-            p = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True, timeout=20)
-            text = p.stdout[p.stdout.index("{"):]
-            clock = json.loads(text)["gpu_data"][0]["clock"]
-            val = lambda v: v["value"] if isinstance(v, dict) else None
-            gfx = [val(v.get("clk")) for k, v in sorted(clock.items()) if k.startswith("gfx_")]
-            self.result = {"gfx_MHz_per_xcd": gfx, "gfx_max_MHz": val(clock.get("gfx_0", {}).get("max_clk")),
-                           "mem_MHz": val(clock.get("mem_0", {}).get("clk")), "read_at_s": delay_s,
-                           "tool": "amd-smi metric -c"}
-        except Exception as e:  # a missing tool or an unexpected format: report, do not fail the bench
-            self.result = {"error": "%s: %s" % (type(e).__name__, str(e)[:160])}
+    def _run(self, offsets_s):
+        num = lambda v: v if isinstance(v, (int, float)) else None
+        t0 = time.perf_counter()
+        for at in offsets_s:
+            time.sleep(max(0.0, at - (time.perf_counter() - t0)))
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+            except Exception as e:
+                self.error = "%s: %s" % (type(e).__name__, str(e)[:160])
+                return
+            gfx = m.get("current_gfxclks")
+            self.samples.append({
+                "at_s": round(time.perf_counter() - t0, 3),
+                "gfx_MHz_per_xcd": [v for v in gfx if num(v) is not None] if isinstance(gfx, list) else None,
+                "mem_MHz": num(m.get("current_uclk")),
+                "gfx_activity_pct": num(m.get("average_gfx_activity"))})
 
-    def get(self, timeout=25.0):
-        self._t.join(timeout)
-        return self.result
+    def get(self, timeout=10.0):
+        if self._t is not None:
+            self._t.join(timeout)
+        if self._smi is not None:
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:
+                pass
+        return {"samples": self.samples, "error": self.error, "source": "amdsmi GPU metrics, device 0"}
 
 
 def parse(argv=None):
@@ -671,8 +688,8 @@ def main():
     # the warm-up steps, then the timed steps; the copy probe runs after them
     # (a 2 GiB copy right before the timed steps slowed the next ones by up
     # to 10%)
+    clocks = ClockSample([a.prewarm_s * f for f in (0.25, 0.5, 0.75)])
     t0 = time.perf_counter()
-    clocks = ClockSample(a.prewarm_s / 2)
     prewarm_steps = leg.prewarm(a.prewarm_s)
     prewarm = {"seconds": time.perf_counter() - t0, "steps": prewarm_steps}
     for i in range(a.warmup):
