@@ -451,6 +451,41 @@ def mix_probe(kvc, src, read_bytes, dst, write_bytes, stream, reps=5):
     return best
 
 
+def pool_block_list(p, table, lens, num_blocks):
+    """Every pool block a paged call reads, as indices of [L * 2 * NB] blocks,
+    in the order of the request-order kernels: slab by slab, request by
+    request, block by block."""
+    import numpy as np
+    per_req = [table[r, :-(-int(n) // p.block_size)] for r, n in enumerate(lens)]
+    one_slab = np.concatenate(per_req).astype(np.int64) if per_req else np.zeros(0, np.int64)
+    slabs = np.arange(p.layers * 2, dtype=np.int64) * num_blocks
+    return (slabs[:, None] + one_slab[None, :]).reshape(-1).astype(np.int32)
+
+
+def blocks_probe(kvc, region, block_bytes, blocks, seq, stream_bytes, scatter, stream, reps=3):
+    """Best GB/s of the library's block gather (scatter = 0) or scatter (1)
+    probe over 4, 8 and 16 waves per CU: a plain kernel moving whole pool
+    blocks in the paged kernels' order against a sequential stream."""
+    import torch
+    sb = stream_bytes // 1024 * 1024
+    moved = blocks.numel() * block_bytes + sb
+    best = None
+    for wpc in (4, 8, 16):
+        kvc.probe_blocks(region, block_bytes, blocks, seq, sb, scatter, waves_per_cu=wpc)
+        ev = TimingEvents(2)
+        ev.record(0, stream)
+        for _ in range(reps):
+            kvc.probe_blocks(region, block_bytes, blocks, seq, sb, scatter, waves_per_cu=wpc)
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        gbps = moved * reps / (ev.ms(0, 1) / 1e3) / 1e9
+        ev.close()
+        if best is None or gbps > best["GBps"]:
+            best = {"GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS, "waves_per_cu": wpc}
+    best.update(block_bytes=int(block_bytes), blocks=int(blocks.numel()), stream_bytes=int(sb))
+    return best
+
+
 def leg_probes(kvc, leg, stream, enc, dec):
     """Same-mix yardsticks of the encode and the decode of a leg, and each
     kernel's fraction of its yardstick."""
@@ -460,9 +495,18 @@ def leg_probes(kvc, leg, stream, enc, dec):
     pd = mix_probe(kvc, leg.outs[0], leg.enc_bytes, dst, leg.raw_bytes, stream)
     enc["frac_same_mix_probe"] = enc["hbm_GBps"] / pe["GBps"]
     dec["frac_same_mix_probe"] = dec["hbm_GBps"] / pd["GBps"]
-    return {"encode_mix": pe, "decode_mix": pd,
-            "what": "library streaming probe reading and writing the kernel's bytes in its ratio, "
-                    "best of 4/8/16 waves per CU"}
+    out = {"encode_mix": pe, "decode_mix": pd,
+           "what": "library streaming probe reading and writing the kernel's bytes in its ratio, "
+                   "best of 4/8/16 waves per CU"}
+    if leg.p.paged:   # the same blocks in the table's order: reads scattered (encode), writes scattered (decode)
+        region = leg.src[0].view(-1).view(__import__("torch").uint8)
+        out["encode_blocks"] = blocks_probe(kvc, region, leg.block_bytes, leg.blocks, leg.outs[0], leg.enc_bytes,
+                                            0, stream)
+        out["decode_blocks"] = blocks_probe(kvc, dst, leg.block_bytes, leg.blocks, leg.outs[0], leg.enc_bytes,
+                                            1, stream)
+        enc["frac_block_probe"] = enc["hbm_GBps"] / out["encode_blocks"]["GBps"]
+        dec["frac_block_probe"] = dec["hbm_GBps"] / out["decode_blocks"]["GBps"]
+    return out
 
 
 class Leg:
@@ -486,6 +530,8 @@ class Leg:
             self.outs = [torch.empty(total, dtype=torch.uint8, device=dev) for _ in range(nsets)]
             self.dsts = [torch.empty_like(self.src[0]) for _ in range(nsets)]
             self.bt, self.sl, self.of = (torch.from_numpy(a).to(dev) for a in (table, lens, offs))
+            self.blocks = torch.from_numpy(pool_block_list(p, table, lens, nb)).to(dev)
+            self.block_bytes = p.block_size * H * D * 2
             self.total = total
             tokens = int(lens.sum())
             self.raw_bytes = L * 2 * tokens * H * D * 2
@@ -580,6 +626,7 @@ class Leg:
     def close(self):
         import torch
         del self.src, self.outs, self.dsts, self.order
+        self.blocks = None
         torch.cuda.empty_cache()
 
 

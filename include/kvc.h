@@ -477,6 +477,26 @@ kvc_status kvc_probe_copy(const void* src, void* dst, uint64_t bytes, void* stre
 kvc_status kvc_probe_stream(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes,
                             int32_t waves_per_cu, void* stream);
 
+/*
+ * Measurement helper with the access pattern of the paged kernels: a block
+ * region of region_blocks blocks of block_bytes (a multiple of 1024) and a
+ * sequential stream of stream_bytes (a multiple of 1024).  For each of the
+ * n_blocks entries of the device array `blocks` (int32, in list order)
+ * whole block blocks[i] of the region is moved, and the stream advances by
+ * its share, so the two keep the ratio n_blocks * block_bytes :
+ * stream_bytes.  scatter = 0 reads the listed blocks of `region` and writes
+ * the stream to `seq` (the encode of a pool in table order); scatter = 1
+ * reads the stream from `seq` and writes the listed blocks of `region` (the
+ * decode).  Entries outside [0, region_blocks) move no block.  Written
+ * bytes are unspecified.  Grid: waves_per_cu (1..32) one-wave workgroups
+ * per CU, grid-strided over the list.  Errors: KVC_EINVAL (null pointer
+ * with a nonzero size, negative counts, scatter not 0 or 1, waves_per_cu
+ * out of range, n_blocks * stream_bytes / 1024 past 2^62), KVC_EALIGN.
+ */
+kvc_status kvc_probe_blocks(void* region, int64_t region_blocks, uint32_t block_bytes, const int32_t* blocks,
+                            int64_t n_blocks, void* seq, uint64_t stream_bytes, int32_t scatter,
+                            int32_t waves_per_cu, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

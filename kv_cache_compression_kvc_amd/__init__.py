@@ -25,7 +25,7 @@ from ._lib import KvcDesc, KvcPaged, KvcError, DTYPE
 
 __all__ = [
     "KvcError", "DTYPE", "abi_version", "encoded_size", "sign_mask", "encode", "decode",
-    "paged_layout", "paged_order", "encode_paged", "decode_paged", "debug_rotate", "probe_copy", "probe_stream",
+    "paged_layout", "paged_order", "encode_paged", "decode_paged", "debug_rotate", "probe_copy", "probe_stream", "probe_blocks",
     "unfused_workspace_size", "encode_unfused", "decode_unfused", "encode_unfused_noalloc",
     "chunked_size", "encode_send", "receive_decode",
 ]
@@ -408,6 +408,22 @@ def probe_copy(src, dst, stream=None):
         raise ValueError("destination too small")
     _lib.check(_lib.lib().kvc_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
     return dst
+
+
+def probe_blocks(region, block_bytes, blocks, seq, stream_bytes, scatter, waves_per_cu=8, stream=None):
+    """Block gather / scatter yardstick (kvc_probe_blocks): ``region`` holds
+    whole blocks of ``block_bytes``; ``blocks`` is a device int32 tensor of
+    block indices moved in list order against ``stream_bytes`` of ``seq``."""
+    _check_cuda(region, seq, blocks)
+    if blocks.dtype != torch.int32 or blocks.dim() != 1:
+        raise ValueError("blocks must be a 1-D int32 tensor")
+    if stream_bytes > _nbytes(seq):
+        raise ValueError("stream_bytes exceeds seq")
+    region_blocks = _nbytes(region) // int(block_bytes)
+    _lib.check(_lib.lib().kvc_probe_blocks(_ptr(region), region_blocks, int(block_bytes), _ptr(blocks),
+                                           blocks.numel(), _ptr(seq), int(stream_bytes), int(scatter),
+                                           int(waves_per_cu), _stream(stream)))
+    return region if scatter else seq
 
 
 def probe_stream(src, read_bytes, dst, write_bytes, waves_per_cu=8, stream=None):

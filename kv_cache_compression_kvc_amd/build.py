@@ -55,7 +55,7 @@ def build(jobs=None, verbose=False):
         obj = os.path.join(BUILD, "kvc_inst_d%d_t%d.o" % (d, dt))
         tasks.append([HIPCC] + HIP_FLAGS + ["-DKVC_D=%d" % d, "-DKVC_DT=%d" % dt, "-c",
                                             os.path.join(CSRC, "kvc_inst.hip"), "-o", obj])
-    for name in ("kvc_launch.hip", "kvc_unfused.hip", "kvc_pipeline.hip", "kvc_host.cpp"):
+    for name in ("kvc_launch.hip", "kvc_probe.hip", "kvc_unfused.hip", "kvc_pipeline.hip", "kvc_host.cpp"):
         obj = os.path.join(BUILD, name.split(".")[0] + ".o")
         src = os.path.join(CSRC, name)
         lang = ["-x", "hip"] if name.endswith(".hip") else []

@@ -15,81 +15,6 @@
 #include "kvc_plan.h"
 
 namespace kvc {
-namespace dev {
-
-/* Streaming 16-byte copy: the achievable-bandwidth yardstick. */
-__global__ __launch_bounds__(256) void copy_kernel(const v4u* __restrict__ src, v4u* __restrict__ dst,
-                                                   uint64_t n) {
-  const uint64_t stride = uint64_t(gridDim.x) * blockDim.x;
-  uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const v4u a0 = __builtin_nontemporal_load(src + i);
-    const v4u a1 = __builtin_nontemporal_load(src + i + stride);
-    const v4u a2 = __builtin_nontemporal_load(src + i + 2 * stride);
-    const v4u a3 = __builtin_nontemporal_load(src + i + 3 * stride);
-    __builtin_nontemporal_store(a0, dst + i);
-    __builtin_nontemporal_store(a1, dst + i + stride);
-    __builtin_nontemporal_store(a2, dst + i + 2 * stride);
-    __builtin_nontemporal_store(a3, dst + i + 3 * stride);
-  }
-  for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
-}
-
-/* Streaming mix of reads and writes at a fixed ratio: nr 1 KiB chunks of src
- * read and nw written to dst (a chunk: 64 lanes x 16 bytes).  The larger
- * stream is walked in runs of 4 consecutive chunks, grid-strided; the run
- * covering chunks [4u, 4u + 4) of it also moves chunks [floor(4u * ns / nl),
- * floor((4u + 4) * ns / nl)) of the smaller stream, so the two keep their
- * ratio at every point.  The stored data does not depend on the loads.  The
- * yardstick for a kernel with the same traffic mix. */
-__global__ __launch_bounds__(64) void stream_kernel(const v4u* __restrict__ src, uint64_t nr, v4u* __restrict__ dst,
-                                                    uint64_t nw) {
-  const uint64_t nl = nr > nw ? nr : nw, ns = nr > nw ? nw : nr;
-  const bool reads_lead = nr >= nw;
-  const int lane = threadIdx.x;
-  v4u acc = {0, 0, 0, 0};
-  const uint64_t nu = (nl + 3) / 4, u0 = blockIdx.x, g = gridDim.x;
-  // lo = floor(4u * ns / nl) with remainder, carried along without divisions
-  uint64_t lo = 4 * u0 * ns / nl, rem = 4 * u0 * ns - lo * nl;
-  const uint64_t dq = 4 * g * ns / nl, dr = 4 * g * ns - dq * nl;
-  for (uint64_t u = u0; u < nu; u += g) {
-    const uint64_t c0 = 4 * u;
-    uint64_t hi = ns;
-    if (c0 + 4 <= nl) {  // floor((4u + 4) * ns / nl) = lo + floor((rem + 4 ns) / nl), at most lo + 4
-      uint64_t t = rem + 4 * ns;
-      hi = lo;
-      while (t >= nl) {
-        t -= nl;
-        ++hi;
-      }
-    }
-    const uint64_t n_lead = nl - c0 < 4 ? nl - c0 : 4;
-    for (uint64_t k = 0; k < n_lead; ++k) {
-      const uint64_t c = c0 + k;
-      if (reads_lead)
-        acc ^= __builtin_nontemporal_load(src + c * 64 + lane);
-      else
-        __builtin_nontemporal_store(v4u{uint32_t(c), uint32_t(lane), 0u, 0u}, dst + c * 64 + lane);
-    }
-    for (uint64_t c = lo; c < hi; ++c) {
-      if (reads_lead)
-        __builtin_nontemporal_store(v4u{uint32_t(c), uint32_t(lane), 0u, 0u}, dst + c * 64 + lane);
-      else
-        acc ^= __builtin_nontemporal_load(src + c * 64 + lane);
-    }
-    lo += dq;
-    rem += dr;
-    if (rem >= nl) {
-      rem -= nl;
-      lo += 1;
-    }
-  }
-  // the loaded data is consumed here, so the loads stay
-  asm volatile("" ::"v"(acc.x), "v"(acc.y), "v"(acc.z), "v"(acc.w));
-}
-
-}  // namespace dev
-
 namespace {
 
 Kernel pick(Op op, int d, int dt, int b, int g, bool paged, int mode) {
@@ -384,40 +309,6 @@ kvc_status kvc_debug_rotate(const kvc_desc* desc, const void* kv, float* y_out, 
   int st = kvc::plan_contiguous(kvc::Op::Rotate, desc, kv, y_out, 0, &plan);
   if (st == KVC_OK) st = kvc::run_plan(kvc::Op::Rotate, plan, stream);
   return static_cast<kvc_status>(st);
-}
-
-kvc_status kvc_probe_stream(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes,
-                            int32_t waves_per_cu, void* stream) {
-  if (read_bytes == 0 && write_bytes == 0) return KVC_OK;
-  if ((read_bytes && !src) || (write_bytes && !dst) || waves_per_cu < 1 || waves_per_cu > 32) return KVC_EINVAL;
-  if ((read_bytes & 1023u) || (write_bytes & 1023u) || (reinterpret_cast<uintptr_t>(src) & 15u) ||
-      (reinterpret_cast<uintptr_t>(dst) & 15u))
-    return KVC_EALIGN;
-  int device = 0, cus = 0;
-  if (hipGetDevice(&device) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
-    return KVC_EHIP;
-  const uint64_t nr = read_bytes / 1024, nw = write_bytes / 1024;
-  const uint64_t grid = std::min<uint64_t>(uint64_t(cus) * uint64_t(waves_per_cu), std::max(nr, nw));
-  hipLaunchKernelGGL(kvc::dev::stream_kernel, dim3(static_cast<unsigned>(grid)), dim3(64), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const kvc::dev::v4u*>(src), nr,
-                     static_cast<kvc::dev::v4u*>(dst), nw);
-  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_EHIP;
-}
-
-kvc_status kvc_probe_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
-  if (bytes == 0) return KVC_OK;
-  if (!src || !dst) return KVC_EINVAL;
-  if ((bytes & 15u) || (reinterpret_cast<uintptr_t>(src) & 15u) || (reinterpret_cast<uintptr_t>(dst) & 15u))
-    return KVC_EALIGN;
-  int64_t resident = 0;
-  int st = kvc::resident_groups(reinterpret_cast<kvc::Kernel>(kvc::dev::copy_kernel), 256, &resident);
-  if (st != KVC_OK) return static_cast<kvc_status>(st);
-  const uint64_t n = bytes / 16;
-  const uint64_t grid = std::min<uint64_t>(uint64_t(resident), (n + 255) / 256);
-  hipLaunchKernelGGL(kvc::dev::copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const kvc::dev::v4u*>(src), static_cast<kvc::dev::v4u*>(dst), n);
-  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_EHIP;
 }
 
 }  // extern "C"

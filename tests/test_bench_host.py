@@ -45,3 +45,17 @@ def test_committed_counters_cover_every_bench_workload():
     for w in ("llama3_8b_4k", "llama3_8b_32k", "llama3_70b_16k", "qwen7b_paged"):
         for op in ("encode", "decode"):
             assert rec[w][op]["hbm_bytes_per_launch"] > 0
+
+
+def test_pool_block_list_order():
+    """The yardstick's block list: every block a paged call reads, slab by
+    slab, request by request, block by block, as indices into L * 2 * NB."""
+    import numpy as np
+    from kv_cache_compression_kvc_amd import presets
+    p = presets.preset("qwen7b_paged").with_(layers=2, block_size=16)
+    table = np.array([[5, 1, 9, -1], [2, -1, -1, -1], [7, 8, 0, 3]], dtype=np.int32)
+    lens = np.array([33, 0, 64], dtype=np.int32)
+    got = bench.pool_block_list(p, table, lens, 10)
+    one = [5, 1, 9, 7, 8, 0, 3]
+    want = [s * 10 + b for s in range(4) for b in one]
+    assert got.dtype == np.int32 and got.tolist() == want

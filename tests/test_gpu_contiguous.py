@@ -162,6 +162,34 @@ def test_probe_stream_stays_in_bounds():
         kvc.probe_stream(src, 1024, src, 0, waves_per_cu=33)
 
 
+def test_probe_blocks_stays_in_bounds():
+    """The block gather / scatter yardstick touches only the listed blocks
+    (entries outside the region are skipped) and the first stream_bytes of
+    its stream, in both directions."""
+    bb, nblk = 4096, 12
+    region_whole, region = gpu_util.guarded(bb * nblk, DEV)
+    seq_whole, seq = gpu_util.guarded(64 * 1024 + 4096, DEV)
+    blocks = torch.tensor([3, 0, 11, -1, 7, 12, 3, 100000], dtype=torch.int32, device=DEV)
+    listed = {0, 3, 7, 11}
+    for scatter in (0, 1):
+        region.fill_(0x5A)
+        seq.fill_(0x5A)
+        kvc.probe_blocks(region, bb, blocks, seq, 64 * 1024, scatter, waves_per_cu=2)
+        torch.cuda.synchronize()
+        assert gpu_util.canaries_intact(region_whole) and gpu_util.canaries_intact(seq_whole), scatter
+        r = region.view(nblk, bb).cpu()
+        for b in range(nblk):
+            untouched = bool((r[b] == 0x5A).all())
+            assert untouched == (not scatter or b not in listed), (scatter, b)
+        assert bool((seq[64 * 1024:] == 0x5A).all())
+        if not scatter:
+            assert not bool((seq[:64 * 1024] == 0x5A).all())
+    with pytest.raises(kvc.KvcError, match="KVC_EALIGN"):
+        kvc.probe_blocks(region, 1000, blocks, seq, 1024, 0)
+    with pytest.raises(kvc.KvcError, match="KVC_EINVAL"):
+        kvc.probe_blocks(region, bb, blocks, seq, 1024, 2)
+
+
 def test_probe_copy():
     a = torch.randint(0, 255, (1 << 24,), dtype=torch.uint8, device=DEV)
     b = torch.zeros_like(a)
