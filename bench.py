@@ -735,7 +735,9 @@ def main():
     # the warm-up steps, then the timed steps; the copy probe runs after them
     # (a 2 GiB copy right before the timed steps slowed the next ones by up
     # to 10%)
-    clocks = ClockSample([a.prewarm_s * f for f in (0.25, 0.5, 0.75)])
+    # the pre-warm, then (2 s on) the transform comparison keep the GPU busy;
+    # the driver refreshes its metrics table only every few hundred ms
+    clocks = ClockSample([a.prewarm_s * f for f in (0.25, 0.5, 0.75)] + [a.prewarm_s + 1.0])
     t0 = time.perf_counter()
     prewarm_steps = leg.prewarm(a.prewarm_s)
     prewarm = {"seconds": time.perf_counter() - t0, "steps": prewarm_steps}
