@@ -1,7 +1,11 @@
 /*
- * kvc_launch.hip -- GPU entry points of the C ABI (include/kvc.h): pick the
- * kernel instance for a validated plan and launch it on the caller's stream
- * with a persistent grid (one or all resident waves per SIMD, per kernel).
+ * kvc_launch.hip -- entry points of the fused path in the C ABI
+ * (include/kvc.h: kvc_encode, kvc_decode, their paged and *_with forms,
+ * kvc_debug_rotate): pick the kernel instance for a validated plan and
+ * launch it on the caller's stream with a persistent grid (one or all
+ * resident waves per SIMD, per kernel).  The measurement probes are in
+ * kvc_probe.hip, the separate-kernel comparator in kvc_unfused.hip, the
+ * chunked send / receive in kvc_pipeline.hip.
  */
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
