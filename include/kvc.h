@@ -47,8 +47,10 @@
  *
  * Conventions for every call:
  *   - the caller allocates and owns all buffers; the library allocates no
- *     memory and keeps no state beyond a per-device occupancy cache (and
- *     the stream-ordering event of the chunked calls below);
+ *     device memory in any call and keeps no state beyond a per-device
+ *     occupancy cache, the stream-ordering event of the chunked calls
+ *     below, and the static workspace array of kvc_encode_unfused_noalloc
+ *     (part of the loaded code object, one per device);
  *   - device pointers must be 16-byte aligned and must not overlap;
  *   - GPU work is enqueued on `stream` (a hipStream_t passed as void*,
  *     NULL = the default stream) and the call returns without waiting;
