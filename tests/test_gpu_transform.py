@@ -189,3 +189,25 @@ def test_paged_calls_with_options():
     ev.close()
     with pytest.raises(kvc.KvcError, match="KVC_EINVAL"):
         kvc.encode_paged(pool, *args, total, p.bits_k, p.bits_v, p.group, seed=p.seed, transform="butterfly")
+
+
+def test_paged_events_span_every_launch():
+    """130 requests in request order take three launches per code width; the
+    events cover all of them, and a call whose requests are all empty still
+    records both."""
+    p = presets.preset("qwen7b_paged").with_(name="paged-opts-many", layers=1, num_requests=130, len_min=0,
+                                             len_max=40, seed=6)
+    lens = inputs.request_lengths(p)
+    table, nb = inputs.block_table(p, lens)
+    offs, total = kvc.paged_layout(lens, p.layers, p.kv_heads, p.head_dim, p.bits_k, p.bits_v, p.group, p.dtype)
+    pool = inputs.make_pool(p, nb, device=DEV)
+    bt, sl, of = (torch.from_numpy(a).to(DEV) for a in (table, lens, offs))
+    ref = kvc.encode_paged(pool, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    ev = _events(4)
+    got = kvc.encode_paged(pool, bt, sl, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, events=ev.pair(0, 1))
+    zero = torch.zeros_like(sl)
+    kvc.encode_paged(pool, bt, zero, of, total, p.bits_k, p.bits_v, p.group, seed=p.seed, events=ev.pair(2, 3))
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert ev.ms(0, 1) > 0 and ev.ms(2, 3) >= 0
+    ev.close()
