@@ -301,6 +301,10 @@ struct Cursor {
   int64_t off;           // byte offset of request r's blob
   // paged: wave-uniform
   int64_t per_slab, total, di, db;
+  // log2 of row_k, row_v and groups * 4: every supported (head_dim, bits,
+  // group) makes them powers of two, so the per-item sizes and offsets are
+  // shifts rather than 64-bit products
+  int32_t sh_k, sh_v, sh_m;
   PagedPos cur, ahead;
 };
 
@@ -322,6 +326,17 @@ __device__ __forceinline__ ReqSizes req_sizes(const LaunchArgs& a, int64_t len) 
   z.ck = align256(rows * uint64_t(a.row_k));
   z.cv = align256(rows * uint64_t(a.row_v));
   z.mslab = align256(rows * uint64_t(a.groups) * 4u);
+  z.total = uint64_t(a.layers) * (z.ck + z.cv) + uint64_t(a.layers) * 2u * z.mslab;
+  return z;
+}
+
+/* req_sizes with the shifts of the cursor (one 32 x 32-bit product). */
+__device__ __forceinline__ ReqSizes req_sizes_sh(const LaunchArgs& a, const Cursor& c, int32_t len) {
+  ReqSizes z;
+  const uint64_t rows = uint64_t(uint32_t(len)) * uint64_t(uint32_t(a.heads));
+  z.ck = align256(rows << c.sh_k);
+  z.cv = align256(rows << c.sh_v);
+  z.mslab = align256(rows << c.sh_m);
   z.total = uint64_t(a.layers) * (z.ck + z.cv) + uint64_t(a.layers) * 2u * z.mslab;
   return z;
 }
@@ -380,6 +395,9 @@ __device__ __forceinline__ void paged_step(const LaunchArgs& a, const Cursor& c,
  * first two items. */
 __device__ __forceinline__ void paged_init(const LaunchArgs& a, Cursor& c) {
   const int lane = threadIdx.x;
+  c.sh_k = __builtin_ctz(uint32_t(a.row_k));
+  c.sh_v = __builtin_ctz(uint32_t(a.row_v));
+  c.sh_m = __builtin_ctz(uint32_t(a.groups) * 4u);
   if (a.order) {  // pool order: the list numbers the items; nothing per lane
     c.per_slab = a.order_len * a.subtiles;
     c.total = c.per_slab * a.n_slabs;
@@ -492,7 +510,7 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
   const PagedPos& p = c.cur;
   const int32_t len = p.len;
   const int64_t off = p.off;
-  const ReqSizes z = req_sizes(a, len);
+  const ReqSizes z = req_sizes_sh(a, c, len);  // meaningful once len >= 0 is checked below
   if (a.order) {  // a listed item carries its own length and offset: check them here
     const bool ok = len >= 0 && int64_t(len) <= int64_t(a.max_blocks) * a.block_size && p.j >= 0 &&
                     int64_t(p.j) * a.block_size < int64_t(len) && off >= 0 && !(off & 15) &&
@@ -515,7 +533,7 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
   const uint64_t meta_start = uint64_t(a.layers) * (z.ck + z.cv);
   const int64_t s = p.i * a.slab_step + a.slab_first;
   const int64_t l = s >> 1, kv = s & 1;
-  const int64_t row = kv ? a.row_v : a.row_k;
+  const int sh = kv ? c.sh_v : c.sh_k;  // log2 of the slab's code row bytes
   const int64_t row0 = int64_t(first_tok) * a.heads + v0;  // t*H + h of the tile's first vector
   const int64_t tile0 = row0 / kTileVectors * kTileVectors;  // first row of its code tile
   t.count = min(kTileVectors, nvec - v0);
@@ -524,11 +542,11 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
   t.src = tensor + ((s * a.num_blocks + p.blk) * int64_t(a.block_size) * a.heads + v0) * vec_bytes;
   uint8_t* cs = blob + off + l * (z.ck + z.cv) + (kv ? z.ck : 0);
   uint8_t* ms = blob + off + meta_start + s * z.mslab;
-  t.codes = cs + tile0 * row;
-  t.meta = ms + row0 * a.groups * 4;
+  t.codes = cs + (tile0 << sh);
+  t.meta = ms + (row0 << c.sh_m);
   if (PAD && row0 + t.count == rows) {  // the slab's last tile also zeroes its padding
-    zero_tail(cs + rows * row, (kv ? z.cv : z.ck) - rows * row);
-    zero_tail(ms + rows * a.groups * 4, z.mslab - rows * a.groups * 4);
+    zero_tail(cs + (rows << sh), (kv ? z.cv : z.ck) - (uint64_t(rows) << sh));
+    zero_tail(ms + (rows << c.sh_m), z.mslab - (uint64_t(rows) << c.sh_m));
   }
   return true;
 }

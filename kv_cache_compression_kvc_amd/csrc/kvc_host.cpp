@@ -235,6 +235,14 @@ int plan_paged(Op op, const kvc_desc* d, const void* src, void* dst,
   if (pg->block_size < 1 || pg->block_size > 1024) return KVC_ERANGE;
   if (pg->num_reqs < 0 || pg->max_blocks < 0 || pg->num_blocks < 0 || pg->reserved != 0)
     return KVC_ERANGE;
+  // the paged kernels size a request's slabs by shifts: code rows and meta
+  // rows must be powers of two (every supported head_dim / bits / group is)
+  {
+    const uint32_t widths[3] = {uint32_t(d->head_dim * d->bits_k / 8), uint32_t(d->head_dim * d->bits_v / 8),
+                                uint32_t(d->head_dim / d->group * 4)};
+    for (uint32_t w : widths)
+      if (w == 0 || (w & (w - 1))) return KVC_ESHAPE;
+  }
   // token positions (j * block_size, lengths) are 32-bit in the kernels
   if (static_cast<int64_t>(pg->max_blocks) * pg->block_size > INT32_MAX) return KVC_ERANGE;
   uint64_t vecs_per_block;
