@@ -14,8 +14,8 @@ plain definition of the method (``oracle/``):
       computed in float64 from the oracle's y -- except where that t lies
       within a band of a rounding boundary k + 1/2, where either neighbour is
       accepted; such flips are counted and the largest boundary distance
-      among them is reported.  The band is the benchmark spec's 1e-5 for 2- and
-      4-bit codes.  For 8-bit codes (no workload uses them) it is 2^-13:
+      among them is reported.  The band is the stated 1e-5 for 2- and 4-bit
+      codes.  For 8-bit codes (no workload uses them) it is 2^-13:
       t reaches 255 < 2^8, and a binary32 decision carries a relative error of
       a few 2^-24 per step over about eight steps (the transform's sums and
       the affine map), so 2^8 * 8 * 2^-24 = 2^-13; flips beyond 1e-5 are

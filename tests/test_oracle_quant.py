@@ -20,7 +20,7 @@ def _rotated(rng, n, D, spread=1.0, offset=0.0):
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 def test_error_bound_and_code_range(bits, G):
-    """Spec invariant, exact in float64: 0 <= t <= 2^b - 1 and
+    """The quantizer's invariant, exact in float64: 0 <= t <= 2^b - 1 and
     |y - yhat| <= scale / 2 for every element, zero <= min y and
     zero + (2^b - 1) scale >= max y for every group."""
     rng = np.random.default_rng(bits * 1000 + G)
