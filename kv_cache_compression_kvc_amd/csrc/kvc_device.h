@@ -265,7 +265,17 @@ __device__ __forceinline__ T ld_const(const T* p) {
  * Contiguous items walk the launch's slabs tile by tile (kvc_cursor.h: slab
  * offsets carried along, no products per step).
  *
- * Paged items: a launch covers requests [req_first, req_first + nreq), at
+ * Paged items are taken in units: unit (c, b) is item b of the launch's
+ * slabs [c * R, min(n_slabs, c * R + R)), units numbered c * per_slab + b.
+ * A wave resolves, checks and addresses a unit's first tile, then walks the
+ * unit's other slabs by adding strides to that tile's addresses (the pool's
+ * slab stride, and the request's code and meta slab sizes), so the per-item
+ * work below is paid once per R tiles.  The decode walks R = a.run slabs
+ * (WALK); the encode takes R = 1, with no walk state: its kernel is short
+ * of scalar registers, and the walk's state cost it more than the walk
+ * saved.
+ *
+ * Request order: a launch covers requests [req_first, req_first + nreq), at
  * most one per lane.  At its start every wave loads the lengths and blob
  * offsets of those requests into its lanes (lane r: request req_first + r),
  * checks them, and numbers the items of a slab request by request with a
@@ -273,20 +283,20 @@ __device__ __forceinline__ T ld_const(const T* p) {
  * subtiles items, so there are no empty items.  An item's request is then
  * the number of lanes whose running total is at or below it (one ballot),
  * and its length and offset come from that lane (readlane).  The cursor runs
- * one item ahead of the tile it hands out: the block-table entry of the
- * next item is loaded while the current one is worked on.
+ * one unit ahead of the tiles it hands out: the block-table entry of the
+ * next unit is loaded while the current one is worked on.
  *
  * Pool order: when the call brings a list of its (request, block) items
  * sorted by pool block (kvc_paged_item), item b of a slab is entry
  * b / subtiles of the list, and the entry carries the pool block, the
  * request's length and its blob offset; the waves then sweep the pool in
  * address order (neighbouring blocks at the same time) instead of in the
- * table's random order.  The entry of the next item is loaded ahead, and
- * its length and offset are checked per item.
+ * table's random order.  The entry of the next unit is loaded ahead, and
+ * its length and offset are checked per unit.
  */
 struct PagedPos {
-  int64_t item;          // item of the launch (slab i, item b of the slab)
-  int64_t i, b;
+  int64_t unit;          // unit of the launch
+  int64_t i, b;          // its first slab i (of the launch) and item b of the slab
   int32_t r, j, sub;     // request, block of the request, subtile of the block
   int32_t blk;           // pool block of (r, j), loaded ahead
   int32_t len;           // tokens of request r
@@ -306,6 +316,10 @@ struct Cursor {
   // shifts rather than 64-bit products
   int32_t sh_k, sh_v, sh_m;
   PagedPos cur, ahead;
+  // paged, WALK: the current unit's slabs after the latest tile handed
+  // out, and the blob bytes from one of its slabs to the next
+  int32_t left;
+  int64_t dcodes, dmeta;
 };
 
 __device__ __forceinline__ int32_t lane_value(int32_t v, int32_t lane) { return __builtin_amdgcn_readlane(v, lane); }
@@ -378,13 +392,36 @@ __device__ __forceinline__ void paged_resolve(const LaunchArgs& a, const Cursor&
   p.off = lane_value64(c.off, p.r);
 }
 
+/* Slabs per unit. */
+template <bool WALK>
+__device__ __forceinline__ int32_t unit_slabs(const LaunchArgs& a) {
+  return WALK ? a.run : 1;
+}
+
+template <bool WALK>
 __device__ __forceinline__ void paged_step(const LaunchArgs& a, const Cursor& c, PagedPos& p) {
-  p.item += gridDim.x;
+  p.unit += gridDim.x;
   p.i += c.di;
   p.b += c.db;
   if (p.b >= c.per_slab) {
     p.b -= c.per_slab;
-    p.i += 1;
+    p.i += unit_slabs<WALK>(a);
+  }
+}
+
+/* Units per item of a slab: the launch's slabs in runs of unit_slabs. */
+template <bool WALK>
+__device__ __forceinline__ int64_t unit_rows(const LaunchArgs& a) {
+  return WALK ? (a.n_slabs + a.run - 1) / a.run : a.n_slabs;
+}
+
+/* The unit steps and the first unit's slab in slabs rather than in runs. */
+template <bool WALK>
+__device__ __forceinline__ void unit_scale(const LaunchArgs& a, Cursor& c) {
+  if constexpr (WALK) {
+    c.di *= a.run;
+    c.cur.i *= a.run;
+    c.left = 0;
   }
 }
 
@@ -392,7 +429,8 @@ __device__ __forceinline__ void paged_step(const LaunchArgs& a, const Cursor& c,
  * outside [0, max_blocks * block_size] or a blob offset that is negative,
  * not a multiple of 16 or whose blob would end past the buffer: the request
  * is skipped and bit 0 of *err set), the item numbering, and the wave's
- * first two items. */
+ * first two units. */
+template <bool WALK>
 __device__ __forceinline__ void paged_init(const LaunchArgs& a, Cursor& c) {
   const int lane = threadIdx.x;
   c.sh_k = __builtin_ctz(uint32_t(a.row_k));
@@ -400,21 +438,22 @@ __device__ __forceinline__ void paged_init(const LaunchArgs& a, Cursor& c) {
   c.sh_m = __builtin_ctz(uint32_t(a.groups) * 4u);
   if (a.order) {  // pool order: the list numbers the items; nothing per lane
     c.per_slab = a.order_len * a.subtiles;
-    c.total = c.per_slab * a.n_slabs;
-    c.cur.item = blockIdx.x;
-    if (c.per_slab == 0 || c.cur.item >= c.total) {
+    c.total = c.per_slab * unit_rows<WALK>(a);
+    c.cur.unit = blockIdx.x;
+    if (c.per_slab == 0 || c.cur.unit >= c.total) {
       c.total = 0;
       return;
     }
     const int64_t step = gridDim.x;
     c.di = step / c.per_slab;
     c.db = step - c.di * c.per_slab;
-    c.cur.i = c.cur.item / c.per_slab;
-    c.cur.b = c.cur.item - c.cur.i * c.per_slab;
+    c.cur.i = c.cur.unit / c.per_slab;
+    c.cur.b = c.cur.unit - c.cur.i * c.per_slab;
+    unit_scale<WALK>(a, c);
     paged_resolve(a, c, c.cur);
     c.ahead = c.cur;
-    paged_step(a, c, c.ahead);
-    if (c.ahead.item < c.total) paged_resolve(a, c, c.ahead);
+    paged_step<WALK>(a, c, c.ahead);
+    if (c.ahead.unit < c.total) paged_resolve(a, c, c.ahead);
     return;
   }
   int32_t len = 0;
@@ -446,51 +485,55 @@ __device__ __forceinline__ void paged_init(const LaunchArgs& a, Cursor& c) {
   c.incl = lane < a.nreq ? incl : INT32_MAX;
   c.len = len;
   c.off = off;
-  c.total = c.per_slab * a.n_slabs;
-  c.cur.item = blockIdx.x;
-  if (c.per_slab == 0 || c.cur.item >= c.total) {
+  c.total = c.per_slab * unit_rows<WALK>(a);
+  c.cur.unit = blockIdx.x;
+  if (c.per_slab == 0 || c.cur.unit >= c.total) {
     c.total = 0;
     return;
   }
   const int64_t step = gridDim.x;
   c.di = step / c.per_slab;
   c.db = step - c.di * c.per_slab;
-  c.cur.i = c.cur.item / c.per_slab;
-  c.cur.b = c.cur.item - c.cur.i * c.per_slab;
+  c.cur.i = c.cur.unit / c.per_slab;
+  c.cur.b = c.cur.unit - c.cur.i * c.per_slab;
+  unit_scale<WALK>(a, c);
   paged_resolve(a, c, c.cur);
   c.ahead = c.cur;
-  paged_step(a, c, c.ahead);
-  if (c.ahead.item < c.total) paged_resolve(a, c, c.ahead);
+  paged_step<WALK>(a, c, c.ahead);
+  if (c.ahead.unit < c.total) paged_resolve(a, c, c.ahead);
 }
 
-/* The ahead item becomes the current one; the next one is resolved and its
+/* The ahead unit becomes the current one; the next one is resolved and its
  * table entry requested. */
+template <bool WALK>
 __device__ __forceinline__ void paged_advance(const LaunchArgs& a, Cursor& c) {
   c.cur = c.ahead;
-  paged_step(a, c, c.ahead);
-  if (c.ahead.item < c.total) paged_resolve(a, c, c.ahead);
+  paged_step<WALK>(a, c, c.ahead);
+  if (c.ahead.unit < c.total) paged_resolve(a, c, c.ahead);
 }
 
-template <bool PAGED>
+template <bool PAGED, bool WALK>
 __device__ __forceinline__ void cursor_init(const LaunchArgs& a, Cursor& c) {
   if constexpr (!PAGED) {
     contig_init(a, int64_t(blockIdx.x), int64_t(gridDim.x), c.k);
   } else {
-    paged_init(a, c);
+    paged_init<WALK>(a, c);
   }
 }
 
 /*
- * The tile of the cursor's item.  Paged items whose subtile lies past the
- * request's last token (the last block's tail) are skipped (false), as are
- * items whose table entry lies outside the pool (bit 0 of *err is then
- * set).  `tensor` is the KV side (source of an encode, destination of a
- * decode), `blob` the encoded side.  With PAD, the last tile of each slab
- * also zeroes the padding that follows the slab's codes and its meta (each
- * is padded to a multiple of 256 bytes), right when it is found.
+ * The tile of the cursor's item (paged: the first tile of the cursor's
+ * unit, which also sets up the walk over the unit's other slabs).  Paged
+ * units whose subtile lies past the request's last token (the last block's
+ * tail) are skipped (false), as are units whose table entry lies outside
+ * the pool (bit 0 of *err is then set).  `tensor` is the KV side (source of
+ * an encode, destination of a decode), `blob` the encoded side.  With PAD,
+ * the last tile of each slab also zeroes the padding that follows the
+ * slab's codes and its meta (each is padded to a multiple of 256 bytes),
+ * right when it is found.
  */
-template <int D, bool PAD, bool PAGED>
-__device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c, const uint8_t* tensor,
+template <int D, bool PAD, bool PAGED, bool WALK>
+__device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, Cursor& c, const uint8_t* tensor,
                                             uint8_t* blob, Tile& t) {
   constexpr int64_t vec_bytes = int64_t(D) * 2;
   if constexpr (!PAGED) {
@@ -548,25 +591,53 @@ __device__ __forceinline__ bool cursor_tile(const LaunchArgs& a, const Cursor& c
     zero_tail(cs + (rows << sh), (kv ? z.cv : z.ck) - (uint64_t(rows) << sh));
     zero_tail(ms + (rows << c.sh_m), z.mslab - (uint64_t(rows) << c.sh_m));
   }
+  if constexpr (WALK) {
+    // the unit's next slab is slab_step slabs on; with slab_step 1 that is
+    // the V slab after a K slab or the next layer's K slab after a V slab,
+    // and the launch then holds K and V of equal code widths (ck == cv)
+    c.left = static_cast<int32_t>(min<int64_t>(a.run, a.n_slabs - c.cur.i)) - 1;
+    c.dcodes = static_cast<int64_t>(a.slab_step == 1 ? z.ck : z.ck + z.cv);
+    c.dmeta = a.slab_step * static_cast<int64_t>(z.mslab);
+  }
   return true;
 }
 
-/* Advance to the next item of this wave that maps to a tile. */
-template <int D, bool PAD, bool PAGED>
+/* The paged cursor's unit on its next slab: tile `prev` (the unit's latest
+ * one) slab_step slabs on (the caller checked c.left > 0). */
+__device__ __forceinline__ void walk_next(const LaunchArgs& a, Cursor& c, const Tile& prev, Tile& t) {
+  --c.left;
+  t = prev;
+  t.src += a.src_stride;
+  t.codes += c.dcodes;
+  t.meta += c.dmeta;
+}
+
+/* Advance to the next item of this wave that maps to a tile (paged: the
+ * current unit's next slab, else the next unit that maps to one).  `prev`
+ * is the tile the previous call handed out (ignored when `first`).  WALK
+ * units hold no padding: the decode walks them, the encode (PAD) does not. */
+template <int D, bool PAD, bool PAGED, bool WALK>
 __device__ __forceinline__ bool next_tile(const LaunchArgs& a, Cursor& c, const uint8_t* tensor, uint8_t* blob,
-                                          Tile& t, bool first) {
+                                          const Tile& prev, Tile& t, bool first) {
+  static_assert(!(PAD && WALK), "a walked unit does not zero padding");
   if constexpr (!PAGED) {
     if (!first) contig_next(a, int64_t(gridDim.x), c.k);
     while (c.k.item < a.total_items) {
-      if (cursor_tile<D, PAD, PAGED>(a, c, tensor, blob, t)) return true;
+      if (cursor_tile<D, PAD, PAGED, WALK>(a, c, tensor, blob, t)) return true;
       contig_next(a, int64_t(gridDim.x), c.k);
     }
     return false;
   } else {
-    if (!first) paged_advance(a, c);
-    while (c.cur.item < c.total) {
-      if (cursor_tile<D, PAD, PAGED>(a, c, tensor, blob, t)) return true;
-      paged_advance(a, c);
+    if (!first) {
+      if (WALK && c.left > 0) {
+        walk_next(a, c, prev, t);
+        return true;
+      }
+      paged_advance<WALK>(a, c);
+    }
+    while (c.cur.unit < c.total) {
+      if (cursor_tile<D, PAD, PAGED, WALK>(a, c, tensor, blob, t)) return true;
+      paged_advance<WALK>(a, c);
     }
     return false;
   }
@@ -958,9 +1029,9 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
   uint8_t* blob = static_cast<uint8_t*>(a.dst);
   load_signs(a, signs);
   Cursor c;
-  cursor_init<PAGED>(a, c);
+  cursor_init<PAGED, false>(a, c);
   Tile cur;
-  if (!next_tile<D, true, PAGED>(a, c, tensor, blob, cur, true)) return;
+  if (!next_tile<D, true, PAGED, false>(a, c, tensor, blob, cur, cur, true)) return;
   dma_rows<D, !PAGED>(cur.src, cur.count, (lds_v4u*)lds);
   wait_vmem<0>();
   lds_order();
@@ -972,7 +1043,7 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
     KVC_PHASE();
     lds_done();  // every lane's row is in registers: the buffer is free
     Tile nxt;
-    const bool more = next_tile<D, true, PAGED>(a, c, tensor, blob, nxt, false);
+    const bool more = next_tile<D, true, PAGED, false>(a, c, tensor, blob, cur, nxt, false);
     if (more) dma_rows<D, !PAGED>(nxt.src, nxt.count, (lds_v4u*)lds);
     KVC_PHASE();
     float y[D];
@@ -1141,9 +1212,9 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
   HadamardA had;
   if constexpr (!BFLY) hadamard_operands<KVC_FP16>(had);
   Cursor c;
-  cursor_init<PAGED>(a, c);
+  cursor_init<PAGED, true>(a, c);
   Tile cur;
-  if (!next_tile<D, false, PAGED>(a, c, tensor, blob, cur, true)) return;
+  if (!next_tile<D, false, PAGED, true>(a, c, tensor, blob, cur, cur, true)) return;
   CodeRegs<D, B, G> cr;
   load_codes<D, B, G, PAGED>(cur, cr);
   // nothing outstanding on entry, so inside the loop the compiler's own wait
@@ -1171,7 +1242,7 @@ KVC_KERNEL void decode_kernel(const LaunchArgs a) {
     }
     KVC_PHASE();
     Tile nxt;
-    const bool more = next_tile<D, false, PAGED>(a, c, tensor, blob, nxt, false);
+    const bool more = next_tile<D, false, PAGED, true>(a, c, tensor, blob, cur, nxt, false);
     if (more) load_codes<D, B, G, PAGED>(nxt, cr);
     KVC_PHASE();
     if constexpr (BFLY) {
@@ -1256,10 +1327,10 @@ __device__ __forceinline__ void rotate_tiles(const LaunchArgs& a, float* out) {
   HadamardA had;
   hadamard_operands<DT>(had);
   Cursor c;
-  cursor_init<false>(a, c);
+  cursor_init<false, false>(a, c);
   Tile t;
-  for (bool ok = next_tile<D, false, false>(a, c, tensor, nullptr, t, true); ok;
-       ok = next_tile<D, false, false>(a, c, tensor, nullptr, t, false)) {
+  for (bool ok = next_tile<D, false, false, false>(a, c, tensor, nullptr, t, t, true); ok;
+       ok = next_tile<D, false, false, false>(a, c, tensor, nullptr, t, t, false)) {
     lds_done();
     dma_rows<D, false>(t.src, t.count, (lds_v4u*)lds);
     wait_vmem<0>();

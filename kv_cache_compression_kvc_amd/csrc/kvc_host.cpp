@@ -300,9 +300,21 @@ int plan_paged(Op op, const kvc_desc* d, const void* src, void* dst,
   base.err = pg->err_flag;
   base.order = pg->order;
   base.order_len = pg->order_len;
+  // the pool's bytes per slab: num_blocks blocks of block_size * H vectors
+  uint64_t pool_slab, pool_bytes;
+  if (!mul_ok(static_cast<uint64_t>(pg->num_blocks), vecs_per_block, &pool_slab) ||
+      !mul_ok(pool_slab, 2ull * static_cast<uint64_t>(d->head_dim), &pool_slab) ||
+      !mul_ok(pool_slab, 2ull * static_cast<uint64_t>(d->layers), &pool_bytes) || pool_bytes > (1ull << 62))
+    return KVC_ESHAPE;
   split_slabs(op, d, plan, base);
-  for (int i = 0; i < plan->n_launch; ++i)   // per request chunk; run_plan sets req_first / nreq
-    plan->args[i].total_items = static_cast<int64_t>(per_slab) * plan->args[i].n_slabs;
+  for (int i = 0; i < plan->n_launch; ++i) {  // per request chunk; run_plan sets req_first / nreq
+    LaunchArgs& a = plan->args[i];
+    a.src_stride = a.slab_step * static_cast<int64_t>(pool_slab);
+    // the decode kernel walks units of kPagedRun slabs, the encode kernel
+    // units of one slab
+    a.run = op == Op::Decode ? static_cast<int32_t>(a.n_slabs < kPagedRun ? a.n_slabs : kPagedRun) : 1;
+    a.total_items = static_cast<int64_t>(per_slab) * ((a.n_slabs + a.run - 1) / a.run);
+  }
   return KVC_OK;
 }
 

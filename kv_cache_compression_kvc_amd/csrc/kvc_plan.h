@@ -21,6 +21,7 @@ namespace kvc {
 
 constexpr int kTileVectors = 64;   // one vector per lane of a wave64
 constexpr int kReqChunk = 64;      // requests of one paged launch: one per lane of a wave64
+constexpr int kPagedRun = 2;       // slabs a paged decode wave walks per item before it resolves the next
 
 /* Arguments of one encode / decode / rotate launch (passed by value). */
 struct LaunchArgs {
@@ -49,6 +50,8 @@ struct LaunchArgs {
   // slab i of this launch (s = i * slab_step + slab_first) starts at byte
   // src_first + i * src_stride of the tensor, its codes at codes_first +
   // i * codes_stride and its meta at meta_first + i * meta_stride of the blob
+  // (paged: src_stride is the pool's byte stride between the launch's
+  // consecutive slabs, slab_step slabs of num_blocks blocks)
   int64_t src_first, src_stride;
   int64_t codes_first, codes_stride;
   int64_t meta_first, meta_stride;
@@ -62,7 +65,9 @@ struct LaunchArgs {
   // kReqChunk, and the items of a slab are numbered request by request with
   // no gaps (the kernel numbers them from the lengths); in pool order
   // (order != NULL) the items of a slab are the order_len listed entries,
-  // each split into its subtiles
+  // each split into its subtiles.  A decode wave takes an item in `run`
+  // consecutive slabs of the launch at a time (a unit of work; 1 for the
+  // encode)
   int64_t num_blocks;
   int32_t block_size;
   int32_t heads;
@@ -71,7 +76,7 @@ struct LaunchArgs {
   int32_t subtiles;       // ceil(block_size * H / 64)
   int32_t req_first;
   int32_t nreq;
-  int32_t pad0;
+  int32_t run;            // slabs per unit, 1..n_slabs
   const int32_t* table;
   const int32_t* lens;
   const int64_t* offsets;
@@ -80,7 +85,7 @@ struct LaunchArgs {
   const kvc_paged_item* order;
   int64_t order_len;
 
-  int64_t total_items;    // items of this launch (paged: an upper bound, for the grid size)
+  int64_t total_items;    // items of this launch (paged: units, an upper bound, for the grid size)
   uint32_t sign_words[64];// bit 15 / bit 31 of word m: sign of element 2m / 2m+1
 };
 

@@ -41,22 +41,27 @@ def _gpu(lens, table, offs):
 
 
 CASES = [
-    # (head_dim, dtype, bits_k, bits_v, group, heads, lengths)
-    (128, "bf16", 2, 4, 64, 4, [37, 0, 16, 5, 1, 33, 200]),
-    (128, "bf16", 4, 4, 128, 8, [17, 64, 3]),
-    (64, "fp16", 8, 2, 32, 2, [15, 16, 31, 2]),
-    (128, "fp16", 4, 8, 32, 1, [100, 7]),
+    # (layers, head_dim, dtype, bits_k, bits_v, group, heads, lengths)
+    (2, 128, "bf16", 2, 4, 64, 4, [37, 0, 16, 5, 1, 33, 200]),
+    (2, 128, "bf16", 4, 4, 128, 8, [17, 64, 3]),
+    (2, 64, "fp16", 8, 2, 32, 2, [15, 16, 31, 2]),
+    (2, 128, "fp16", 4, 8, 32, 1, [100, 7]),
     # 48 and 80 rows per block: block tiles start inside a 64-row code tile
     # and run into the next one
-    (128, "bf16", 4, 2, 32, 3, [50, 17, 100, 1]),
-    (64, "fp16", 2, 8, 64, 5, [33, 16, 1, 70]),
+    (2, 128, "bf16", 4, 2, 32, 3, [50, 17, 100, 1]),
+    (2, 64, "fp16", 2, 8, 64, 5, [33, 16, 1, 70]),
+    # a decode wave walks an item through consecutive slabs of its launch
+    # (2 at a time): 5 layers make launches of 5 slabs (K and V apart), whose
+    # last walk is shorter, and of 10 slabs (K and V together)
+    (5, 128, "bf16", 2, 4, 64, 4, [37, 0, 16, 5, 90]),
+    (5, 64, "fp16", 4, 4, 32, 3, [50, 17, 1]),
 ]
 
 
-@pytest.mark.parametrize("D,dtype,bk,bv,G,H,lens", CASES)
-def test_paged_matches_oracle(D, dtype, bk, bv, G, H, lens):
-    p = presets.preset("qwen7b_paged").with_(name="paged-%d-%s-%d%d-%d-%d" % (D, dtype, bk, bv, G, H),
-                                              layers=2, kv_heads=H, head_dim=D, dtype=dtype,
+@pytest.mark.parametrize("L,D,dtype,bk,bv,G,H,lens", CASES)
+def test_paged_matches_oracle(L, D, dtype, bk, bv, G, H, lens):
+    p = presets.preset("qwen7b_paged").with_(name="paged-%d-%d-%s-%d%d-%d-%d" % (L, D, dtype, bk, bv, G, H),
+                                              layers=L, kv_heads=H, head_dim=D, dtype=dtype,
                                               bits_k=bk, bits_v=bv, group=G, seed=5)
     lens, table, pool, offs, total = _setup(p, lens)
     bt, sl, of = _gpu(lens, table, offs)
@@ -112,13 +117,13 @@ def _order(table, lens, offs, p, nb):
     return torch.from_numpy(items.view(np.uint8)).to(DEV)
 
 
-@pytest.mark.parametrize("D,dtype,bk,bv,G,H,lens", CASES)
-def test_paged_pool_order_equals_request_order(D, dtype, bk, bv, G, H, lens):
+@pytest.mark.parametrize("L,D,dtype,bk,bv,G,H,lens", CASES)
+def test_paged_pool_order_equals_request_order(L, D, dtype, bk, bv, G, H, lens):
     """The pool-order traversal (items sorted by pool block) writes the same
     blob and decodes to the same pool, bit for bit, as the request-order
     traversal (which the oracle tests above check)."""
-    p = presets.preset("qwen7b_paged").with_(name="order-%d-%s-%d%d-%d-%d" % (D, dtype, bk, bv, G, H),
-                                              layers=2, kv_heads=H, head_dim=D, dtype=dtype,
+    p = presets.preset("qwen7b_paged").with_(name="order-%d-%d-%s-%d%d-%d-%d" % (L, D, dtype, bk, bv, G, H),
+                                              layers=L, kv_heads=H, head_dim=D, dtype=dtype,
                                               bits_k=bk, bits_v=bv, group=G, seed=5)
     lens, table, pool, offs, total = _setup(p, lens)
     bt, sl, of = _gpu(lens, table, offs)
