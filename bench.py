@@ -13,7 +13,10 @@ Warm-up: after an idle period the GPU needs some hundreds of milliseconds
 of load to reach its steady clocks, so before the W warm-up steps the
 headline workload runs encode + decode back to back for --prewarm-s seconds
 of wall time (reported as "prewarm"), whatever W is; the probes run after
-the timed steps.
+the timed steps.  Python's cyclic garbage collector is off for the run and
+collects at the start of every pre-warm instead: a full collection stalls
+the host for tens of milliseconds, the GPU idles meanwhile, and the steps
+after such a stall ran up to 35% slower while the clocks recovered.
 
 Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
   value          raw bytes per step / ms_per_step, GB/s (1e9); ms_per_step is
@@ -50,6 +53,7 @@ Reported, all on raw input bytes (the bf16 KV tensor) unless stated:
 
 import argparse
 import ctypes
+import gc
 import hashlib
 import json
 import os
@@ -573,8 +577,11 @@ class Leg:
                             out=self.dsts[k], transform=self.transform, events=events)
 
     def prewarm(self, seconds):
-        """Encode + decode back to back for `seconds` of wall time; returns the steps run."""
+        """Encode + decode back to back for `seconds` of wall time; returns the
+        steps run.  Python's garbage is collected first, while the GPU is idle
+        anyway (the collector is off for the rest of the run)."""
         import torch
+        gc.collect()
         n, t0 = 0, time.perf_counter()
         while True:
             for _ in range(8):
@@ -725,6 +732,7 @@ def main():
     import kv_cache_compression_kvc_amd as kvc
     from kv_cache_compression_kvc_amd import presets
 
+    gc.disable()   # collections run at the start of each pre-warm (Leg.prewarm)
     p = presets.preset(a.workload)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
