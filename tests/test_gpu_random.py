@@ -73,7 +73,7 @@ def test_random_paged(seed):
     bs = int(rng.choice([4, 8, 16, 32, 64]))
     R = int(rng.integers(1, 7))
     lens = rng.integers(0, 150, R).astype(np.int32)
-    L = int(rng.integers(1, 3))
+    L = int(rng.integers(1, 5))   # odd slab counts end a decode walk early
     p = presets.preset("qwen7b_paged").with_(name="rand-p%d" % seed, layers=L, kv_heads=H, head_dim=D,
                                               dtype=dtype, bits_k=bk, bits_v=bv, group=G, seed=seed,
                                               block_size=bs)
