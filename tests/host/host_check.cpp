@@ -106,6 +106,28 @@ int main() {
     pg.num_reqs = 130;
     CHECK(kvc::plan_paged(kvc::Op::Encode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_OK);
     CHECK(plan.req_chunks == 3 && plan.n_launch == 2);
+    // the encode takes an item one slab at a time: 64 requests x 4 blocks per
+    // slab, 28 slabs per code width; the pool's slab stride spans K and V
+    // slabs (2 x 8 blocks x 16 tokens x 4 heads x 256 bytes)
+    for (int i = 0; i < 2; ++i) {
+      CHECK(plan.args[i].run == 1 && plan.args[i].total_items == 256 * 28);
+      CHECK(plan.args[i].slab_step == 2 && plan.args[i].src_stride == 2 * 8 * 16 * 4 * 256);
+    }
+    // the decode walks kPagedRun slabs per item
+    CHECK(kvc::plan_paged(kvc::Op::Decode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_OK);
+    for (int i = 0; i < 2; ++i)
+      CHECK(plan.args[i].run == kvc::kPagedRun && plan.args[i].total_items == 256 * (28 / kvc::kPagedRun));
+    // equal code widths: one launch over the 10 slabs of 5 layers, K and V alternating
+    kvc_desc d5 = d;
+    d5.layers = 5;
+    d5.bits_k = d5.bits_v = 4;
+    CHECK(kvc::plan_paged(kvc::Op::Decode, &d5, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_OK);
+    CHECK(plan.n_launch == 1 && plan.args[0].slab_step == 1 && plan.args[0].n_slabs == 10);
+    CHECK(plan.args[0].src_stride == 8 * 16 * 4 * 256);
+    CHECK(plan.args[0].total_items == 256 * ((10 + kvc::kPagedRun - 1) / kvc::kPagedRun));
+    // a pool whose bytes pass 2^62 is refused
+    pg.num_blocks = int64_t(1) << 50;
+    CHECK(kvc::plan_paged(kvc::Op::Decode, &d, pbuf, pbuf, 1 << 20, &pg, &plan) == KVC_ESHAPE);
   }
   // sign mask: 128 bits, the first 64 equal for head_dim 64
   uint64_t m128[2], m64[1];
