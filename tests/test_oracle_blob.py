@@ -130,6 +130,11 @@ def test_paged_equals_contiguous_per_request():
     o2, total = oracle.paged_layout(lens, p.layers, p.kv_heads, p.head_dim, p.bits_k, p.bits_v, p.group)
     assert np.array_equal(offs, o2) and blob.size == total
     assert np.all(offs % 256 == 0)
+    # by hand, 2 layers x 2 heads, D 64, K 2-bit / V 4-bit, G 32, each slab padded to 256 B:
+    # 37 tokens: K codes 74 rows x 16 B = 1184 -> 1280, V 74 x 32 = 2368 -> 2560, meta 74 x 8
+    # = 592 -> 768: 2 (1280 + 2560) + 4 x 768 = 10752; 16 tokens: 2 (512 + 1024) + 4 x 256 =
+    # 4096; 5 tokens: 2 (256 + 512) + 4 x 256 = 2560; offsets are the running sums
+    assert offs.tolist() == [0, 10752, 10752, 14848] and total == 17408
     for r, n in enumerate(lens):
         x = oracle.gather_request(pool, table[r], int(n))
         b, _ = oracle.encode(x, p.dtype, p.bits_k, p.bits_v, p.group, p.seed)

@@ -40,6 +40,7 @@ BATTERY = [
     (T_blob.test_decode_inverts_encode_up_to_quantization, ("bf16",)),
     (T_round.test_rne_bf16_matches_torch_float32_conversion, ()),
     (T_blob.test_tiny_preset_matches_scalar_twin, ()),
+    (T_blob.test_paged_equals_contiguous_per_request, ()),
     (T_round.test_directed_rounding_matches_exhaustive_search, ()),
 ]
 
@@ -63,6 +64,7 @@ def _everywhere(mp, name, fn):
 
 
 _hadamard, _rotate_raw, _dequantize = o_rht.hadamard, o_rht.rotate_raw, o_quant.dequantize
+_blob_layout = o_blob.blob_layout
 _splitmix = o_signs.splitmix64_outputs
 
 
@@ -163,8 +165,29 @@ def m_strided_groups(mp):  # groups taken with a stride instead of as consecutiv
     mp.setattr(o_quant, "_groups", groups)
 
 
+def m_block_slot(mp):      # the slots of a block read in reverse order
+    def gather(pool, table_row, seq_len):
+        L, two, NB, BS, H, D = pool.shape
+        out = np.zeros((L, 2, seq_len, H, D), dtype=pool.dtype)
+        for t in range(seq_len):
+            out[:, :, t] = pool[:, :, int(table_row[t // BS]), BS - 1 - t % BS]
+        return out
+    _everywhere(mp, "gather_request", gather)
+
+
+def m_inclusive_offsets(mp):  # each request's offset taken after its own blob instead of before
+    def layout(seq_lens, layers, kv_heads, head_dim, bits_k, bits_v, group):
+        offsets, total = [], 0
+        for n in seq_lens:
+            total += _blob_layout(layers, int(n), kv_heads, head_dim, bits_k, bits_v, group).total
+            offsets.append(total)
+        return np.array(offsets, dtype=np.int64), total + (offsets[-1] if offsets else 0)
+    _everywhere(mp, "paged_layout", layout)
+
+
 MUTATIONS = [m_gamma, m_sign_bit, m_hadamard_rows, m_no_norm, m_inverse_sign, m_sign_after, m_zero_nearest,
-             m_scale_levels, m_strided_groups, m_ties_up, m_msb_first, m_no_zero, m_untiled, m_bf16_truncate]
+             m_scale_levels, m_strided_groups, m_ties_up, m_msb_first, m_no_zero, m_untiled, m_bf16_truncate,
+             m_block_slot, m_inclusive_offsets]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=[m.__name__ for m in MUTATIONS])
