@@ -431,26 +431,31 @@ def pipeline_leg(kvc, p, x, xout, stream, raw_bytes, reps=3, chunk_layers=8):
 
 
 def mix_probe(kvc, src, read_bytes, dst, write_bytes, stream, reps=5):
-    """Best GB/s (read + write) of the library's streaming probe moving the
-    same bytes in the same read:write ratio, over 4, 8 and 16 waves per CU:
-    the achievable-bandwidth yardstick for a kernel with that traffic mix.
-    It overwrites dst."""
+    """Best GB/s (read + write) of the library's streaming probes moving the
+    same bytes in the same read:write ratio: 4 KiB runs of the larger stream
+    at 4, 8 and 16 waves per CU (kvc_probe_stream), and runs of 16 KiB
+    issued at once (an encode tile's loads in flight) at 2, 4 and 8 waves per
+    CU (kvc_probe_stream_runs).  The achievable-bandwidth yardstick for a
+    kernel with that traffic mix.  It overwrites dst."""
     import torch
     rb, wb = read_bytes // 1024 * 1024, write_bytes // 1024 * 1024
+    trials = [("4KiB runs", wpc, lambda w: kvc.probe_stream(src, rb, dst, wb, waves_per_cu=w)) for wpc in (4, 8, 16)]
+    trials += [("16KiB runs at once", wpc, lambda w: kvc.probe_stream_runs(src, rb, dst, wb, run_kib=16,
+                                                                            waves_per_cu=w)) for wpc in (2, 4, 8)]
     best = None
-    for wpc in (4, 8, 16):
+    for pattern, wpc, run in trials:
         for _ in range(2):
-            kvc.probe_stream(src, rb, dst, wb, waves_per_cu=wpc)
+            run(wpc)
         ev = TimingEvents(2)
         ev.record(0, stream)
         for _ in range(reps):
-            kvc.probe_stream(src, rb, dst, wb, waves_per_cu=wpc)
+            run(wpc)
         ev.record(1, stream)
         torch.cuda.synchronize()
         gbps = (rb + wb) * reps / (ev.ms(0, 1) / 1e3) / 1e9
         ev.close()
         if best is None or gbps > best["GBps"]:
-            best = {"GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS, "waves_per_cu": wpc}
+            best = {"GBps": gbps, "frac_hbm_peak": gbps / HBM_PEAK_GBPS, "waves_per_cu": wpc, "pattern": pattern}
     best.update(read_bytes=rb, write_bytes=wb)
     return best
 
@@ -500,8 +505,8 @@ def leg_probes(kvc, leg, stream, enc, dec):
     enc["frac_same_mix_probe"] = enc["hbm_GBps"] / pe["GBps"]
     dec["frac_same_mix_probe"] = dec["hbm_GBps"] / pd["GBps"]
     out = {"encode_mix": pe, "decode_mix": pd,
-           "what": "library streaming probe reading and writing the kernel's bytes in its ratio, "
-                   "best of 4/8/16 waves per CU"}
+           "what": "library streaming probes reading and writing the kernel's bytes in its ratio, best of "
+                   "4 KiB runs at 4/8/16 waves per CU and 16 KiB runs issued at once at 2/4/8"}
     if leg.p.paged:   # the same blocks in the table's order: reads scattered (encode), writes scattered (decode)
         region = leg.src[0].view(-1).view(__import__("torch").uint8)
         out["encode_blocks"] = blocks_probe(kvc, region, leg.block_bytes, leg.blocks, leg.outs[0], leg.enc_bytes,

@@ -95,8 +95,9 @@ extern "C" {
 
 /* 2: every code and meta slab of the blob padded to a multiple of 256 bytes.
  * 3: kvc_paged carries an optional pool-order item list (kvc_paged_order).
- * 4: the *_with calls, whose kvc_launch_opts carries the transform and kernel timing events. */
-#define KVC_ABI_VERSION 4
+ * 4: the *_with calls, whose kvc_launch_opts carries the transform and kernel timing events.
+ * 5: kvc_probe_stream_runs. */
+#define KVC_ABI_VERSION 5
 
 typedef enum kvc_status {
   KVC_OK = 0,
@@ -478,6 +479,20 @@ kvc_status kvc_probe_copy(const void* src, void* dst, uint64_t bytes, void* stre
  */
 kvc_status kvc_probe_stream(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes,
                             int32_t waves_per_cu, void* stream);
+
+/*
+ * Measurement helper: the mix of kvc_probe_stream with each run of the
+ * larger stream issued at once -- run_kib (4, 8 or 16) consecutive 1 KiB
+ * chunks per run, so a wave has a whole run of loads in flight when reads
+ * lead (16 KiB: one encode tile at head_dim 128) -- grid-strided over the
+ * runs across waves_per_cu (1..32) one-wave workgroups per CU, each run
+ * also moving its share of the smaller stream.  Sizes and pointers as for
+ * kvc_probe_stream; dst receives unspecified bytes.  Errors: KVC_EINVAL
+ * (null pointer with a nonzero size, run_kib or waves_per_cu out of range,
+ * the larger size in KiB times the smaller past 2^62), KVC_EALIGN.
+ */
+kvc_status kvc_probe_stream_runs(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes,
+                                 int32_t run_kib, int32_t waves_per_cu, void* stream);
 
 /*
  * Measurement helper with the access pattern of the paged kernels: a block

@@ -25,7 +25,7 @@ from ._lib import KvcDesc, KvcPaged, KvcError, DTYPE
 
 __all__ = [
     "KvcError", "DTYPE", "abi_version", "encoded_size", "sign_mask", "encode", "decode",
-    "paged_layout", "paged_order", "encode_paged", "decode_paged", "debug_rotate", "probe_copy", "probe_stream", "probe_blocks",
+    "paged_layout", "paged_order", "encode_paged", "decode_paged", "debug_rotate", "probe_copy", "probe_stream", "probe_stream_runs", "probe_blocks",
     "unfused_workspace_size", "encode_unfused", "decode_unfused", "encode_unfused_noalloc",
     "chunked_size", "encode_send", "receive_decode",
 ]
@@ -434,4 +434,16 @@ def probe_stream(src, read_bytes, dst, write_bytes, waves_per_cu=8, stream=None)
         raise ValueError("probe sizes exceed the tensors")
     _lib.check(_lib.lib().kvc_probe_stream(_ptr(src), int(read_bytes), _ptr(dst), int(write_bytes),
                                            int(waves_per_cu), _stream(stream)))
+    return dst
+
+
+def probe_stream_runs(src, read_bytes, dst, write_bytes, run_kib=16, waves_per_cu=4, stream=None):
+    """Streaming yardstick with each run of ``run_kib`` KiB of the larger
+    stream issued at once: read ``read_bytes`` of ``src`` and write
+    ``write_bytes`` of ``dst`` (multiples of 1024, within the tensors)."""
+    _check_cuda(src, dst)
+    if read_bytes > _nbytes(src) or write_bytes > _nbytes(dst):
+        raise ValueError("probe sizes exceed the tensors")
+    _lib.check(_lib.lib().kvc_probe_stream_runs(_ptr(src), int(read_bytes), _ptr(dst), int(write_bytes),
+                                                int(run_kib), int(waves_per_cu), _stream(stream)))
     return dst

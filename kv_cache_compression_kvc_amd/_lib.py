@@ -30,6 +30,7 @@ EXPORTS = [
     "kvc_chunked_size", "kvc_encode_send", "kvc_receive_decode", "kvc_probe_copy",
     "kvc_encode_unfused_noalloc", "kvc_probe_stream", "kvc_paged_order", "kvc_encode_with",
     "kvc_decode_with", "kvc_encode_paged_with", "kvc_decode_paged_with", "kvc_probe_blocks",
+    "kvc_probe_stream_runs",
 ]
 TRANSFORM = {"auto": 0, "matrix": 1, "butterfly": 2}   # kvc_transform
 NOALLOC_WORKSPACE_BYTES = 64 << 20   # KVC_NOALLOC_WORKSPACE_BYTES
@@ -142,6 +143,8 @@ def _declare(lib, names):
                                                 ctypes.c_void_p]),
         "kvc_probe_stream": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
                                               ctypes.c_int32, ctypes.c_void_p]),
+        "kvc_probe_stream_runs": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                                   ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
         "kvc_probe_blocks": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p,
                                               ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_void_p]),

@@ -72,10 +72,12 @@ struct Norm;
 template <>
 struct Norm<64> {
   static constexpr float inv_sqrt = 0.125f;
+  static constexpr double inv_sqrt_d = 0.125;
 };
 template <>
 struct Norm<128> {
   static constexpr float inv_sqrt = 0.088388347648318440550f;  // 1/sqrt(128)
+  static constexpr double inv_sqrt_d = 0.088388347648318440550;
 };
 
 /* ---- element conversions ------------------------------------------------ */
@@ -957,9 +959,155 @@ __device__ __forceinline__ void quantize_group(const float* y, float A, float Bz
   *words = pack_word<B>(tq);
 }
 
-/* Meta, codes and stores of one vector from its unnormalized rotated values u. */
-template <int D, int B, int G, bool PAGED>
-__device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t) {
+/* ---- exact 8-bit decisions near a tie ----------------------------------------
+ *
+ * At 8 bits t reaches 255, where one binary32 ulp is 2^-16, so the binary32
+ * decision above (u from fp32 sums, t = fma(u, A, Bz)) can fall on the wrong
+ * side of k + 1/2 when the exact t lies within a few 1e-5 of it.  Such
+ * elements are found with a bound on the decision's error and decided again
+ * exactly: y_i summed in fp64 from the lane's own signed row (the stored
+ * values are exact in fp64, as is their sum unless their exponents span more
+ * than about 35 binades), t = (y - zero) / scale in fp64, rounded half to
+ * even.  Every other element provably has the code of its exact t.
+ *
+ * Bound of |t32 - t| against the exact t of the same meta (w = 2^-24):
+ *   w (2 D rs S / scale + 4 |zero| / scale + 3 (|t32| + 1)),
+ * S = sum_j |x_j| of the vector.  Each element of u comes out of D - 1 fp32
+ * additions whose partial sums are bounded by S; taking each addition's
+ * relative error below 2w, whatever order or rounding the matrix cores use,
+ * gives |u - u_exact| <= 2 D w S.  A = fl(fl(1 / scale) rs) and Bz =
+ * fl(-zero fl(1 / scale)) carry 2w each, the fused multiply-add w; the rest
+ * are second-order terms, covered with the binary32 evaluation of the bound
+ * itself by a 5% slack. */
+
+/* y_i = (H (s * x))_i / sqrt(D) in fp64 from the signed row xs (chunk p =
+ * elements 8p .. 8p+7, element 2m of a chunk in the low half of word m);
+ * i may differ per lane.  Row i of H has the sign (-1)^popcount(i & j). */
+template <int D, int DT>
+__device__ __forceinline__ double exact_rotated(const v4u (&xs)[D / 8], int i) {
+  uint32_t base = 0;  // bit j: parity of popcount(i & j), j < 32
+  if (i & 1) base ^= 0xAAAAAAAAu;
+  if (i & 2) base ^= 0xCCCCCCCCu;
+  if (i & 4) base ^= 0xF0F0F0F0u;
+  if (i & 8) base ^= 0xFF00FF00u;
+  if (i & 16) base ^= 0xFFFF0000u;
+  double sum = 0.0;
+#pragma unroll
+  for (int p = 0; p < D / 8; ++p) {
+    const uint32_t w = (__builtin_popcount((i >> 5) & (p >> 2)) & 1) ? ~base : base;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int sh = (8 * p + 2 * m) & 31;
+      const uint32_t flip = (((w >> sh) & 1u) << 15) | (((w >> (sh + 1)) & 1u) << 31);
+      float lo, hi;
+      unpack_pair<DT>(xs[p][m] ^ flip, lo, hi);
+      sum += static_cast<double>(lo);
+      sum += static_cast<double>(hi);
+    }
+  }
+  return sum * Norm<D>::inv_sqrt_d;
+}
+
+/* The 8-bit code of y against a meta word, in fp64: round half to even of
+ * (y - zero) / scale, within [0, 255]; 0 for a constant group. */
+__device__ __forceinline__ uint32_t exact_code8(double y, uint32_t meta) {
+  const double sc = f16_value(meta & 0xffffu), ze = f16_value(meta >> 16);
+  if (!(sc > 0.0)) return 0u;
+  const double t = __builtin_rint((y - ze) / sc);
+  return static_cast<uint32_t>(__builtin_fmin(__builtin_fmax(t, 0.0), 255.0));
+}
+
+/* Whether a binary32 t lies within `bound` of a tie k + 1/2 (t - floor(t) is
+ * exact for t >= 0, and the distance is taken on |t| otherwise). */
+__device__ __forceinline__ bool near_tie(float t, float bound) {
+  const float a = fabsf(t);
+  return fabsf((a - floorf(a)) - 0.5f) <= bound;
+}
+
+/* Bound of |t32 - t| for the elements of one group, without its |t32| term:
+ * w (c_u rs S / scale + 4 |zero| / scale + 3) with 5% slack; c_u rs S bounds
+ * the fp32 error of u in units of y (c_u = 2 D with S = sum |x_j|). */
+__device__ __forceinline__ float tie_bound_base(float err_u_y, uint32_t meta) {
+  constexpr float W = 5.9604644775390625e-8f;  // 2^-24
+  const float sc = f16_value(meta & 0xffffu), ze = f16_value(meta >> 16);
+  return 1.05f * W * ((err_u_y + 4.0f * fabsf(ze)) / sc + 3.0f);
+}
+constexpr float kTieBoundT = 1.05f * 3.0f * 5.9604644775390625e-8f;  // per |t32|
+
+/* Re-decide exactly the 8-bit codes of this lane's vector whose binary32 t
+ * lies within the bound of a tie.  u: the unnormalized rotated values; xs:
+ * the signed row they came from; words: the packed codes (code k at byte
+ * k % 4 of word k / 4), patched in place. */
+template <int D, int DT, int G>
+__device__ __forceinline__ void refine_ties8(const float (&u)[D], const v4u (&xs)[D / 8], const uint32_t* meta,
+                                             uint32_t* words) {
+#pragma clang fp contract(off)
+  constexpr int NG = D / G, NW = D / 32;
+  constexpr float RS = Norm<D>::inv_sqrt;
+  float S = 0.0f;
+#pragma unroll
+  for (int p = 0; p < D / 8; ++p) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float lo, hi;
+      unpack_pair<DT>(xs[p][m], lo, hi);
+      S += fabsf(lo);
+      S += fabsf(hi);
+    }
+  }
+  uint32_t flags[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) flags[w] = 0u;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (!(f16_value(meta[g] & 0xffffu) > 0.0f)) continue;  // constant group: every code 0, exactly
+    float A, Bz;
+    code_affine<D>(meta[g], A, Bz);
+    const float base = tie_bound_base(2.0f * D * RS * S, meta[g]);
+#pragma unroll
+    for (int j = g * G; j < (g + 1) * G; ++j) {
+      const float t = fmaf(u[j], A, Bz);
+      if (near_tie(t, base + kTieBoundT * fabsf(t))) flags[j / 32] |= 1u << (j % 32);
+    }
+  }
+  for (;;) {
+    uint32_t any = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= flags[w];
+    if (__builtin_amdgcn_ballot_w64(any != 0u) == 0) break;
+    if (any != 0u) {
+      int wsel = 0;
+      uint32_t fw = 0u;
+#pragma unroll
+      for (int w = NW - 1; w >= 0; --w) {
+        if (flags[w] != 0u) {
+          wsel = w;
+          fw = flags[w];
+        }
+      }
+      const int k = 32 * wsel + __builtin_ctz(fw);
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        if (w == wsel) flags[w] = fw & (fw - 1u);
+      uint32_t mg = meta[0];
+#pragma unroll
+      for (int g = 1; g < NG; ++g)
+        if (k / G == g) mg = meta[g];
+      const uint32_t q = exact_code8(exact_rotated<D, DT>(xs, k), mg);
+      const int wk = k >> 2;
+      const uint32_t sh = 8u * static_cast<uint32_t>(k & 3);
+#pragma unroll
+      for (int w = 0; w < D / 4; ++w)
+        if (w == wk) words[w] = (words[w] & ~(0xffu << sh)) | (q << sh);
+    }
+  }
+}
+
+/* Meta, codes and stores of one vector from its unnormalized rotated values
+ * u; at 8 bits the codes near a tie are decided again exactly from the
+ * signed row xs (unused at 2 and 4 bits). */
+template <int D, int DT, int B, int G, bool PAGED>
+__device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t, const v4u (&xs)[D / 8]) {
   constexpr int NG = D / G;
   constexpr float QMAX = float((1 << B) - 1);
   constexpr int WPG = G * B / 32;  // code words per group
@@ -991,6 +1139,7 @@ __device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t) {
     }
     KVC_PHASE();
   }
+  if constexpr (B == 8) refine_ties8<D, DT, G>(y, xs, meta, words);
   if (static_cast<int>(threadIdx.x) < t.count) {
     constexpr int RB = D * B / 8;
     int stride;
@@ -1046,6 +1195,11 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
     const bool more = next_tile<D, true, PAGED, false>(a, c, tensor, blob, cur, nxt, false);
     if (more) dma_rows<D, !PAGED>(nxt.src, nxt.count, (lds_v4u*)lds);
     KVC_PHASE();
+    v4u xs[D / 8];  // the signed row, kept for the exact 8-bit decisions
+    if constexpr (B == 8) {
+#pragma unroll
+      for (int p = 0; p < D / 8; ++p) xs[p] = xc[p];
+    }
     float y[D];
     if constexpr (XF == kEncodeButterfly) {
 #pragma unroll
@@ -1058,7 +1212,7 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
       hadamard_mfma<D, DT>(xc, had, y);
     }
     KVC_PHASE();
-    encode_vector<D, B, G, PAGED>(y, cur);
+    encode_vector<D, DT, B, G, PAGED>(y, cur, xs);
     if (!more) break;
     // outstanding: the next tile's DMA, then this tile's code and meta
     // stores (RB / 16 + 1 instructions, issued by the lanes < count)

@@ -87,6 +87,58 @@ __global__ __launch_bounds__(64) void stream_kernel(const v4u* __restrict__ src,
   asm volatile("" ::"v"(acc.x), "v"(acc.y), "v"(acc.z), "v"(acc.w));
 }
 
+/* The same mix with every run of the larger stream issued at once: RUN
+ * consecutive 1 KiB chunks per run (RUN loads in flight per wave when reads
+ * lead, like an encode tile arriving), grid-strided over the runs, and the
+ * run covering chunks [RUN u, RUN u + RUN) of the larger stream also moves
+ * chunks [floor(RUN u ns / nl), floor((RUN u + RUN) ns / nl)) of the smaller
+ * one.  The host keeps nl * ns below 2^62. */
+template <int RUN>
+__global__ __launch_bounds__(64) void stream_runs_kernel(const v4u* __restrict__ src, uint64_t nr,
+                                                         v4u* __restrict__ dst, uint64_t nw) {
+  const uint64_t nl = nr > nw ? nr : nw, ns = nr > nw ? nw : nr;
+  const bool reads_lead = nr >= nw;
+  const int lane = threadIdx.x;
+  v4u acc = {0, 0, 0, 0};
+  const uint64_t nu = (nl + RUN - 1) / RUN;
+  for (uint64_t u = blockIdx.x; u < nu; u += gridDim.x) {
+    const uint64_t c0 = u * RUN;
+    const uint64_t lo = c0 * ns / nl;
+    const uint64_t hi = c0 + RUN <= nl ? (c0 + RUN) * ns / nl : ns;
+    if (c0 + RUN <= nl) {
+      if (reads_lead) {
+        v4u v[RUN];
+#pragma unroll
+        for (int k = 0; k < RUN; ++k) v[k] = __builtin_nontemporal_load(src + (c0 + k) * 64 + lane);
+        for (uint64_t c = lo; c < hi; ++c)
+          __builtin_nontemporal_store(v4u{uint32_t(c), uint32_t(lane), 0u, 0u}, dst + c * 64 + lane);
+#pragma unroll
+        for (int k = 0; k < RUN; ++k) acc ^= v[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < RUN; ++k)
+          __builtin_nontemporal_store(v4u{uint32_t(c0 + k), uint32_t(lane), 0u, 0u}, dst + (c0 + k) * 64 + lane);
+        for (uint64_t c = lo; c < hi; ++c) acc ^= __builtin_nontemporal_load(src + c * 64 + lane);
+      }
+    } else {  // the last, partial run
+      for (uint64_t c = c0; c < nl; ++c) {
+        if (reads_lead)
+          acc ^= __builtin_nontemporal_load(src + c * 64 + lane);
+        else
+          __builtin_nontemporal_store(v4u{uint32_t(c), uint32_t(lane), 0u, 0u}, dst + c * 64 + lane);
+      }
+      for (uint64_t c = lo; c < hi; ++c) {
+        if (reads_lead)
+          __builtin_nontemporal_store(v4u{uint32_t(c), uint32_t(lane), 0u, 0u}, dst + c * 64 + lane);
+        else
+          acc ^= __builtin_nontemporal_load(src + c * 64 + lane);
+      }
+    }
+  }
+  // the loaded data is consumed here, so the loads stay
+  asm volatile("" ::"v"(acc.x), "v"(acc.y), "v"(acc.z), "v"(acc.w));
+}
+
 /* Block gather / scatter against a sequential stream (kvc_probe_blocks):
  * unit u moves block blocks[u] of the region (cpb 1-KiB chunks) and chunks
  * [floor(u * ns / n), floor((u + 1) * ns / n)) of the stream.  scatter = 0
@@ -141,6 +193,36 @@ kvc_status kvc_probe_stream(const void* src, uint64_t read_bytes, void* dst, uin
   hipLaunchKernelGGL(kvc::dev::stream_kernel, dim3(static_cast<unsigned>(grid)), dim3(64), 0,
                      static_cast<hipStream_t>(stream), static_cast<const kvc::dev::v4u*>(src), nr,
                      static_cast<kvc::dev::v4u*>(dst), nw);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_EHIP;
+}
+
+kvc_status kvc_probe_stream_runs(const void* src, uint64_t read_bytes, void* dst, uint64_t write_bytes,
+                                 int32_t run_kib, int32_t waves_per_cu, void* stream) {
+  if (read_bytes == 0 && write_bytes == 0) return KVC_OK;
+  if ((read_bytes && !src) || (write_bytes && !dst) || waves_per_cu < 1 || waves_per_cu > 32 ||
+      (run_kib != 4 && run_kib != 8 && run_kib != 16))
+    return KVC_EINVAL;
+  if ((read_bytes & 1023u) || (write_bytes & 1023u) || (reinterpret_cast<uintptr_t>(src) & 15u) ||
+      (reinterpret_cast<uintptr_t>(dst) & 15u))
+    return KVC_EALIGN;
+  const uint64_t nr = read_bytes / 1024, nw = write_bytes / 1024;
+  const uint64_t nl = std::max(nr, nw), ns = std::min(nr, nw);
+  if (ns && nl > (uint64_t(1) << 62) / ns) return KVC_EINVAL;   // (c0 + RUN) * ns stays in range
+  int device = 0, cus = 0;
+  if (hipGetDevice(&device) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+    return KVC_EHIP;
+  const uint64_t runs = (nl + run_kib - 1) / run_kib;
+  const dim3 grid(static_cast<unsigned>(std::min<uint64_t>(uint64_t(cus) * uint64_t(waves_per_cu), runs)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const kvc::dev::v4u* in = static_cast<const kvc::dev::v4u*>(src);
+  kvc::dev::v4u* out = static_cast<kvc::dev::v4u*>(dst);
+  if (run_kib == 4)
+    hipLaunchKernelGGL(kvc::dev::stream_runs_kernel<4>, grid, dim3(64), 0, s, in, nr, out, nw);
+  else if (run_kib == 8)
+    hipLaunchKernelGGL(kvc::dev::stream_runs_kernel<8>, grid, dim3(64), 0, s, in, nr, out, nw);
+  else
+    hipLaunchKernelGGL(kvc::dev::stream_runs_kernel<16>, grid, dim3(64), 0, s, in, nr, out, nw);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_EHIP;
 }
 

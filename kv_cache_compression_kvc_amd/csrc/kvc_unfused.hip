@@ -21,8 +21,9 @@
  *
  * The encode stages make the same binary32 decisions as the fused encode
  * (E1 is its transform code; the meta and code arithmetic are the same
- * functions), so the blob is bit-identical to the fused one; only the memory
- * traffic differs.  The decode stages take the textbook order -- dequantize,
+ * functions), and at 8 bits E3 decides the codes near a tie exactly as the
+ * fused encode does, so the blob is bit-identical to the fused one; only
+ * the memory traffic differs.  The decode stages take the textbook order -- dequantize,
  * then the whole inverse transform -- where the fused decode transforms the
  * integer codes within their groups first and scales afterwards, so the two
  * decoded tensors differ in rounding only (both well inside the decode
@@ -131,8 +132,61 @@ __global__ __launch_bounds__(kThreads) void minmax_kernel(const LaunchArgs a, co
   }
 }
 
+/* E3 at 8 bits: the codes of unit i of slab s (elements e0 .. e0+3 of row
+ * r) whose binary32 t lies within the bound of a tie are decided again
+ * exactly from the row of the input tensor -- the fused encode's rule
+ * (kvc_device.h, refine_ties8), with S = sum |x_j| bounded from the row's
+ * meta instead: S <= D max|y|, and every rotated value of a group lies in
+ * [zero, zero + 255 scale]. */
+template <int D, int DT, int G>
+__device__ __forceinline__ uint32_t refine_unit8(const LaunchArgs& a, int64_t s, int64_t i, float4 w, uint32_t c,
+                                                 const uint32_t* meta) {
+#pragma clang fp contract(off)
+  constexpr int NG = D / G;
+  constexpr float RS = dev::Norm<D>::inv_sqrt;
+  const int64_t r = i / (D / 4);
+  const int e0 = static_cast<int>(i % (D / 4)) * 4;
+  const uint32_t* mrow = meta + r * NG;
+  float M = 0.0f;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const float sc = dev::f16_value(mrow[g] & 0xffffu), ze = dev::f16_value(mrow[g] >> 16);
+    M = fmaxf(M, fmaxf(fabsf(ze), fabsf(ze + 255.0f * sc)));
+  }
+  M *= 1.004f;
+  const uint32_t mg = mrow[e0 / G];
+  if (!(dev::f16_value(mg & 0xffffu) > 0.0f)) return c;
+  float A, Bz;
+  dev::code_affine<D>(mg, A, Bz);
+  const float base = dev::tie_bound_base(2.0f * D * RS * (float(D) * M), mg);
+  const float v[4] = {w.x, w.y, w.z, w.w};
+  uint32_t fl = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float t = fmaf(v[e], A, Bz);
+    if (dev::near_tie(t, base + dev::kTieBoundT * fabsf(t))) fl |= 1u << e;
+  }
+  if (fl == 0u) return c;
+  const v4u* xr = reinterpret_cast<const v4u*>(static_cast<const uint8_t*>(a.src) + (s * a.rows + r) * (2 * D));
+  v4u xs[D / 8];
+#pragma unroll
+  for (int p = 0; p < D / 8; ++p) {
+    const v4u x = xr[p];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xs[p][m] = x[m] ^ a.sign_words[4 * p + m];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if ((fl >> e) & 1u) {
+      const uint32_t q = dev::exact_code8(dev::exact_rotated<D, DT>(xs, e0 + e), mg);
+      c = (c & ~(0xffu << (8 * e))) | (q << (8 * e));
+    }
+  }
+  return c;
+}
+
 /* E3: 4 codes per unit (one fp32 float4 in, one u32 of bytes out). */
-template <int D, int B, int G>
+template <int D, int DT, int B, int G>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const LaunchArgs a, const float* u, uint8_t* q8) {
   constexpr float QMAX = float((1 << B) - 1);
   constexpr int NG = D / G;
@@ -164,6 +218,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const LaunchArgs a, 
       c = dev::put_byte(fminf(fmaf(w[k].y, A, Bz), QMAX), 1, c);
       c = dev::put_byte(fminf(fmaf(w[k].z, A, Bz), QMAX), 2, c);
       c = dev::put_byte(fminf(fmaf(w[k].w, A, Bz), QMAX), 3, c);
+      if constexpr (B == 8) {
+        if (i < units) c = refine_unit8<D, DT, G>(a, s, i, w[k], c, meta);
+      }
       if (i < units) q[i] = c;
     }
   }
@@ -379,7 +436,7 @@ int encode_launch(const LaunchArgs& a, hipStream_t st, uint8_t* q8, float* u) {
     const unsigned ex = blocks_x(c.rows * (D / 4), kUnitsPerBlock, c.n_slabs);
     const unsigned px = blocks_x(c.rows, kTileVectors, c.n_slabs);
     hipLaunchKernelGGL((minmax_kernel<D, B, G>), dim3(rx, gy), dim3(kThreads), 0, st, c, u);
-    hipLaunchKernelGGL((quantize_kernel<D, B, G>), dim3(ex, gy), dim3(kThreads), 0, st, c, u, q8);
+    hipLaunchKernelGGL((quantize_kernel<D, DT, B, G>), dim3(ex, gy), dim3(kThreads), 0, st, c, u, q8);
     hipLaunchKernelGGL((pack_kernel<D, B>), dim3(px, gy), dim3(kThreads), 0, st, c, q8);
   });
 }

@@ -162,6 +162,29 @@ def test_probe_stream_stays_in_bounds():
         kvc.probe_stream(src, 1024, src, 0, waves_per_cu=33)
 
 
+def test_probe_stream_runs_stays_in_bounds():
+    """The run-at-once yardstick reads and writes only the sizes it is given,
+    at any ratio and run length, including a last partial run, with any grid."""
+    src = torch.randint(0, 255, (1 << 22,), dtype=torch.uint8, device=DEV)
+    for rb, wb, run, wpc in ((1 << 22, 1 << 20, 16, 4), (1 << 20, 1 << 22, 16, 8), (1 << 22, 0, 16, 2),
+                             (0, 1 << 21, 8, 8), (1024 * 37, 1024 * 5, 16, 1), (1024 * 5, 1024 * 37, 16, 32),
+                             (1024 * 37, 1024 * 37, 4, 3), (1024 * 3, 1024 * 2, 16, 4)):
+        whole, dst = gpu_util.guarded(max(wb, 1024) + 4096, DEV)
+        dst.fill_(0x5A)
+        kvc.probe_stream_runs(src, rb, dst, wb, run_kib=run, waves_per_cu=wpc)
+        torch.cuda.synchronize()
+        assert gpu_util.canaries_intact(whole), (rb, wb, run)
+        assert bool((dst[wb:] == 0x5A).all()), (rb, wb, run)
+        if wb:
+            assert not bool((dst[:wb] == 0x5A).all()), (rb, wb, run)
+    with pytest.raises(kvc.KvcError, match="KVC_EALIGN"):
+        kvc.probe_stream_runs(src, 1000, src, 0)
+    with pytest.raises(kvc.KvcError, match="KVC_EINVAL"):
+        kvc.probe_stream_runs(src, 1024, src, 0, run_kib=5)
+    with pytest.raises(kvc.KvcError, match="KVC_EINVAL"):
+        kvc.probe_stream_runs(src, 1024, src, 0, waves_per_cu=0)
+
+
 def test_probe_blocks_stays_in_bounds():
     """The block gather / scatter yardstick touches only the listed blocks
     (entries outside the region are skipped) and the first stream_bytes of
