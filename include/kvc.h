@@ -75,13 +75,17 @@
  * are decided in binary32 (1/sqrt(D) folded into the meta, t = fma(u, A, B)
  * with A = rs / scale and B = -zero / scale, each rounded once).  A stored
  * zero or scale is then within one fp16 step of the definition above, and a
- * code is the nearest level of the stored meta except where the exact t
- * lies within a few 2^-24 of (|y| + |zero|) / scale of a rounding boundary
- * k + 1/2: within 1e-5 for 2- and 4-bit codes of ordinary data, about 1e-4
- * (2^-13) for 8-bit codes, whose t reaches 255.  In a group whose range is
- * comparable with the binary32 resolution of its values (a huge offset
- * with a tiny range) the codes are only as good as that resolution; they
- * always stay within [0, 2^b - 1].
+ * 2- or 4-bit code is the nearest level of the stored meta except where the
+ * exact t lies within a few 2^-24 of (|y| + |zero|) / scale of a rounding
+ * boundary k + 1/2 (within 1e-5 for ordinary data).  8-bit codes, whose t
+ * reaches 255 where binary32 cannot resolve 1e-5, are the nearest level of
+ * the stored meta to float64 accuracy: every element whose binary32 t lies
+ * within a proven bound of a boundary is decided again from its input row
+ * in float64, which makes the 8-bit encode several times slower than the
+ * 2- and 4-bit ones.  In a 2- or 4-bit group whose range is comparable with
+ * the binary32 resolution of its values (a huge offset with a tiny range)
+ * the codes are only as good as that resolution.  Codes always stay within
+ * [0, 2^b - 1].
  */
 #ifndef KVC_H
 #define KVC_H
