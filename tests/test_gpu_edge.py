@@ -288,3 +288,28 @@ def _encode_check_multihead(x, p):
     res = parity.check_blob(xb, blob.cpu().numpy(), p.dtype, p.bits_k, p.bits_v, p.group, p.seed)
     rr = parity.check_decode(inputs.as_u16(xd), res.reference, p.dtype)
     return blob, res, rr
+
+
+@pytest.mark.parametrize("D,dtype,name", [(128, "bf16", "llama3_8b_4k"), (128, "bf16", "llama3_70b_16k"),
+                                          (64, "fp16", "llama3_8b_4k")])
+def test_transform_error_within_the_8bit_bound(D, dtype, name):
+    """The 8-bit encode re-decides every code whose binary32 t lies within a
+    bound of a tie; the bound's main term takes each of the D - 1 fp32
+    additions behind an element of u = H (s * x) to err by at most 2^-23 of
+    sum |x_j|.  On the matrix-core transform of real-shaped data (the rotate
+    hook runs the encode's own transform, then rounds u / sqrt(D) once more),
+    every element's error against the exact float64 rotation stays within
+    2 D 2^-24 sum|x_j| / sqrt(D) + 2^-24 |y|."""
+    p = presets.preset(name).with_(name="bound-%s-%d" % (name, D), layers=2, tokens=4096, head_dim=D, dtype=dtype)
+    x = inputs.make_kv(p)
+    xb = inputs.as_u16(x).reshape(-1, D)
+    y_gpu = kvc.debug_rotate(x.to(DEV), seed=p.seed).cpu().numpy().astype(np.float64).reshape(-1, D)
+    x64 = oracle.storage_to_f64(xb, dtype)
+    y_ref = oracle.rotate(x64, oracle.sign_vector(p.seed, D))
+    w = 2.0 ** -24
+    S = np.abs(x64).sum(axis=1, keepdims=True)
+    bound = 2 * D * w * S / np.sqrt(D) + w * np.abs(y_ref)
+    err = np.abs(y_gpu - y_ref)
+    ratio = float((err / bound).max())
+    _say("   %s D=%d %s: %d elements, worst error / bound %.4f" % (name, D, dtype, err.size, ratio))
+    assert ratio <= 1.0
