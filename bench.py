@@ -778,9 +778,11 @@ def main():
     t_dom = max(t_enc, t_dec)
     achieved = leg.algo_bytes / t_dom / 1e9
     result = {
-        "metric": "encode+decode throughput of raw bf16 KV input (GB/s); per-kernel % of HBM peak; "
-                  "break-even at 400 Gbit",
+        "metric": "encode/decode GB/s of raw bf16 KV input, % of HBM peak; break-even at 400 Gbit",
         "value": leg.raw_bytes / (ms_per_step / 1e3) / 1e9,
+        "value_is": "raw KV bytes of one step (one encode and one decode of the workload) / ms_per_step; "
+                    "per-kernel GB/s and fractions of the 8 TB/s peak under encode / decode, break-even "
+                    "under break_even",
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": a.steps,
