@@ -445,16 +445,25 @@ kvc_status kvc_encode_unfused_noalloc(const kvc_desc* desc, const void* kv, void
  * (device, >= total bytes) and, after each chunk, copies it to the same
  * offset of `dst` on copy_stream.  Starts only after the work already
  * enqueued on copy_stream (an earlier call's copies out of `out`).  When
- * copy_stream has passed the work, dst holds the chunked blob.
+ * copy_stream has passed the work, dst holds the chunked blob; until then
+ * the copies still read `out`, so other work that writes or frees `out`
+ * must first wait for copy_stream.
  *
  * kvc_receive_decode: copies chunk k from `src` into the same offset of
  * `staging` (device, >= total bytes) on copy_stream, then decodes it into
  * kv_out [L, 2, T, H, D] on compute_stream, so the decode of chunk k
  * overlaps the copy of chunk k+1.  Starts only after the work already
  * enqueued on compute_stream (an earlier call's decodes out of `staging`).
+ * When compute_stream has passed the work, kv_out holds the decode; until
+ * then the decodes still read `staging`, so other work that writes or frees
+ * `staging` must first wait for compute_stream.
  *
- * Both streams must have the default priority.  The two calls keep one
- * HIP event per (host thread, device) to order the streams.
+ * Both streams must have the default priority (they may be the same
+ * stream: the work then runs in order, without overlap).  The two calls
+ * keep one HIP event per (host thread, device) to order the streams.
+ * Arguments are checked before anything is enqueued; a launch failure
+ * (KVC_EHIP) after the first chunk leaves the earlier chunks' work
+ * enqueued.
  */
 kvc_status kvc_chunked_size(const kvc_desc* desc, int64_t chunk_layers, uint64_t* total, uint64_t* stride);
 kvc_status kvc_encode_send(const kvc_desc* desc, const void* kv, void* out, uint64_t out_bytes,
