@@ -91,6 +91,25 @@ def test_repeated_calls_reuse_buffers():
         assert torch.equal(y.view(torch.int16), full.view(torch.int16))
 
 
+def test_one_stream_for_both():
+    """The compute and copy streams may be one stream: the work then runs in
+    order and gives the same bytes as two streams."""
+    p = _preset(3, 50, 2, 4, 4, 128)
+    x = inputs.make_kv(p).to(DEV)
+    total, _ = kvc.chunked_size(p.layers, p.tokens, p.kv_heads, p.head_dim, p.bits_k, p.bits_v, p.group, 1)
+    dst = torch.full((total,), 0x5A, dtype=torch.uint8, pin_memory=True)
+    s = torch.cuda.current_stream()
+    _say("encode_send / receive_decode on one stream")
+    kvc.encode_send(x, p.bits_k, p.bits_v, p.group, 1, dst, seed=p.seed, copy_stream=s)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.to(DEV), _per_chunk_blob(p, x, 1))
+    xd = kvc.receive_decode(dst, x.shape, p.dtype, p.bits_k, p.bits_v, p.group, 1, seed=p.seed, copy_stream=s)
+    torch.cuda.synchronize()
+    full = kvc.decode(kvc.encode(x, p.bits_k, p.bits_v, p.group, seed=p.seed), x.shape, p.dtype, p.bits_k,
+                      p.bits_v, p.group, seed=p.seed)
+    assert torch.equal(xd.view(torch.int16), full.view(torch.int16))
+
+
 def test_pipeline_validation():
     x = torch.zeros((2, 2, 8, 1, 128), dtype=torch.bfloat16, device=DEV)
     dst = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)
