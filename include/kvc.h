@@ -81,8 +81,11 @@
  * reaches 255 where binary32 cannot resolve 1e-5, are the nearest level of
  * the stored meta to float64 accuracy: every element whose binary32 t lies
  * within a proven bound of a boundary is decided again from its input row
- * in float64, which makes the 8-bit encode several times slower than the
- * 2- and 4-bit ones.  In a 2- or 4-bit group whose range is comparable with
+ * in float64.  Contiguous 8-bit encodes therefore rotate with the
+ * in-register butterfly by default (KVC_TRANSFORM_AUTO below): its IEEE
+ * additions admit a bound 2D / log2(D) times tighter than the matrix cores'
+ * and leave that many times fewer elements to decide again.  The 8-bit
+ * encode is still the slowest width.  In a 2- or 4-bit group whose range is comparable with
  * the binary32 resolution of its values (a huge offset with a tiny range)
  * the codes are only as good as that resolution.  Codes always stay within
  * [0, 2^b - 1].

@@ -959,6 +959,12 @@ __device__ __forceinline__ void quantize_group(const float* y, float A, float Bz
   *words = pack_word<B>(tq);
 }
 
+/* The encode's transform: kEncodeMatrix runs u = H x on the matrix cores
+ * (hadamard_mfma), kEncodeButterfly as the in-register butterfly of each
+ * lane's own vector in fp32.  Both are exact products with +-1 and fp32
+ * sums, in different orders, so their u differ by rounding only. */
+constexpr int kEncodeMatrix = 0, kEncodeButterfly = 1;
+
 /* ---- exact 8-bit decisions near a tie ----------------------------------------
  *
  * At 8 bits t reaches 255, where one binary32 ulp is 2^-16, so the binary32
@@ -1034,16 +1040,9 @@ __device__ __forceinline__ float tie_bound_base(float err_u_y, uint32_t meta) {
 }
 constexpr float kTieBoundT = 1.05f * 3.0f * 5.9604644775390625e-8f;  // per |t32|
 
-/* Re-decide exactly the 8-bit codes of this lane's vector whose binary32 t
- * lies within the bound of a tie.  u: the unnormalized rotated values; xs:
- * the signed row they came from; words: the packed codes (code k at byte
- * k % 4 of word k / 4), patched in place. */
-template <int D, int DT, int G>
-__device__ __forceinline__ void refine_ties8(const float (&u)[D], const v4u (&xs)[D / 8], const uint32_t* meta,
-                                             uint32_t* words) {
-#pragma clang fp contract(off)
-  constexpr int NG = D / G, NW = D / 32;
-  constexpr float RS = Norm<D>::inv_sqrt;
+/* S = sum_j |x_j| of a signed row (exact values, binary32 sum). */
+template <int D, int DT>
+__device__ __forceinline__ float row_abs_sum(const v4u (&xs)[D / 8]) {
   float S = 0.0f;
 #pragma unroll
   for (int p = 0; p < D / 8; ++p) {
@@ -1055,7 +1054,17 @@ __device__ __forceinline__ void refine_ties8(const float (&u)[D], const v4u (&xs
       S += fabsf(hi);
     }
   }
-  uint32_t flags[NW];
+  return S;
+}
+
+/* Flags (bit j % 32 of word j / 32) of the elements whose binary32 t lies
+ * within the bound of a tie; err_u_y bounds the error of u in units of y
+ * divided by w (c_u rs S). */
+template <int D, int G>
+__device__ __forceinline__ void ties8_flags(const float (&u)[D], float err_u_y, const uint32_t* meta,
+                                            uint32_t (&flags)[D / 32]) {
+#pragma clang fp contract(off)
+  constexpr int NG = D / G, NW = D / 32;
 #pragma unroll
   for (int w = 0; w < NW; ++w) flags[w] = 0u;
 #pragma unroll
@@ -1063,13 +1072,22 @@ __device__ __forceinline__ void refine_ties8(const float (&u)[D], const v4u (&xs
     if (!(f16_value(meta[g] & 0xffffu) > 0.0f)) continue;  // constant group: every code 0, exactly
     float A, Bz;
     code_affine<D>(meta[g], A, Bz);
-    const float base = tie_bound_base(2.0f * D * RS * S, meta[g]);
+    const float base = tie_bound_base(err_u_y, meta[g]);
 #pragma unroll
     for (int j = g * G; j < (g + 1) * G; ++j) {
       const float t = fmaf(u[j], A, Bz);
       if (near_tie(t, base + kTieBoundT * fabsf(t))) flags[j / 32] |= 1u << (j % 32);
     }
   }
+}
+
+/* Decide every flagged element again exactly from the signed row xs and
+ * patch its code into words (code k at byte k % 4 of word k / 4).  The
+ * wave repeats until no lane has a flag left. */
+template <int D, int DT, int G>
+__device__ __forceinline__ void ties8_resolve(const v4u (&xs)[D / 8], const uint32_t* meta, uint32_t (&flags)[D / 32],
+                                              uint32_t* words) {
+  constexpr int NG = D / G, NW = D / 32;
   for (;;) {
     uint32_t any = 0u;
 #pragma unroll
@@ -1103,11 +1121,59 @@ __device__ __forceinline__ void refine_ties8(const float (&u)[D], const v4u (&xs
   }
 }
 
+/* Re-decide exactly the 8-bit codes of this lane's vector whose binary32 t
+ * lies within the bound of a tie, u from the matrix cores (2 D additions'
+ * worth of error, each at most 2w, whatever their order and rounding).
+ * u: the unnormalized rotated values; xs: the signed row they came from;
+ * words: the packed codes, patched in place. */
+template <int D, int DT, int G>
+__device__ __forceinline__ void refine_ties8(const float (&u)[D], const v4u (&xs)[D / 8], const uint32_t* meta,
+                                             uint32_t* words) {
+  constexpr float RS = Norm<D>::inv_sqrt;
+  uint32_t flags[D / 32];
+  ties8_flags<D, G>(u, 2.0f * D * RS * row_abs_sum<D, DT>(xs), meta, flags);
+  ties8_resolve<D, DT, G>(xs, meta, flags, words);
+}
+
+/* The same for u from the in-register butterfly: log2 D stages of IEEE
+ * binary32 additions, round to nearest.  Element i's value at stage k is the
+ * sum of one of the D / 2^k disjoint blocks of the signed row, so the
+ * additions of stage k err by at most w times that block's sum of |x_j|
+ * (times (1 + w)^k), and the stages together by log2(D) w S to first order
+ * -- 2D / log2(D) times less than the matrix-core bound, and so that many
+ * times fewer elements to decide again.  S is given (summed from the row
+ * before the butterfly); the row itself is read back from `stash` (this
+ * lane's LDS copy, chunk p at slot index base ^ p) only when some lane of
+ * the wave has an element to decide. */
+template <int D, int DT, int G>
+__device__ __forceinline__ void refine_ties8_stash(const float (&u)[D], float S, const v4u* stash,
+                                                   const uint32_t* meta, uint32_t* words) {
+  constexpr float RS = Norm<D>::inv_sqrt;
+  constexpr int LOG2D = D == 64 ? 6 : 7;
+  static_assert(D == 64 || D == 128, "head_dim");
+  uint32_t flags[D / 32];
+  ties8_flags<D, G>(u, float(LOG2D) * RS * S, meta, flags);
+  uint32_t any = 0u;
+#pragma unroll
+  for (int w = 0; w < D / 32; ++w) any |= flags[w];
+  if (__builtin_amdgcn_ballot_w64(any != 0u) == 0) return;
+  constexpr int CH = D / 8;
+  const int v = static_cast<int>(threadIdx.x);
+  const int base = v * CH + (v % CH);
+  v4u xs[D / 8];
+#pragma unroll
+  for (int p = 0; p < CH; ++p) xs[p] = stash[base ^ p];
+  ties8_resolve<D, DT, G>(xs, meta, flags, words);
+}
+
 /* Meta, codes and stores of one vector from its unnormalized rotated values
  * u; at 8 bits the codes near a tie are decided again exactly from the
- * signed row xs (unused at 2 and 4 bits). */
-template <int D, int DT, int B, int G, bool PAGED>
-__device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t, const v4u (&xs)[D / 8]) {
+ * signed row: xs in registers after the matrix cores, or the lane's LDS
+ * copy in `stash` with S8 = sum |x_j| after the butterfly (all unused at 2
+ * and 4 bits). */
+template <int D, int DT, int B, int G, bool PAGED, int XF>
+__device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t, const v4u (&xs)[D / 8], float S8,
+                                              const v4u* stash) {
   constexpr int NG = D / G;
   constexpr float QMAX = float((1 << B) - 1);
   constexpr int WPG = G * B / 32;  // code words per group
@@ -1139,7 +1205,12 @@ __device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t, cons
     }
     KVC_PHASE();
   }
-  if constexpr (B == 8) refine_ties8<D, DT, G>(y, xs, meta, words);
+  if constexpr (B == 8) {
+    if constexpr (XF == kEncodeButterfly)
+      refine_ties8_stash<D, DT, G>(y, S8, stash, meta, words);
+    else
+      refine_ties8<D, DT, G>(y, xs, meta, words);
+  }
   if (static_cast<int>(threadIdx.x) < t.count) {
     constexpr int RB = D * B / 8;
     int stride;
@@ -1158,11 +1229,6 @@ __device__ __forceinline__ void encode_vector(float (&y)[D], const Tile& t, cons
   }
 }
 
-/* The encode's transform: kEncodeMatrix runs u = H x on the matrix cores
- * (hadamard_mfma), kEncodeButterfly as the in-register butterfly of each
- * lane's own vector in fp32.  Both are exact products with +-1 and fp32
- * sums, in different orders, so their u differ by rounding only. */
-constexpr int kEncodeMatrix = 0, kEncodeButterfly = 1;
 
 /*
  * Encode: per tile, the rows arrive in LDS by DMA; each lane reads its own
@@ -1172,7 +1238,11 @@ constexpr int kEncodeMatrix = 0, kEncodeButterfly = 1;
 template <int D, int DT, int B, int G, bool PAGED, int XF = kEncodeMatrix>
 KVC_KERNEL void encode_kernel(const LaunchArgs a) {
   constexpr int CH = D / 8;
+  // the 8-bit butterfly encode keeps each lane's signed row in LDS for the
+  // exact decisions instead of in registers
+  constexpr bool STASH = B == 8 && XF == kEncodeButterfly;
   __shared__ v4u lds[kTileVectors * CH];
+  __shared__ v4u stash[STASH ? kTileVectors * CH : 1];
   __shared__ uint32_t signs[64];
   const uint8_t* tensor = static_cast<const uint8_t*>(a.src);
   uint8_t* blob = static_cast<uint8_t*>(a.dst);
@@ -1189,6 +1259,12 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
   for (;;) {
     v4u xc[D / 8];
     read_row_signed<D>(lds, signs, xc);
+    if constexpr (STASH) {
+      const int v = static_cast<int>(threadIdx.x);
+      const int base = v * CH + (v % CH);
+#pragma unroll
+      for (int p = 0; p < CH; ++p) stash[base ^ p] = xc[p];
+    }
     KVC_PHASE();
     lds_done();  // every lane's row is in registers: the buffer is free
     Tile nxt;
@@ -1196,23 +1272,28 @@ KVC_KERNEL void encode_kernel(const LaunchArgs a) {
     if (more) dma_rows<D, !PAGED>(nxt.src, nxt.count, (lds_v4u*)lds);
     KVC_PHASE();
     v4u xs[D / 8];  // the signed row, kept for the exact 8-bit decisions
-    if constexpr (B == 8) {
+    if constexpr (B == 8 && !STASH) {
 #pragma unroll
       for (int p = 0; p < D / 8; ++p) xs[p] = xc[p];
     }
     float y[D];
+    float S8 = 0.0f;
     if constexpr (XF == kEncodeButterfly) {
 #pragma unroll
       for (int p = 0; p < D / 8; ++p) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) unpack_pair<DT>(xc[p][m], y[8 * p + 2 * m], y[8 * p + 2 * m + 1]);
       }
+      if constexpr (STASH) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) S8 += fabsf(y[j]);
+      }
       butterfly_stages<D, 1, D>(y);
     } else {
       hadamard_mfma<D, DT>(xc, had, y);
     }
     KVC_PHASE();
-    encode_vector<D, DT, B, G, PAGED>(y, cur, xs);
+    encode_vector<D, DT, B, G, PAGED, XF>(y, cur, xs, S8, stash);
     if (!more) break;
     // outstanding: the next tile's DMA, then this tile's code and meta
     // stores (RB / 16 + 1 instructions, issued by the lanes < count)

@@ -128,6 +128,25 @@ def _fma_f32(a, b, c):
     return r
 
 
+def butterfly_model(rows, seed, D):
+    """White-box model of the in-register butterfly that 8-bit contiguous
+    encodes run by default, on rows of values exact in the storage type
+    (float64 [N, D]): the signed row in binary32 (exact), then log2 D
+    stages of binary32 additions and subtractions in the kernel's order
+    (element j of each block of 2h takes a + b, element j + h takes a - b).
+    numpy's float32 arithmetic rounds to nearest even like the kernel's, so
+    the model gives the kernel's unnormalized u to the bit (float64 [N, D])."""
+    x = rows.astype(np.float32) * oracle.sign_vector(seed, D).astype(np.float32)
+    y = x.reshape(len(x), D)
+    h = 1
+    while h < D:
+        blk = y.reshape(len(y), D // (2 * h), 2, h)
+        a, b = blk[:, :, 0, :], blk[:, :, 1, :]
+        y = np.stack([a + b, a - b], axis=2).reshape(len(y), D)
+        h *= 2
+    return y.astype(np.float64)
+
+
 def kernel_decision_model(u, D, G, bits):
     """White-box binary32 model of the encode kernel's meta and code decision
     from its unnormalized rotated values u (binary32 values as float64, [N, D]):
@@ -193,7 +212,10 @@ def test_degenerate_groups(D, dtype, bits):
     decision is also modelled on the GPU's transform output (exact there:
     1/sqrt(64) = 1/8), and codes and meta must equal the model's to the bit,
     including groups where the clamp to 2^b - 1 acts -- so the clamp branch
-    runs and keeps every code within its bits."""
+    runs and keeps every code within its bits.  8-bit contiguous encodes
+    rotate with the in-register butterfly, not the matrix cores of
+    kvc_debug_rotate: there the GPU's own rotated values are those of the
+    butterfly (butterfly_model, held to criterion (1) as well)."""
     rng = np.random.default_rng(17 * D + bits)
     G, seed = 32, 9
     rk = _degenerate_rows(D, dtype, bits, G, seed, 640, rng)
@@ -205,6 +227,10 @@ def test_degenerate_groups(D, dtype, bits):
     y_ref = oracle.rotate(np.concatenate([rk, rv]), oracle.sign_vector(seed, D))
     y_gpu = kvc.debug_rotate(xg, seed=seed).cpu().numpy().astype(np.float64).reshape(-1, D)
     rot = parity.check_rotation(y_gpu, y_ref)
+    if bits == 8:
+        rs = np.float32(1.0 / np.sqrt(D))
+        y_gpu = (butterfly_model(np.concatenate([rk, rv]), seed, D).astype(np.float32) * rs).astype(np.float64)
+        rot = max(rot, parity.check_rotation(y_gpu, y_ref))
     total, _ = kvc.encoded_size(1, n, 1, D, bits, bits, G, dtype)
     whole, out = gpu_util.guarded(total, DEV)
     kvc.encode(xg, bits, bits, G, seed=seed, out=out)

@@ -65,9 +65,11 @@ def test_butterfly_encode_and_decodes(D, dtype, bk, bv, G):
         torch.cuda.synchronize()
         assert gpu_util.canaries_intact(whole), "encode (%s) wrote outside its blob" % xf
         blobs[xf] = out
-    # the default encode runs the matrix cores: the same bytes
+    # the default encode runs the matrix cores, and the butterfly for 8-bit
+    # codes (its tighter error bound leaves fewer ties to decide again): the
+    # same bytes
     auto = kvc.encode(xg, bk, bv, G, seed=p.seed)
-    assert torch.equal(auto, blobs["matrix"])
+    assert torch.equal(auto, blobs["butterfly" if bk == bv == 8 else "matrix"])
     res = parity.check_blob(xb, blobs["butterfly"].cpu().numpy(), dtype, bk, bv, G, p.seed)
     _say("  butterfly encode vs oracle:", res.report)
     outs = _decode_all(blobs["butterfly"], xg, p)

@@ -1,6 +1,6 @@
 """GPU parity of the separate-kernel comparator (kvc_encode_unfused /
-kvc_decode_unfused): its blob is bit-identical to the fused path's, its
-decode agrees with the fused decode within the decode criterion (the two
+kvc_decode_unfused): its blob is bit-identical to the fused matrix-core
+encode's (the default transform except at 8 bits), its decode agrees with the fused decode within the decode criterion (the two
 round in different places: the comparator dequantizes and then runs the
 whole inverse transform, the fused decode transforms the integer codes
 within their groups first), and both meet the oracle criteria on their own."""
@@ -58,7 +58,9 @@ def _both(p, x):
     ws_bytes = kvc.unfused_workspace_size(p.layers, p.tokens, p.kv_heads, D, p.bits_k, p.bits_v, p.group, p.dtype)
     ws_whole, ws = gpu_util.guarded(ws_bytes, DEV)
     whole, out_u = gpu_util.guarded(total, DEV)
-    out_f = kvc.encode(x, p.bits_k, p.bits_v, p.group, seed=p.seed)
+    # the comparator mirrors the matrix-core encode (its first stage is that
+    # transform), which 8-bit encodes take only when asked
+    out_f = kvc.encode(x, p.bits_k, p.bits_v, p.group, seed=p.seed, transform="matrix")
     kvc.encode_unfused(x, p.bits_k, p.bits_v, p.group, seed=p.seed, out=out_u, workspace=ws)
     torch.cuda.synchronize()
     assert gpu_util.canaries_intact(whole) and gpu_util.canaries_intact(ws_whole)
@@ -154,7 +156,7 @@ def test_large_ragged_blob_both_decodes(D, dtype, b, G, T, H, line_mib):
         xl = x[l:l + 1].contiguous()
         tl, _ = kvc.encoded_size(1, p.tokens, p.kv_heads, D, b, b, G, dtype)
         assert tl < line_mib << 20
-        bl = kvc.encode(xl, b, b, G, seed=p.seed)
+        bl = kvc.encode(xl, b, b, G, seed=p.seed, transform="matrix")
         dl = kvc.decode(bl, xl.shape, dtype, b, b, G, seed=p.seed)
         torch.cuda.synchronize()
         _say("  layer %d: per-layer decode vs whole decode" % l)
