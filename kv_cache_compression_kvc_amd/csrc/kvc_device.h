@@ -1040,23 +1040,6 @@ __device__ __forceinline__ float tie_bound_base(float err_u_y, uint32_t meta) {
 }
 constexpr float kTieBoundT = 1.05f * 3.0f * 5.9604644775390625e-8f;  // per |t32|
 
-/* S = sum_j |x_j| of a signed row (exact values, binary32 sum). */
-template <int D, int DT>
-__device__ __forceinline__ float row_abs_sum(const v4u (&xs)[D / 8]) {
-  float S = 0.0f;
-#pragma unroll
-  for (int p = 0; p < D / 8; ++p) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      float lo, hi;
-      unpack_pair<DT>(xs[p][m], lo, hi);
-      S += fabsf(lo);
-      S += fabsf(hi);
-    }
-  }
-  return S;
-}
-
 /* Flags (bit j % 32 of word j / 32) of the elements whose binary32 t lies
  * within the bound of a tie; err_u_y bounds the error of u in units of y
  * divided by w (c_u rs S). */
@@ -1129,10 +1112,69 @@ __device__ __forceinline__ void ties8_resolve(const v4u (&xs)[D / 8], const uint
 template <int D, int DT, int G>
 __device__ __forceinline__ void refine_ties8(const float (&u)[D], const v4u (&xs)[D / 8], const uint32_t* meta,
                                              uint32_t* words) {
+  // one body on purpose: built from ties8_flags and ties8_resolve, this
+  // kernel's register allocation spilled several times more and ran at
+  // half the speed
+#pragma clang fp contract(off)
+  constexpr int NG = D / G, NW = D / 32;
   constexpr float RS = Norm<D>::inv_sqrt;
-  uint32_t flags[D / 32];
-  ties8_flags<D, G>(u, 2.0f * D * RS * row_abs_sum<D, DT>(xs), meta, flags);
-  ties8_resolve<D, DT, G>(xs, meta, flags, words);
+  float S = 0.0f;
+#pragma unroll
+  for (int p = 0; p < D / 8; ++p) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float lo, hi;
+      unpack_pair<DT>(xs[p][m], lo, hi);
+      S += fabsf(lo);
+      S += fabsf(hi);
+    }
+  }
+  uint32_t flags[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) flags[w] = 0u;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (!(f16_value(meta[g] & 0xffffu) > 0.0f)) continue;  // constant group: every code 0, exactly
+    float A, Bz;
+    code_affine<D>(meta[g], A, Bz);
+    const float base = tie_bound_base(2.0f * D * RS * S, meta[g]);
+#pragma unroll
+    for (int j = g * G; j < (g + 1) * G; ++j) {
+      const float t = fmaf(u[j], A, Bz);
+      if (near_tie(t, base + kTieBoundT * fabsf(t))) flags[j / 32] |= 1u << (j % 32);
+    }
+  }
+  for (;;) {
+    uint32_t any = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) any |= flags[w];
+    if (__builtin_amdgcn_ballot_w64(any != 0u) == 0) break;
+    if (any != 0u) {
+      int wsel = 0;
+      uint32_t fw = 0u;
+#pragma unroll
+      for (int w = NW - 1; w >= 0; --w) {
+        if (flags[w] != 0u) {
+          wsel = w;
+          fw = flags[w];
+        }
+      }
+      const int k = 32 * wsel + __builtin_ctz(fw);
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        if (w == wsel) flags[w] = fw & (fw - 1u);
+      uint32_t mg = meta[0];
+#pragma unroll
+      for (int g = 1; g < NG; ++g)
+        if (k / G == g) mg = meta[g];
+      const uint32_t q = exact_code8(exact_rotated<D, DT>(xs, k), mg);
+      const int wk = k >> 2;
+      const uint32_t sh = 8u * static_cast<uint32_t>(k & 3);
+#pragma unroll
+      for (int w = 0; w < D / 4; ++w)
+        if (w == wk) words[w] = (words[w] & ~(0xffu << sh)) | (q << sh);
+    }
+  }
 }
 
 /* The same for u from the in-register butterfly: log2 D stages of IEEE
