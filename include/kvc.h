@@ -81,8 +81,8 @@
  * reaches 255 where binary32 cannot resolve 1e-5, are the nearest level of
  * the stored meta to float64 accuracy: every element whose binary32 t lies
  * within a proven bound of a boundary is decided again from its input row
- * in float64.  Contiguous 8-bit encodes therefore rotate with the
- * in-register butterfly by default (KVC_TRANSFORM_AUTO below): its IEEE
+ * in float64.  8-bit encodes therefore rotate with the in-register
+ * butterfly by default (KVC_TRANSFORM_AUTO below): its IEEE
  * additions admit a bound 2D / log2(D) times tighter than the matrix cores'
  * and leave that many times fewer elements to decide again.  The 8-bit
  * encode is still the slowest width.  In a 2- or 4-bit group whose range is comparable with
@@ -258,7 +258,8 @@ typedef enum kvc_transform {
 /*
  * Options of the *_with calls (a NULL pointer means all defaults).
  *   transform: a kvc_transform value.  Paged calls accept AUTO and MATRIX
- *     (their kernels run on the matrix cores).
+ *     (their kernels run on the matrix cores, except the 8-bit encode, which
+ *     AUTO runs on the butterfly as for contiguous calls).
  *   start_event, stop_event: hipEvent_t handles created by the caller on the
  *     current device, or NULL.  start_event takes the time the call's first
  *     kernel starts, stop_event the time its last kernel ends (a call runs

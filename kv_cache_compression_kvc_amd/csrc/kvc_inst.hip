@@ -22,9 +22,10 @@ template <int D, int DT, int B, int G, bool PAGED>
 Kernel pick_op(Op op, int mode) {
   if (op == Op::Encode) {
     if (mode == dev::kEncodeMatrix) return dev::encode_kernel<D, DT, B, G, PAGED, dev::kEncodeMatrix>;
-    // the butterfly encode is a contiguous comparator only
-    if constexpr (!PAGED)
-      if (mode == dev::kEncodeButterfly) return dev::encode_kernel<D, DT, B, G, false, dev::kEncodeButterfly>;
+    // paged butterfly encodes exist at 8 bits only, where they are the
+    // default; at 2 and 4 bits the butterfly is a contiguous comparator
+    if constexpr (!PAGED || B == 8)
+      if (mode == dev::kEncodeButterfly) return dev::encode_kernel<D, DT, B, G, PAGED, dev::kEncodeButterfly>;
     return nullptr;
   }
   if constexpr (!PAGED) {

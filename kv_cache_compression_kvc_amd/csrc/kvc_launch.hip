@@ -141,10 +141,10 @@ bool decode_large(const LaunchArgs& a, int head_dim, int bits) {
 LaunchShape launch_shape(Op op, const LaunchArgs& a, int head_dim, int bits, int transform) {
   const bool bfly = transform == KVC_TRANSFORM_BUTTERFLY;
   if (op == Op::Encode) {
-    // 8-bit contiguous encodes take the butterfly by default: its error
-    // bound is 2 D / log2(D) times tighter than the matrix cores', so far
-    // fewer codes near a tie are decided again in float64
-    const bool bfly_enc = bfly || (transform == KVC_TRANSFORM_AUTO && !a.paged && bits == 8);
+    // 8-bit encodes take the butterfly by default: its error bound is
+    // 2 D / log2(D) times tighter than the matrix cores', so far fewer codes
+    // near a tie are decided again in float64
+    const bool bfly_enc = bfly || (transform == KVC_TRANSFORM_AUTO && bits == 8);
     return {(a.paged && head_dim == 64) ? 0 : 1, bfly_enc ? dev::kEncodeButterfly : dev::kEncodeMatrix, 0};
   }
   if (op != Op::Decode) return {0, 0, 0};
