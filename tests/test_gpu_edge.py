@@ -11,6 +11,7 @@ import torch
 
 import oracle
 import parity
+from kernel_models import butterfly_model
 import gpu_util
 import kv_cache_compression_kvc_amd as kvc
 from kv_cache_compression_kvc_amd import inputs, presets
@@ -126,25 +127,6 @@ def _fma_f32(a, b, c):
     r = np.where((s == mid_lo) & (e < 0), lo, r)
     r = np.where((s == mid_hi) & (e > 0), hi, r)
     return r
-
-
-def butterfly_model(rows, seed, D):
-    """White-box model of the in-register butterfly that 8-bit contiguous
-    encodes run by default, on rows of values exact in the storage type
-    (float64 [N, D]): the signed row in binary32 (exact), then log2 D
-    stages of binary32 additions and subtractions in the kernel's order
-    (element j of each block of 2h takes a + b, element j + h takes a - b).
-    numpy's float32 arithmetic rounds to nearest even like the kernel's, so
-    the model gives the kernel's unnormalized u to the bit (float64 [N, D])."""
-    x = rows.astype(np.float32) * oracle.sign_vector(seed, D).astype(np.float32)
-    y = x.reshape(len(x), D)
-    h = 1
-    while h < D:
-        blk = y.reshape(len(y), D // (2 * h), 2, h)
-        a, b = blk[:, :, 0, :], blk[:, :, 1, :]
-        y = np.stack([a + b, a - b], axis=2).reshape(len(y), D)
-        h *= 2
-    return y.astype(np.float64)
 
 
 def kernel_decision_model(u, D, G, bits):
